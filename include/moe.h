@@ -1,0 +1,174 @@
+/*
+ * moe.h - C ABI of the single-GPU fine-grained Mixture-of-Experts FFN layer
+ * forward for AMD Instinct MI355X (gfx950).
+ *
+ * The layer has five steps, one entry point each:
+ *   moe_route      gate scores, softmax, top-k, renormalised weights
+ *   moe_dispatch   expert histogram, offsets, stable permutation, row gather
+ *   moe_expert_ffn grouped Linear -> erf-GeLU -> Linear over ragged segments
+ *                  (plus the optional always-on shared expert)
+ *   moe_combine    weighted sum of each token's k expert rows (+ shared row)
+ *   moe_load_stats capacity, overflow / drops, skew, Gini, stragglers
+ *
+ * Sources of the method (three web pages; cited by title and section):
+ *   [K3]   "hncyxsy.com Kimi K3 fine-grained MoE" article: router listing
+ *          (FineGrainedMoERouter), the dispatch / local expert FFN / combine
+ *          flow, the shared expert, the FFN cost equation.
+ *   [DIAG] "Kimi K3 专家路由不均衡诊断" (bjdmk.com.cn): section 3 diagnostics
+ *          module (MoERouteDiagnostics) and section 4.2 (biased score).
+ *   [BLOG] "lpqz.cn MoE engineering blog": section 3.1 (expert = two Linear
+ *          layers with GeLU; dispatcher with one shared buffer).
+ *
+ * Conventions for every call:
+ *   - All tensor pointers are DEVICE memory owned by the caller, row-major and
+ *     contiguous, 16-byte aligned. The library never allocates, frees or keeps
+ *     a pointer past the call. Scratch memory comes from a caller-provided
+ *     workspace whose size the *_workspace_bytes queries return.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream). Every
+ *     call only enqueues work on it and returns; there is no host
+ *     synchronisation, so device-resident results (e.g. offsets) feed the next
+ *     call directly. Calls keep no global state and are re-entrant.
+ *   - Return value: MOE_OK (0) or a negative moe_status. Arguments are
+ *     validated on the host before any HIP call; on error nothing is
+ *     enqueued. A failed launch returns MOE_ERR_HIP.
+ *   - dtype: MOE_F32 (fp32 activations, weights, arithmetic) or MOE_BF16
+ *     (bf16 activations and weights, fp32 accumulation, bf16 results rounded
+ *     to nearest even).
+ *   - Supported shapes: 1 <= E <= 256, 1 <= k <= min(E, 8), H % 64 == 0,
+ *     F % 64 == 0, Fs % 64 == 0 (or Fs == 0), T >= 1, T*k < 2^31.
+ *     Anything else returns MOE_ERR_UNSUPPORTED (or MOE_ERR_INVALID_ARG for
+ *     null pointers / non-positive sizes).
+ *   - Weights use the [out, in] layout of a Linear layer: Wg [E,H],
+ *     W1 [E,F,H], W2 [E,H,F], Ws1 [Fs,H], Ws2 [H,Fs]. No Linear has a bias.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum */
+  MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported range */
+  MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query */
+  MOE_ERR_HIP = -4          /* a HIP launch failed */
+} moe_status;
+
+/* Load diagnostics of one step ([DIAG] section 3). Written to device memory. */
+typedef struct {
+  int64_t num_tokens;      /* T */
+  int64_t assignments;     /* T*k */
+  int64_t capacity;        /* int((T*k / E) * cf), evaluated in double */
+  int64_t max_load;        /* max_e counts[e] */
+  int64_t min_load;        /* min_e counts[e] */
+  int64_t dropped;         /* sum_e max(0, counts[e] - capacity); counted only */
+  int64_t num_stragglers;  /* #{e : counts[e] > capacity} */
+  int64_t gini_num;        /* 2*sum_i i*c_(i) - (E+1)*sum c  (c sorted ascending, i = 1..E) */
+  int64_t gini_den;        /* E * sum c (1 when sum c == 0) */
+  double load_skew_ratio;  /* (double)max / ((double)min + 1e-5) */
+  double gini;             /* (double)gini_num / (double)gini_den, one division; 0 if sum c == 0 */
+  double drop_rate;        /* (double)dropped / (double)(T*k) */
+} moe_load_stats_t;
+
+/*
+ * moe_route - top-k softmax gating ([K3] router listing; [DIAG] section 4.2).
+ *   s[t,e]  = sum_h x[t,h] * wg[e,h] + bias[e]          (fp32 accumulation)
+ *   topk_idx[t,0..k-1] = the k largest s[t,:], descending; equal scores take
+ *                        the lower expert id first
+ *   topk_w[t,j] = exp(s[t,idx_j] - m) / sum_j' exp(s[t,idx_j'] - m), m = max_e s[t,e]
+ *               (the softmax over all E experts renormalised over the k chosen
+ *                ones; the full-E denominator cancels)
+ * x        [T,H] dtype          device, read
+ * wg       [E,H] dtype          device, read
+ * bias     [E]   fp32 or NULL   device, read (NULL = no routing bias)
+ * topk_idx [T,k] int32          device, written
+ * topk_w   [T,k] fp32           device, written
+ */
+int moe_route(const void* x, const void* wg, const float* bias, int T, int H, int E, int k,
+              int dtype, int32_t* topk_idx, float* topk_w, void* stream);
+
+/* Workspace bytes moe_dispatch needs for (T, E, k); 0 on unsupported sizes. */
+size_t moe_dispatch_workspace_bytes(int T, int E, int k);
+
+/*
+ * moe_dispatch - group the T*k (token, slot) assignments by expert
+ * ([BLOG] section 3.1 dispatcher; histogram as in [DIAG] section 3).
+ *   counts[e]   = #{(t,j) : topk_idx[t,j] == e}
+ *   offsets[0]  = 0, offsets[e+1] = offsets[e] + counts[e]
+ *   perm[p]     = t*k + j for buffer row p, in expert-major, token-ascending
+ *                 order (a stable sort of the row-major assignments by expert)
+ *   inv[t*k+j]  = p, the inverse of perm
+ *   xs[p,:]     = x[perm[p] / k, :] (exact copy)
+ * topk_idx [T,k] int32 in [0,E)  device, read (ids of one token are distinct)
+ * x        [T,H] dtype           device, read
+ * counts [E], offsets [E+1], perm [T*k], inv [T*k] int32; xs [T*k,H] dtype: device, written
+ * ws / ws_bytes: device workspace of at least moe_dispatch_workspace_bytes(T,E,k)
+ */
+int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k, int dtype,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* xs,
+                 void* ws, size_t ws_bytes, void* stream);
+
+/* Workspace bytes moe_expert_ffn needs; 0 on unsupported sizes. */
+size_t moe_expert_ffn_workspace_bytes(int rows, int T, int H, int E, int F, int Fs, int dtype);
+
+/*
+ * moe_expert_ffn - grouped expert FFN over the expert-contiguous buffer
+ * ([BLOG] section 3.1: each expert is Linear -> GeLU -> Linear; [K3]: one
+ * always-on shared expert; FLOPs 4*rows*H*F + 4*T*H*Fs as in [K3]'s
+ * compute-time equation).
+ *   for each expert e and row p in [offsets[e], offsets[e+1]):
+ *     h      = GeLU(xs[p,:] . W1[e]^T)      GeLU(a) = 0.5*a*(1 + erf(a/sqrt(2)))
+ *     ys[p,:] = h . W2[e]^T
+ *   shared expert (when Fs > 0): ysh[t,:] = GeLU(x[t,:] . Ws1^T) . Ws2^T
+ * xs [rows,H], offsets [E+1] (device, from moe_dispatch; offsets[E] == rows)
+ * w1 [E,F,H], w2 [E,H,F]; x [T,H], ws1 [Fs,H], ws2 [H,Fs] (NULL / Fs = 0: no shared expert)
+ * ys [rows,H], ysh [T,H] (NULL when Fs = 0): device, written.
+ * In bf16 mode h is rounded to bf16 before the second Linear (fp32 accumulation
+ * in both); ys and ysh are rounded to bf16.
+ * ws / ws_bytes: device workspace of at least moe_expert_ffn_workspace_bytes(...)
+ */
+int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H, int F,
+                   const void* w1, const void* w2, const void* x, const void* ws1,
+                   const void* ws2, int T, int Fs, int dtype, void* ys, void* ysh, void* ws,
+                   size_t ws_bytes, void* stream);
+
+/*
+ * moe_combine - weighted combine back to token order ([K3] combine phase;
+ * [BLOG] section 3.1 "scatter back to the original positions").
+ *   out[t,:] = sum_{j=0..k-1} topk_w[t,j] * ys[inv[t*k+j],:]  (+ ysh[t,:])
+ * summed in fp32, j ascending, shared row last; one write per token (no atomics).
+ * ys [T*k,H] dtype, inv [T*k] int32, topk_w [T,k] fp32, ysh [T,H] dtype or NULL: device, read
+ * out [T,H] dtype: device, written
+ */
+int moe_combine(const void* ys, const int32_t* inv, const float* topk_w, const void* ysh, int T,
+                int H, int k, int dtype, void* out, void* stream);
+
+/*
+ * moe_load_stats - per-step load diagnostics ([DIAG] section 3) from the
+ * expert counts that moe_dispatch produced (the routing actually taken).
+ * counts        [E] int32            device, read (sum must be T*k)
+ * stats         moe_load_stats_t     device, written
+ * overflow      [E] int32 or NULL    device, written: max(0, counts[e] - capacity)
+ * straggler_ids [E] int32            device, written: ids with counts[e] > capacity,
+ *                                    ascending, then -1 up to E entries
+ * capacity_factor > 0.
+ */
+int moe_load_stats(const int32_t* counts, int T, int E, int k, double capacity_factor,
+                   moe_load_stats_t* stats, int32_t* overflow, int32_t* straggler_ids,
+                   void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H_ */

@@ -1,0 +1,230 @@
+"""ctypes binding of libmoe.so: argument marshalling only.
+
+Tensors are PyTorch device tensors (memory and streams only); every
+computation happens in the library's HIP kernels, enqueued on the current
+stream. Missing library or non-GPU tensors raise: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe.so")
+
+MOE_F32, MOE_BF16 = 0, 1
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+
+_vp, _i, _sz, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
+
+SIGNATURES = {
+    "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_dispatch_workspace_bytes": (_sz, [_i, _i, _i]),
+    "moe_dispatch": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
+    "moe_expert_ffn": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp,
+                            _vp, _vp, _sz, _vp]),
+    "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "moe_load_stats": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
+    "moe_status_string": (ctypes.c_char_p, [_i]),
+}
+
+
+class MoELoadStats(ctypes.Structure):
+    """Mirror of moe_load_stats_t."""
+    _fields_ = [(n, ctypes.c_int64) for n in
+                ["num_tokens", "assignments", "capacity", "max_load", "min_load", "dropped",
+                 "num_stragglers", "gini_num", "gini_den"]] + \
+               [(n, ctypes.c_double) for n in ["load_skew_ratio", "gini", "drop_rate"]]
+
+
+STATS_BYTES = ctypes.sizeof(MoELoadStats)
+
+
+class MoEError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn}: {STATUS.get(status, status)} ({moe_status_string(status)})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libmoe.so (built in-tree); raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m sparse_mixture_experts_05_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def moe_status_string(status: int) -> str:
+    return lib().moe_status_string(status).decode()
+
+
+def _check(fn: str, status: int):
+    if status != 0:
+        raise MoEError(fn, status)
+
+
+def _dev(t: torch.Tensor | None, name: str, dtype=None):
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cuda":
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOE_BF16
+    if t.dtype == torch.float32:
+        return MOE_F32
+    raise ValueError(f"unsupported dtype {t.dtype} (bf16 or fp32)")
+
+
+def _stream(stream):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, stream=None):
+    """Top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+    T, H = x.shape
+    E = wg.shape[0]
+    if topk_idx is None:
+        topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
+    if topk_w is None:
+        topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
+    dt = _dtype_code(x)
+    _check("moe_route", lib().moe_route(
+        _dev(x, "x"), _dev(wg, "wg", x.dtype), _dev(bias, "bias", torch.float32), T, H, E, k, dt,
+        _dev(topk_idx, "topk_idx", torch.int32), _dev(topk_w, "topk_w", torch.float32),
+        _stream(stream)))
+    return topk_idx, topk_w
+
+
+def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
+    return lib().moe_dispatch_workspace_bytes(T, E, k)
+
+
+def moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dtype_code) -> int:
+    return lib().moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dtype_code)
+
+
+def _workspace(nbytes: int, device, ws=None):
+    if ws is not None:
+        if ws.numel() * ws.element_size() < nbytes:
+            raise ValueError("workspace too small")
+        return ws
+    return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+
+
+def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None):
+    """Returns dict(counts, offsets, perm, inv, xs)."""
+    T, H = x.shape
+    k = topk_idx.shape[1]
+    dev = x.device
+    if out is None:
+        out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+                   inv=torch.empty(T * k, dtype=torch.int32, device=dev),
+                   xs=torch.empty((T * k, H), dtype=x.dtype, device=dev))
+    nbytes = moe_dispatch_workspace_bytes(T, E, k)
+    ws = _workspace(nbytes, dev, ws)
+    _check("moe_dispatch", lib().moe_dispatch(
+        _dev(topk_idx, "topk_idx", torch.int32), _dev(x, "x"), T, H, E, k, _dtype_code(x),
+        _dev(out["counts"], "counts", torch.int32), _dev(out["offsets"], "offsets", torch.int32),
+        _dev(out["perm"], "perm", torch.int32), _dev(out["inv"], "inv", torch.int32),
+        _dev(out["xs"], "xs", x.dtype), _dev(ws, "ws"), ws.numel(), _stream(stream)))
+    return out
+
+
+def moe_expert_ffn(xs, offsets, w1, w2, x=None, ws1=None, ws2=None, T=None, ys=None, ysh=None,
+                   ws=None, stream=None):
+    """Returns (ys [rows,H], ysh [T,H] or None)."""
+    rows, H = xs.shape
+    E, F, _ = w1.shape
+    Fs = 0 if ws1 is None else ws1.shape[0]
+    if T is None:
+        T = x.shape[0] if x is not None else rows
+    dt = _dtype_code(xs)
+    dev = xs.device
+    if ys is None:
+        ys = torch.empty((rows, H), dtype=xs.dtype, device=dev)
+    if Fs > 0 and ysh is None:
+        ysh = torch.empty((T, H), dtype=xs.dtype, device=dev)
+    nbytes = moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dt)
+    ws = _workspace(nbytes, dev, ws)
+    _check("moe_expert_ffn", lib().moe_expert_ffn(
+        _dev(xs, "xs"), _dev(offsets, "offsets", torch.int32), rows, E, H, F,
+        _dev(w1, "w1", xs.dtype), _dev(w2, "w2", xs.dtype), _dev(x, "x", xs.dtype),
+        _dev(ws1, "ws1", xs.dtype), _dev(ws2, "ws2", xs.dtype), T, Fs, dt, _dev(ys, "ys", xs.dtype),
+        _dev(ysh, "ysh", xs.dtype) if Fs > 0 else None, _dev(ws, "ws"), ws.numel(),
+        _stream(stream)))
+    return ys, (ysh if Fs > 0 else None)
+
+
+def moe_combine(ys, inv, topk_w, ysh=None, out=None, stream=None):
+    """Returns out [T,H]."""
+    T, k = topk_w.shape
+    H = ys.shape[1]
+    if out is None:
+        out = torch.empty((T, H), dtype=ys.dtype, device=ys.device)
+    _check("moe_combine", lib().moe_combine(
+        _dev(ys, "ys"), _dev(inv, "inv", torch.int32), _dev(topk_w, "topk_w", torch.float32),
+        _dev(ysh, "ysh", ys.dtype), T, H, k, _dtype_code(ys), _dev(out, "out", ys.dtype),
+        _stream(stream)))
+    return out
+
+
+def moe_load_stats(counts, T: int, k: int, capacity_factor: float, stats=None, overflow=None,
+                   straggler_ids=None, stream=None, read_back: bool = True):
+    """Enqueue the diagnostics; with read_back, synchronise and return a dict."""
+    E = counts.shape[0]
+    dev = counts.device
+    if stats is None:
+        stats = torch.empty(STATS_BYTES, dtype=torch.uint8, device=dev)
+    if overflow is None:
+        overflow = torch.empty(E, dtype=torch.int32, device=dev)
+    if straggler_ids is None:
+        straggler_ids = torch.empty(E, dtype=torch.int32, device=dev)
+    _check("moe_load_stats", lib().moe_load_stats(
+        _dev(counts, "counts", torch.int32), T, E, k, float(capacity_factor), _dev(stats, "stats"),
+        _dev(overflow, "overflow", torch.int32), _dev(straggler_ids, "straggler_ids", torch.int32),
+        _stream(stream)))
+    if not read_back:
+        return dict(stats=stats, overflow=overflow, straggler_ids=straggler_ids)
+    raw = MoELoadStats.from_buffer_copy(bytes(stats.cpu().numpy().tobytes()))
+    d = {name: getattr(raw, name) for name, _ in MoELoadStats._fields_}
+    d["overflow"] = overflow.cpu().tolist()
+    ids = straggler_ids.cpu().tolist()
+    d["straggler_ids"] = ids[: d["num_stragglers"]]
+    d["straggler_tail"] = ids[d["num_stragglers"]:]
+    return d
+
+
+def moe_layer_forward(x, wg, bias, w1, w2, k: int, ws1=None, ws2=None, stream=None):
+    """All five steps on one stream (no host synchronisation). Returns a dict."""
+    E = wg.shape[0]
+    idx, w = moe_route(x, wg, bias, k, stream=stream)
+    d = moe_dispatch(idx, x, E, stream=stream)
+    ys, ysh = moe_expert_ffn(d["xs"], d["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2,
+                             T=x.shape[0], stream=stream)
+    out = moe_combine(ys, d["inv"], w, ysh, stream=stream)
+    return dict(topk_idx=idx, topk_w=w, ys=ys, ysh=ysh, out=out, **d)

@@ -1,0 +1,127 @@
+// Step 4 - weighted combine back to the original token order.
+//
+// Method: "hncyxsy.com Kimi K3 fine-grained MoE" article, combine phase (the
+// expert outputs return to the token's owner and are summed with the routing
+// weights) and "lpqz.cn MoE engineering blog" section 3.1 (results are
+// scattered back to the original positions); the always-on shared expert's
+// row is added with weight 1.
+//
+// One wavefront per token. The token's k buffer rows are found through inv
+// (a gather, so every output row is written exactly once: no atomics, and a
+// fixed summation order j = 0..k-1, then the shared row). 16-byte loads and
+// stores; fp32 accumulation in registers.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void fma_bf16x8(float (&acc)[8], uint4 v, float w) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] = fmaf(w, bf16_to_f32(u[q] & 0xffffu), acc[2 * q]);
+    acc[2 * q + 1] = fmaf(w, bf16_to_f32(u[q] >> 16), acc[2 * q + 1]);
+  }
+}
+
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], uint4 v) {
+  const uint32_t u[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    acc[2 * q] += bf16_to_f32(u[q] & 0xffffu);
+    acc[2 * q + 1] += bf16_to_f32(u[q] >> 16);
+  }
+}
+
+// bf16: each 16-byte vector holds 8 values.
+__global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
+    const uint4* __restrict__ ys, const int32_t* __restrict__ inv, const float* __restrict__ w,
+    const uint4* __restrict__ ysh, int T, int vpr, int k, uint4* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int row[8];
+  float wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    row[j] = j < k ? min(max(inv[(size_t)t * k + j], 0), T * k - 1) : 0;
+    wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
+  }
+  for (int c = lane; c < vpr; c += kWave) {
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    uint4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) v[j] = ys[(size_t)row[j] * vpr + c];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (j < k) fma_bf16x8(acc, v[j], wt[j]);
+    if (ysh != nullptr) add_bf16x8(acc, ysh[(size_t)t * vpr + c]);
+    uint4 o;
+    o.x = pack_bf16x2(acc[0], acc[1]);
+    o.y = pack_bf16x2(acc[2], acc[3]);
+    o.z = pack_bf16x2(acc[4], acc[5]);
+    o.w = pack_bf16x2(acc[6], acc[7]);
+    out[(size_t)t * vpr + c] = o;
+  }
+}
+
+// fp32: each 16-byte vector holds 4 values.
+__global__ __launch_bounds__(kThreads) void combine_f32_kernel(
+    const float4* __restrict__ ys, const int32_t* __restrict__ inv, const float* __restrict__ w,
+    const float4* __restrict__ ysh, int T, int vpr, int k, float4* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int row[8];
+  float wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    row[j] = j < k ? min(max(inv[(size_t)t * k + j], 0), T * k - 1) : 0;
+    wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
+  }
+  for (int c = lane; c < vpr; c += kWave) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        const float4 v = ys[(size_t)row[j] * vpr + c];
+        acc.x = fmaf(wt[j], v.x, acc.x);
+        acc.y = fmaf(wt[j], v.y, acc.y);
+        acc.z = fmaf(wt[j], v.z, acc.z);
+        acc.w = fmaf(wt[j], v.w, acc.w);
+      }
+    }
+    if (ysh != nullptr) {
+      const float4 v = ysh[(size_t)t * vpr + c];
+      acc.x += v.x;
+      acc.y += v.y;
+      acc.z += v.z;
+      acc.w += v.w;
+    }
+    out[(size_t)t * vpr + c] = acc;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(const void* ys, const int32_t* inv, const float* topk_w,
+                          const void* ysh, int T, int H, int k, bool bf16, void* out,
+                          hipStream_t s) {
+  const int grid = (T + 3) / 4;
+  if (bf16) {
+    hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(ys), inv, topk_w, static_cast<const uint4*>(ysh),
+                       T, H / 8, k, static_cast<uint4*>(out));
+  } else {
+    hipLaunchKernelGGL(combine_f32_kernel, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const float4*>(ys), inv, topk_w,
+                       static_cast<const float4*>(ysh), T, H / 4, k, static_cast<float4*>(out));
+  }
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+// Step 2 - token dispatch: expert histogram, offsets, stable permutation and
+// the gather of token rows into one expert-contiguous buffer.
+//
+// Method: "lpqz.cn MoE engineering blog" section 3.1 (the dispatcher groups
+// token indices by expert id into one pre-allocated shared buffer, runs each
+// expert on its group and scatters results back to the original order) and
+// "Kimi K3 专家路由不均衡诊断" section 3 (per-expert hit counts). Here the buffer
+// is unpadded: expert e owns rows [offsets[e], offsets[e+1]), filled in
+// token order.
+//
+// Three launches, all deterministic (no order-dependent atomics):
+//   hist    - one workgroup per 256-token block: LDS-privatised histogram,
+//             written expert-major as blk[e * nb + b].
+//   rank    - one workgroup per block: every workgroup reads the whole
+//             [E x nb] table (tiny, L2 resident) to get the expert offsets
+//             (exclusive scan over experts) and its own prefix over earlier
+//             blocks; then each wave walks its 64 tokens' assignments in order,
+//             64 at a time, ranking equal expert ids with ballots (a lane's
+//             rank = earlier lanes with the same id) on top of per-wave running
+//             counters. Writes perm and inv (block 0 also counts and offsets).
+//   scatter - one wavefront per token: reads the token's row once with 16-byte
+//             loads and writes it to its k buffer rows.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+// Expert ids are in [0, E) by contract; clamping keeps a bad id from turning
+// into an out-of-range position (hist and rank must agree, so both clamp).
+__device__ __forceinline__ int expert_of(const int32_t* idx, int a, int E) {
+  return min(max(idx[a], 0), E - 1);
+}
+
+constexpr int kThreads = 256;
+constexpr int kBlockTokens = 256;  // tokens per hist/rank workgroup (64 per wave)
+
+__global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
+                                                        int E, int k, int nb,
+                                                        int32_t* __restrict__ blk) {
+  __shared__ int h[256];
+  for (int e = threadIdx.x; e < E; e += kThreads) h[e] = 0;
+  __syncthreads();
+  const int a0 = blockIdx.x * kBlockTokens * k;
+  const int a1 = min(T, (blockIdx.x + 1) * kBlockTokens) * k;
+  for (int a = a0 + threadIdx.x; a < a1; a += kThreads) atomicAdd(&h[expert_of(idx, a, E)], 1);
+  __syncthreads();
+  for (int e = threadIdx.x; e < E; e += kThreads) blk[(size_t)e * nb + blockIdx.x] = h[e];
+}
+
+__global__ __launch_bounds__(kThreads) void rank_kernel(
+    const int32_t* __restrict__ idx, int T, int E, int k, int nb, const int32_t* __restrict__ blk,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
+    int32_t* __restrict__ inv) {
+  __shared__ int tot[256];      // per-expert totals, then exclusive offsets
+  __shared__ int run[4][256];   // per-wave running positions
+  __shared__ int wcnt[4][256];  // per-wave counts
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int b = blockIdx.x;
+
+  // Totals over all blocks and this block's prefix over earlier blocks.
+  int total = 0, before = 0;
+  if (tid < E) {
+    const int32_t* row = blk + (size_t)tid * nb;
+    for (int i = 0; i < nb; ++i) {
+      const int c = row[i];
+      total += c;
+      if (i < b) before += c;
+    }
+  }
+  tot[tid] = tid < E ? total : 0;
+  for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+  __syncthreads();
+  // Exclusive scan of the totals over experts (Hillis-Steele on 256 entries).
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = tid >= d ? tot[tid - d] : 0;
+    __syncthreads();
+    tot[tid] += v;
+    __syncthreads();
+  }
+  const int excl = tot[tid] - (tid < E ? total : 0);
+  if (b == 0 && tid < E) {
+    counts[tid] = total;
+    offsets[tid] = excl;
+    if (tid == E - 1) offsets[E] = excl + total;
+  }
+
+  // Per-wave counts of this block (order-free integer adds).
+  const int tw0 = b * kBlockTokens + wave * 64;  // first token of this wave
+  const int a0 = min(tw0, T) * k, a1 = min(tw0 + 64, T) * k;
+  for (int a = a0 + lane; a < a1; a += 64) atomicAdd(&wcnt[wave][expert_of(idx, a, E)], 1);
+  __syncthreads();
+  if (tid < E) {
+    int base = excl + before;
+    for (int w = 0; w < 4; ++w) {
+      run[w][tid] = base;
+      base += wcnt[w][tid];
+    }
+  }
+  __syncthreads();
+
+  // Stable ranking: assignments of this wave in row-major (t, j) order.
+  int bits = 1;
+  while ((1 << bits) < E + 1) ++bits;  // ids 0..E-1 plus the idle-lane id E
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int c0 = a0; c0 < a1; c0 += 64) {
+    const int a = c0 + lane;
+    const bool valid = a < a1;
+    const int e = valid ? expert_of(idx, a, E) : E;
+    uint64_t peers = ~0ull;
+    for (int bt = 0; bt < bits; ++bt) {
+      const uint64_t bal = __ballot((e >> bt) & 1);
+      peers &= ((e >> bt) & 1) ? bal : ~bal;
+    }
+    const int rank = __popcll(peers & lt);
+    int pos = 0;
+    if (valid) pos = run[wave][e] + rank;
+    __builtin_amdgcn_wave_barrier();
+    if (valid && rank == 0) run[wave][e] = pos + __popcll(peers);
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      inv[a] = pos;
+      perm[pos] = a;
+    }
+  }
+}
+
+// One wavefront per token: read the row once, write it to its k buffer rows.
+template <typename V>
+__global__ __launch_bounds__(kThreads) void scatter_kernel(const V* __restrict__ x,
+                                                           const int32_t* __restrict__ inv,
+                                                           int T, int vec_per_row, int k,
+                                                           V* __restrict__ xs) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int dst[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dst[j] = j < k ? inv[(size_t)t * k + j] : 0;
+  const V* src = x + (size_t)t * vec_per_row;
+  for (int c = lane; c < vec_per_row; c += 4 * kWave) {
+    V v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (c + u * kWave < vec_per_row) v[u] = src[c + u * kWave];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        V* d = xs + (size_t)dst[j] * vec_per_row;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (c + u * kWave < vec_per_row) d[c + u * kWave] = v[u];
+      }
+    }
+  }
+}
+
+}  // namespace
+
+int dispatch_blocks(int T) { return (T + kBlockTokens - 1) / kBlockTokens; }
+
+size_t dispatch_ws_bytes(int T, int E) {
+  const size_t b = (size_t)E * dispatch_blocks(T) * sizeof(int32_t);
+  return (b + 255) & ~size_t(255);
+}
+
+hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
+                           bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int32_t* inv, void* xs, void* ws, hipStream_t s) {
+  const int nb = dispatch_blocks(T);
+  int32_t* blk = static_cast<int32_t*>(ws);
+  hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, blk);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, blk,
+                     counts, offsets, perm, inv);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int row_bytes = H * (bf16 ? 2 : 4);
+  const int grid = (T + 3) / 4;
+  hipLaunchKernelGGL(scatter_kernel<uint4>, dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const uint4*>(x), inv, T, row_bytes / 16, k,
+                     static_cast<uint4*>(xs));
+  return hipGetLastError();
+}
+
+}  // namespace moe

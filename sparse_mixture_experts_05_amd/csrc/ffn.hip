@@ -1,0 +1,387 @@
+// Step 3 - grouped expert FFN over the expert-contiguous buffer.
+//
+// Method: "lpqz.cn MoE engineering blog" section 3.1 (each expert is two
+// Linear layers with a GeLU between them) and the "hncyxsy.com Kimi K3
+// fine-grained MoE" article (top-8 of many small experts plus one always-on
+// shared expert; FFN cost 2*B*S*K*(2*H*D_ffn) FLOPs).
+//
+// Two launches of one grouped-GEMM kernel:
+//   up:   h[p, :]  = GeLU(xs[p, :] . W1[e]^T)   N = F,  K = H  (erf-GeLU epilogue)
+//   down: ys[p, :] = h[p, :] . W2[e]^T           N = H,  K = F
+// Each launch also carries the shared expert as one more group (x -> hs -> ysh).
+//
+// Tiles: workgroup g covers rows [row0, row0+BM) of one expert segment and
+// columns [n0, n0+BN). The expert of a tile is looked up on the device from
+// offsets (per-expert tile counts, LDS scan), so the host never reads the
+// routing. The grid is sized for the worst case (sum over experts of
+// ceil(count/BM) <= rows/BM + E); surplus workgroups exit at once.
+//
+// bf16 path: v_mfma_f32_32x32x16_bf16, 4 waves in a WM x WN grid, operand
+// tiles of BK = 64 staged in LDS, double buffered (global loads of step k+1
+// in flight while step k runs on the matrix cores), 16-byte chunks XOR
+// swizzled by row so fragment reads are bank-conflict free. Rows past the
+// segment end are clamped on load and masked on store.
+// fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+
+struct Group {
+  const void* A;  // [M, K] rows (routed: the whole buffer; shared: x or hs)
+  const void* B;  // routed: [E, N, K]; shared: [N, K]
+  void* C;        // [M, N]
+  int N, K;
+};
+
+struct GemmArgs {
+  Group routed, shared;
+  const int32_t* offsets;  // [E+1]
+  int E;
+  int rows;          // rows of the routed buffer
+  int routed_tiles;  // grid share of the routed group: mtiles_max * ntiles
+  int shared_M;      // 0 = no shared group
+  int gelu;
+};
+
+struct Tile {
+  int group;  // 0 routed, 1 shared
+  int e;      // expert (routed)
+  int row0;   // first row of the tile in A / C
+  int M;      // valid rows in this tile (<= BM)
+  int n0;     // first column
+};
+
+// Field-wise select (a reference into the kernel arguments chosen at run time
+// would force a private-memory copy of the whole struct).
+__device__ __forceinline__ Group pick_group(const GemmArgs& a, int group) {
+  Group g;
+  g.A = group ? a.shared.A : a.routed.A;
+  g.B = group ? a.shared.B : a.routed.B;
+  g.C = group ? a.shared.C : a.routed.C;
+  g.N = group ? a.shared.N : a.routed.N;
+  g.K = group ? a.shared.K : a.routed.K;
+  return g;
+}
+
+// Finds the tile of this workgroup. Returns false if it has no work.
+template <int BM, int BN>
+__device__ bool find_tile(const GemmArgs& a, Tile& t) {
+  __shared__ int pre[256];
+  __shared__ int sel[3];
+  const int g = blockIdx.x;
+  if (g >= a.routed_tiles) {
+    const int gs = g - a.routed_tiles;
+    const int ntn = (a.shared.N + BN - 1) / BN;
+    t.group = 1;
+    t.e = 0;
+    t.row0 = (gs / ntn) * BM;
+    t.M = min(BM, a.shared_M - t.row0);
+    t.n0 = (gs % ntn) * BN;
+    return t.M > 0;
+  }
+  const int ntn = (a.routed.N + BN - 1) / BN;
+  const int mt = g / ntn;
+  const int tid = threadIdx.x;
+  int off = 0, cnt = 0, tiles = 0;
+  if (tid < a.E) {
+    // offsets come from the dispatch step; clamping keeps any segment inside
+    // the buffer even if a caller passes inconsistent offsets
+    off = min(max(a.offsets[tid], 0), a.rows);
+    cnt = min(max(a.offsets[tid + 1], off), a.rows) - off;
+    tiles = (cnt + BM - 1) / BM;
+  }
+  pre[tid] = tiles;
+  if (tid == 0) sel[0] = -1;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = tid >= d ? pre[tid - d] : 0;
+    __syncthreads();
+    pre[tid] += v;
+    __syncthreads();
+  }
+  if (tid < a.E) {
+    const int incl = pre[tid], excl = incl - tiles;
+    if (mt >= excl && mt < incl) {
+      sel[0] = tid;
+      sel[1] = off + (mt - excl) * BM;
+      sel[2] = min(BM, cnt - (mt - excl) * BM);
+    }
+  }
+  __syncthreads();
+  t.group = 0;
+  t.e = sel[0];
+  t.row0 = sel[1];
+  t.M = sel[2];
+  t.n0 = (g % ntn) * BN;
+  return t.e >= 0;
+}
+
+// ----------------------------------------------------------------- bf16 MFMA
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
+  constexpr int BK = 64;                      // bf16 elements per K step
+  constexpr int ROWB = BK * 2;                // bytes per staged row (128)
+  constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
+  constexpr int SM = WTM / 32, SN = WTN / 32; // 32x32 sub-tiles per wave
+  constexpr int A_LD = BM * (ROWB / 16) / kThreads;  // 16-byte chunks per thread
+  constexpr int B_LD = BN * (ROWB / 16) / kThreads;
+  constexpr int STAGE = (BM + BN) * ROWB;
+  static_assert(WM * WN == 4, "4 waves");
+  static_assert(SM >= 1 && SN >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  Tile t;
+  if (!find_tile<BM, BN>(args, t)) return;
+  const Group G = pick_group(args, t.group);
+  const int N = G.N, K = G.K;
+  const uint16_t* A = static_cast<const uint16_t*>(G.A) + (size_t)t.row0 * K;
+  const uint16_t* B = static_cast<const uint16_t*>(G.B) + (size_t)t.e * N * K + (size_t)t.n0 * K;
+  uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
+  const int M = t.M;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+
+  // Global source pointers and LDS destinations of this thread's chunks.
+  const uint16_t* ga[A_LD];
+  const uint16_t* gb[B_LD];
+  int la[A_LD], lb[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) {
+    const int q = tid + i * kThreads, r = q >> 3, c = q & 7;
+    ga[i] = A + (size_t)min(r, M - 1) * K + c * 8;
+    la[i] = r * ROWB + ((c ^ (r & 7)) << 4);
+  }
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int q = tid + i * kThreads, r = q >> 3, c = q & 7;
+    gb[i] = B + (size_t)min(r, N - t.n0 - 1) * K + c * 8;
+    lb[i] = BM * ROWB + r * ROWB + ((c ^ (r & 7)) << 4);
+  }
+
+  f32x16_t acc[SM][SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  u32x4_t ra[A_LD], rb[B_LD];
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) ra[i] = ld16(ga[i]);
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) rb[i] = ld16(gb[i]);
+#pragma unroll
+  for (int i = 0; i < A_LD; ++i) st16(smem + la[i], ra[i]);
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) st16(smem + lb[i], rb[i]);
+  __syncthreads();
+
+  // Fragment rows (A: tile rows, B: tile columns) of this lane.
+  int fa[SM], fb[SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i) fa[i] = wm * WTM + i * 32 + (lane & 31);
+#pragma unroll
+  for (int j = 0; j < SN; ++j) fb[j] = BM + wn * WTN + j * 32 + (lane & 31);
+  const int khalf = lane >> 5;
+
+  const int KT = K / BK;
+  for (int kt = 0; kt < KT; ++kt) {
+    const int cur = (kt & 1) * STAGE;
+    const bool more = kt + 1 < KT;
+    if (more) {
+      const int k1 = (kt + 1) * BK;
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) ra[i] = ld16(ga[i] + k1);
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) rb[i] = ld16(gb[i] + k1);
+    }
+#pragma unroll
+    for (int ks = 0; ks < BK / 16; ++ks) {
+      const int chunk = ks * 2 + khalf;
+      u32x4_t fra[SM], frb[SN];
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+        fra[i] = ld16(smem + cur + fa[i] * ROWB + ((chunk ^ (fa[i] & 7)) << 4));
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+        frb[j] = ld16(smem + cur + fb[j] * ROWB + ((chunk ^ (fb[j] & 7)) << 4));
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+#pragma unroll
+        for (int j = 0; j < SN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fra[i]),
+                                                              as_bf16x8(frb[j]), acc[i][j], 0, 0, 0);
+    }
+    if (more) {
+      const int nxt = ((kt + 1) & 1) * STAGE;
+#pragma unroll
+      for (int i = 0; i < A_LD; ++i) st16(smem + nxt + la[i], ra[i]);
+#pragma unroll
+      for (int i = 0; i < B_LD; ++i) st16(smem + nxt + lb[i], rb[i]);
+    }
+    __syncthreads();
+  }
+
+  // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
+  // (v/4)*8 + (lane/32)*4 + v%4 of each sub-tile.
+  const bool gelu = args.gelu != 0;
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int col = wn * WTN + j * 32 + (lane & 31);
+      if (t.n0 + col >= N) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (row < M) {
+          float y = acc[i][j][v];
+          if (gelu) y = gelu_erf(y);
+          C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
+        }
+      }
+    }
+}
+
+// ----------------------------------------------------------------- fp32 VALU
+
+__global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs args) {
+  constexpr int BM = 64, BN = 64, BK = 16;
+  __shared__ float As[BK][BM + 4];
+  __shared__ float Bs[BK][BN + 4];
+  Tile t;
+  if (!find_tile<BM, BN>(args, t)) return;
+  const Group G = pick_group(args, t.group);
+  const int N = G.N, K = G.K;
+  const float* A = static_cast<const float*>(G.A) + (size_t)t.row0 * K;
+  const float* B = static_cast<const float*>(G.B) + (size_t)t.e * N * K + (size_t)t.n0 * K;
+  float* C = static_cast<float*>(G.C) + (size_t)t.row0 * N + t.n0;
+  const int M = t.M;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row, first k of a float4
+  const float* ga = A + (size_t)min(lr, M - 1) * K + lk;
+  const float* gb = B + (size_t)min(lr, N - t.n0 - 1) * K + lk;
+  float acc[4][4] = {};
+  for (int k0 = 0; k0 < K; k0 += BK) {
+    const float4 va = *reinterpret_cast<const float4*>(ga + k0);
+    const float4 vb = *reinterpret_cast<const float4*>(gb + k0);
+    As[lk + 0][lr] = va.x;
+    As[lk + 1][lr] = va.y;
+    As[lk + 2][lr] = va.z;
+    As[lk + 3][lr] = va.w;
+    Bs[lk + 0][lr] = vb.x;
+    Bs[lk + 1][lr] = vb.y;
+    Bs[lk + 2][lr] = vb.z;
+    Bs[lk + 3][lr] = vb.w;
+    __syncthreads();
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) b[j] = Bs[kk][tx * 4 + j];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = ty * 4 + i;
+    if (row >= M) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int col = tx * 4 + j;
+      if (t.n0 + col >= N) continue;
+      float y = acc[i][j];
+      if (args.gelu) y = gelu_erf(y);
+      C[(size_t)row * N + col] = y;
+    }
+  }
+}
+
+// ----------------------------------------------------------------- host side
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+template <int BM, int BN>
+void grid_of(GemmArgs& a, int rows, int E, dim3& grid) {
+  const int mt_max = rows / BM + E;  // sum_e ceil(c_e / BM) <= rows / BM + E
+  a.routed_tiles = mt_max * ((a.routed.N + BN - 1) / BN);
+  const int shared_tiles =
+      a.shared_M > 0 ? ((a.shared_M + BM - 1) / BM) * ((a.shared.N + BN - 1) / BN) : 0;
+  grid = dim3(a.routed_tiles + shared_tiles);
+}
+
+template <int BM, int BN, int WM, int WN>
+hipError_t run_bf16(GemmArgs a, int rows, int E, hipStream_t s) {
+  dim3 grid;
+  grid_of<BM, BN>(a, rows, E, grid);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_segments,
+                    hipStream_t s) {
+  if (!bf16) {
+    GemmArgs b = a;
+    dim3 grid;
+    grid_of<64, 64>(b, rows, E, grid);
+    hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kThreads), 0, s, b);
+    return hipGetLastError();
+  }
+  if (small_segments) return run_bf16<32, 128, 1, 4>(a, rows, E, s);
+  return run_bf16<128, 128, 2, 2>(a, rows, E, s);
+}
+
+}  // namespace
+
+size_t ffn_ws_bytes(int rows, int T, int F, int Fs, bool bf16) {
+  const size_t es = bf16 ? 2 : 4;
+  return align256((size_t)rows * F * es) + align256((size_t)T * Fs * es);
+}
+
+hipError_t launch_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H,
+                             int F, const void* w1, const void* w2, const void* x,
+                             const void* ws1, const void* ws2, int T, int Fs, bool bf16,
+                             void* ys, void* ysh, void* ws, hipStream_t s) {
+  const size_t es = bf16 ? 2 : 4;
+  uint8_t* h = static_cast<uint8_t*>(ws);
+  uint8_t* hs = h + align256((size_t)rows * F * es);
+  const bool shared = Fs > 0;
+  // Few rows per expert on average: decode-like, weight-streaming bound.
+  const bool small_segments = (long long)rows < 64LL * E;
+
+  GemmArgs up{};
+  up.routed = Group{xs, w1, h, F, H};
+  up.shared = Group{x, ws1, hs, Fs, H};
+  up.offsets = offsets;
+  up.E = E;
+  up.rows = rows;
+  up.shared_M = shared ? T : 0;
+  up.gelu = 1;
+  hipError_t err = run_gemm(up, rows, E, bf16, small_segments, s);
+  if (err != hipSuccess) return err;
+
+  GemmArgs down{};
+  down.routed = Group{h, w2, ys, H, F};
+  down.shared = Group{hs, ws2, ysh, H, Fs};
+  down.offsets = offsets;
+  down.E = E;
+  down.rows = rows;
+  down.shared_M = shared ? T : 0;
+  down.gelu = 0;
+  return run_gemm(down, rows, E, bf16, small_segments, s);
+}
+
+}  // namespace moe

@@ -1,0 +1,122 @@
+// C ABI of the MoE layer library: argument validation (always before any HIP
+// call, so a rejected call enqueues nothing), workspace sizing, launches on
+// the caller's stream. The semantics of each entry point are documented in
+// include/moe.h.
+#include "moe.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+
+#include "kernels.hpp"
+
+namespace {
+
+constexpr int kMaxExperts = 256;
+constexpr int kMaxTopK = 8;
+
+bool dtype_ok(int dt) { return dt == MOE_F32 || dt == MOE_BF16; }
+
+// Shared shape checks of (T, H, E, k). Returns MOE_OK or an error status.
+int check_tokens(int T, int H, int E, int k) {
+  if (T < 1 || H < 1 || E < 1 || k < 1) return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || k > kMaxTopK || k > E) return MOE_ERR_UNSUPPORTED;
+  if (H % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((long long)T * k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_string(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or bad dtype)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported shape (needs 1<=E<=256, 1<=k<=min(E,8), H%64==0, F%64==0, T*k<2^31)";
+    case MOE_ERR_WORKSPACE: return "workspace missing or smaller than the size query returned";
+    case MOE_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_route(const void* x, const void* wg, const float* bias, int T, int H, int E, int k,
+              int dtype, int32_t* topk_idx, float* topk_w, void* stream) {
+  if (!x || !wg || !topk_idx || !topk_w || !dtype_ok(dtype)) return MOE_ERR_INVALID_ARG;
+  const int st = check_tokens(T, H, E, k);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_route(x, wg, bias, T, H, E, k, dtype == MOE_BF16, topk_idx, topk_w,
+                                    as_stream(stream)));
+}
+
+size_t moe_dispatch_workspace_bytes(int T, int E, int k) {
+  if (check_tokens(T, 64, E, k) != MOE_OK) return 0;
+  return moe::dispatch_ws_bytes(T, E);
+}
+
+int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k, int dtype,
+                 int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* xs,
+                 void* ws, size_t ws_bytes, void* stream) {
+  if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !xs || !dtype_ok(dtype))
+    return MOE_ERR_INVALID_ARG;
+  const int st = check_tokens(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  return from_hip(moe::launch_dispatch(topk_idx, x, T, H, E, k, dtype == MOE_BF16, counts,
+                                       offsets, perm, inv, xs, ws, as_stream(stream)));
+}
+
+static int check_ffn(int rows, int T, int H, int E, int F, int Fs, int dtype) {
+  if (rows < 1 || T < 1 || H < 1 || E < 1 || F < 1 || Fs < 0 || !dtype_ok(dtype))
+    return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts || H % 64 != 0 || F % 64 != 0 || Fs % 64 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((long long)rows > (long long)T * kMaxTopK) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+size_t moe_expert_ffn_workspace_bytes(int rows, int T, int H, int E, int F, int Fs, int dtype) {
+  if (check_ffn(rows, T, H, E, F, Fs, dtype) != MOE_OK) return 0;
+  return moe::ffn_ws_bytes(rows, T, F, Fs, dtype == MOE_BF16);
+}
+
+int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H, int F,
+                   const void* w1, const void* w2, const void* x, const void* ws1,
+                   const void* ws2, int T, int Fs, int dtype, void* ys, void* ysh, void* ws,
+                   size_t ws_bytes, void* stream) {
+  if (!xs || !offsets || !w1 || !w2 || !ys) return MOE_ERR_INVALID_ARG;
+  const int st = check_ffn(rows, T, H, E, F, Fs, dtype);
+  if (st != MOE_OK) return st;
+  if (Fs > 0 && (!x || !ws1 || !ws2 || !ysh)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, F, Fs, dtype == MOE_BF16))
+    return MOE_ERR_WORKSPACE;
+  return from_hip(moe::launch_expert_ffn(xs, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T, Fs,
+                                         dtype == MOE_BF16, ys, Fs > 0 ? ysh : nullptr, ws,
+                                         as_stream(stream)));
+}
+
+int moe_combine(const void* ys, const int32_t* inv, const float* topk_w, const void* ysh, int T,
+                int H, int k, int dtype, void* out, void* stream) {
+  if (!ys || !inv || !topk_w || !out || !dtype_ok(dtype)) return MOE_ERR_INVALID_ARG;
+  const int st = check_tokens(T, H, kMaxTopK, k);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_combine(ys, inv, topk_w, ysh, T, H, k, dtype == MOE_BF16, out,
+                                      as_stream(stream)));
+}
+
+int moe_load_stats(const int32_t* counts, int T, int E, int k, double capacity_factor,
+                   moe_load_stats_t* stats, int32_t* overflow, int32_t* straggler_ids,
+                   void* stream) {
+  if (!counts || !stats || !straggler_ids) return MOE_ERR_INVALID_ARG;
+  if (!(capacity_factor > 0.0) || !std::isfinite(capacity_factor)) return MOE_ERR_INVALID_ARG;
+  const int st = check_tokens(T, 64, E, k);
+  if (st != MOE_OK) return st;
+  return from_hip(moe::launch_load_stats(counts, T, E, k, capacity_factor, stats, overflow,
+                                         straggler_ids, as_stream(stream)));
+}
+
+}  // extern "C"

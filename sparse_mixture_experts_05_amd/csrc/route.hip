@@ -1,0 +1,306 @@
+// Step 1 - router gating: scores, softmax over experts, top-k, renormalisation.
+//
+// Method: "hncyxsy.com Kimi K3 fine-grained MoE" article, router listing
+// (gate Linear without bias, softmax over all experts, top-k, divide the k
+// weights by their sum) and "Kimi K3 专家路由不均衡诊断" section 4.2 (the
+// per-expert bias B is added inside the softmax).
+//
+// The k renormalised weights are exp(s_j - m) / sum_j' exp(s_j' - m) with
+// m = max_e s_e: the full-E softmax denominator cancels, so only the k chosen
+// scores are exponentiated. Selection runs on the scores s (exp is monotone).
+//
+// Layout of the work: one workgroup of 256 threads owns BT tokens.
+//   phase 1: scores [BT x E] into LDS. bf16: MFMA 16x16x32 tiles (tokens x
+//            experts, K = H), fp32 accumulation, operands straight from
+//            global memory (x rows are shared by the 4 waves through L1,
+//            Wg comes from L2). fp32: plain dot products.
+//   phase 2: one wavefront per token; every lane holds up to 4 scores
+//            (E <= 256); k rounds of a wave-wide arg-max done in registers
+//            with DPP (quad_perm, row mirrors) and ds_swizzle, lanes 0/32
+//            merged with readlane. Ties go to the lower expert id.
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace moe {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxE = 256;
+constexpr int kLogitStride = kMaxE + 4;  // LDS row stride (floats) of the score tile
+
+__device__ __forceinline__ void take_better(float& v, int& i, float ov, int oi) {
+  if (ov > v || (ov == v && oi < i)) {
+    v = ov;
+    i = oi;
+  }
+}
+
+template <int CTRL>
+__device__ __forceinline__ void dpp_step(float& v, int& i) {
+  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
+  take_better(v, i, ov, oi);
+}
+
+// All 64 lanes end with the wave's best (v, i).
+__device__ __forceinline__ void wave_argmax(float& v, int& i) {
+  dpp_step<0xB1>(v, i);   // quad_perm [1,0,3,2]: lane ^ 1
+  dpp_step<0x4E>(v, i);   // quad_perm [2,3,0,1]: lane ^ 2
+  dpp_step<0x141>(v, i);  // row_half_mirror: pairs the two quads of each 8
+  dpp_step<0x140>(v, i);  // row_mirror: pairs the two 8-lane halves of each row
+  {                       // ds_swizzle bit-mask mode, xor 16: pairs the rows of each 32
+    const float ov = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    const int oi = __builtin_amdgcn_ds_swizzle(i, 0x401F);
+    take_better(v, i, ov, oi);
+  }
+  const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const int i0 = __builtin_amdgcn_readlane(i, 0);
+  const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const int i1 = __builtin_amdgcn_readlane(i, 32);
+  v = v0;
+  i = i0;
+  take_better(v, i, v1, i1);
+}
+
+// Best live slot of this lane. Slots that are out of range or already taken
+// are dead and never win (a NaN score is read as -inf, so every live slot
+// beats every dead one and the k ids are always distinct and < E).
+__device__ __forceinline__ void lane_best(const float (&v)[4], unsigned alive, int lane, float& bv,
+                                          int& bi) {
+  bv = -INFINITY;
+  bi = 0x7fffffff;
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    if (alive & (1u << q)) {
+      const int i = lane + 64 * q;
+      if (v[q] > bv || bi == 0x7fffffff) {
+        bv = v[q];
+        bi = i;
+      }
+    }
+}
+
+// Phase 2: scores of BT tokens are in LDS (row-major, kLogitStride).
+__device__ __forceinline__ void topk_phase(const float* sc, int BT, int t0, int T, int E, int k,
+                                           const float* __restrict__ bias,
+                                           int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_w) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float b[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int e = lane + 64 * q;
+    b[q] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
+  }
+  for (int t = wave; t < BT; t += kThreads / kWave) {
+    const int tok = t0 + t;
+    if (tok >= T) break;
+    float v[4];
+    unsigned alive = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      const float s = e < E ? sc[t * kLogitStride + e] + b[q] : -INFINITY;
+      v[q] = s == s ? s : -INFINITY;
+      if (e < E) alive |= 1u << q;
+    }
+    float bv;
+    int bi;
+    lane_best(v, alive, lane, bv, bi);
+    float sv[8];
+    int si[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        float wv = bv;
+        int wi = bi;
+        wave_argmax(wv, wi);
+        sv[j] = wv;
+        si[j] = wi;
+        if ((wi & 63) == lane) {
+          alive &= ~(1u << (wi >> 6));
+          lane_best(v, alive, lane, bv, bi);
+        }
+      }
+    }
+    const float m = sv[0];
+    float ex[8];
+    float sum = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k) {
+        ex[j] = expf(sv[j] - m);
+        sum += ex[j];
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < k && lane == j) {
+        topk_idx[(size_t)tok * k + j] = si[j];
+        topk_w[(size_t)tok * k + j] = ex[j] / sum;
+      }
+    }
+  }
+}
+
+// bf16 scores with MFMA. MC: 16-token row chunks per workgroup; NCW: 16-expert
+// column chunks per wave; KSPLIT: 1 = each wave owns NCW column chunks over
+// all of H, 4 = the 4 waves split the K steps (interleaved) and the partial
+// tiles are summed in a fixed order.
+template <int MC, int NCW, int KSPLIT>
+__global__ __launch_bounds__(kThreads) void route_bf16_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
+    const float* __restrict__ bias, int T, int H, int E, int k, int32_t* __restrict__ topk_idx,
+    float* __restrict__ topk_w) {
+  constexpr int BT = MC * 16;
+  __shared__ float sc[BT * kLogitStride];
+  __shared__ float part[KSPLIT == 4 ? 4 * BT * 48 : 1];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * BT;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int c0 = KSPLIT == 4 ? 0 : wave * NCW * 16;  // first expert column of this wave
+
+  const uint16_t* arow[MC];
+#pragma unroll
+  for (int r = 0; r < MC; ++r) arow[r] = x + (size_t)min(t0 + r * 16 + r16, T - 1) * H + kq;
+  const uint16_t* brow[NCW];
+#pragma unroll
+  for (int c = 0; c < NCW; ++c) brow[c] = wg + (size_t)min(c0 + c * 16 + r16, E - 1) * H + kq;
+
+  f32x4_t acc[MC][NCW];
+#pragma unroll
+  for (int r = 0; r < MC; ++r)
+#pragma unroll
+    for (int c = 0; c < NCW; ++c) acc[r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const bool active = KSPLIT == 4 || c0 < E;
+  if (active) {
+    const int nsteps = H / 32;
+    const int s0 = KSPLIT == 4 ? wave : 0;
+    for (int s = s0; s < nsteps; s += KSPLIT) {
+      const int kk = s * 32;
+      u32x4_t a[MC], b[NCW];
+#pragma unroll
+      for (int r = 0; r < MC; ++r) a[r] = ld16(arow[r] + kk);
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) b[c] = ld16(brow[c] + kk);
+#pragma unroll
+      for (int r = 0; r < MC; ++r)
+#pragma unroll
+        for (int c = 0; c < NCW; ++c)
+          acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[r]), as_bf16x8(b[c]),
+                                                              acc[r][c], 0, 0, 0);
+    }
+  }
+  // D layout of 16x16: lane holds column lane%16, rows (lane/16)*4 + v.
+  if (KSPLIT == 1) {
+    if (active) {
+#pragma unroll
+      for (int r = 0; r < MC; ++r)
+#pragma unroll
+        for (int c = 0; c < NCW; ++c) {
+          const int col = c0 + c * 16 + r16;
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int row = r * 16 + (lane >> 4) * 4 + v;
+            if (col < E) sc[row * kLogitStride + col] = acc[r][c][v];
+          }
+        }
+    }
+    __syncthreads();
+  } else {
+#pragma unroll
+    for (int r = 0; r < MC; ++r)
+#pragma unroll
+      for (int c = 0; c < NCW; ++c)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = r * 16 + (lane >> 4) * 4 + v;
+          part[(wave * BT + row) * 48 + c * 16 + r16] = acc[r][c][v];
+        }
+    __syncthreads();
+    for (int p = threadIdx.x; p < BT * E; p += kThreads) {
+      const int row = p / E, col = p % E;
+      float s = part[(0 * BT + row) * 48 + col];
+      s += part[(1 * BT + row) * 48 + col];
+      s += part[(2 * BT + row) * 48 + col];
+      s += part[(3 * BT + row) * 48 + col];
+      sc[row * kLogitStride + col] = s;
+    }
+    __syncthreads();
+  }
+  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w);
+}
+
+// fp32 scores with plain dot products (small fp32 layers).
+__global__ __launch_bounds__(kThreads) void route_f32_kernel(
+    const float* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
+    int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+  constexpr int BT = 16;
+  __shared__ float sc[BT * kLogitStride];
+  const int t0 = blockIdx.x * BT;
+  for (int p = threadIdx.x; p < BT * E; p += kThreads) {
+    const int t = p / E, e = p % E;
+    const float4* xr = reinterpret_cast<const float4*>(x + (size_t)min(t0 + t, T - 1) * H);
+    const float4* wr = reinterpret_cast<const float4*>(wg + (size_t)e * H);
+    float s = 0.0f;
+    for (int h = 0; h < H / 4; ++h) {
+      const float4 a = xr[h], b = wr[h];
+      s = fmaf(a.x, b.x, s);
+      s = fmaf(a.y, b.y, s);
+      s = fmaf(a.z, b.z, s);
+      s = fmaf(a.w, b.w, s);
+    }
+    sc[t * kLogitStride + e] = s;
+  }
+  __syncthreads();
+  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w);
+}
+
+template <int MC, int NCW, int KSPLIT>
+hipError_t launch_bf16(const void* x, const void* wg, const float* bias, int T, int H, int E,
+                       int k, int32_t* idx, float* w, hipStream_t s) {
+  const int grid = (T + MC * 16 - 1) / (MC * 16);
+  hipLaunchKernelGGL((route_bf16_kernel<MC, NCW, KSPLIT>), dim3(grid), dim3(kThreads), 0, s,
+                     static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, T,
+                     H, E, k, idx, w);
+  return hipGetLastError();
+}
+
+template <int MC>
+hipError_t launch_bf16_mc(const void* x, const void* wg, const float* bias, int T, int H, int E,
+                          int k, int32_t* idx, float* w, hipStream_t s) {
+  const int nc = (E + 15) / 16;
+  if (nc < 4) {
+    switch (nc) {
+      case 1: return launch_bf16<MC, 1, 4>(x, wg, bias, T, H, E, k, idx, w, s);
+      case 2: return launch_bf16<MC, 2, 4>(x, wg, bias, T, H, E, k, idx, w, s);
+      default: return launch_bf16<MC, 3, 4>(x, wg, bias, T, H, E, k, idx, w, s);
+    }
+  }
+  switch ((nc + 3) / 4) {
+    case 1: return launch_bf16<MC, 1, 1>(x, wg, bias, T, H, E, k, idx, w, s);
+    case 2: return launch_bf16<MC, 2, 1>(x, wg, bias, T, H, E, k, idx, w, s);
+    case 3: return launch_bf16<MC, 3, 1>(x, wg, bias, T, H, E, k, idx, w, s);
+    default: return launch_bf16<MC, 4, 1>(x, wg, bias, T, H, E, k, idx, w, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_route(const void* x, const void* wg, const float* bias, int T, int H, int E,
+                        int k, bool bf16, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+  if (!bf16) {
+    const int grid = (T + 15) / 16;
+    hipLaunchKernelGGL(route_f32_kernel, dim3(grid), dim3(kThreads), 0, s,
+                       static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, H, E,
+                       k, topk_idx, topk_w);
+    return hipGetLastError();
+  }
+  // Tokens per workgroup: as many as keep >= 256 workgroups (one per CU).
+  if (T >= 64 * 256) return launch_bf16_mc<4>(x, wg, bias, T, H, E, k, topk_idx, topk_w, s);
+  if (T >= 32 * 256) return launch_bf16_mc<2>(x, wg, bias, T, H, E, k, topk_idx, topk_w, s);
+  return launch_bf16_mc<1>(x, wg, bias, T, H, E, k, topk_idx, topk_w, s);
+}
+
+}  // namespace moe

@@ -15,7 +15,7 @@ import functools
 import numpy as np
 
 import oracle
-from synth import get_config, make_layer, redraw_rows
+from synth import MoEConfig, get_config, make_layer, redraw_rows
 
 GAP = 1e-3
 MAX_ATTEMPTS = 64
@@ -52,12 +52,17 @@ def condition_x(cfg, L: dict) -> int:
 
 
 @functools.lru_cache(maxsize=2)
-def conditioned_layer(name: str, weights: bool = True):
+def conditioned_layer(name, weights: bool = True):
     """(cfg, layer dict, redrawn count) with x conditioned by the gap rule.
 
-    Decode configs (decode@T<n>) condition the 128-row draw once and use a
-    prefix, so every T of the sweep sees the same token rows.
+    ``name`` is a config name or a MoEConfig. Decode configs (decode@T<n>)
+    condition the 128-row draw once and use a prefix, so every T of the sweep
+    sees the same token rows.
     """
+    if isinstance(name, MoEConfig):
+        cfg = name
+        L = make_layer(cfg, weights=weights)
+        return cfg, L, condition_x(cfg, L)
     cfg = get_config(name)
     if name.startswith("decode"):
         full = get_config("decode")
