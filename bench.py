@@ -1,0 +1,262 @@
+"""Benchmark of the MoE FFN layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the whole layer over one batch: route, dispatch, grouped
+expert FFN, combine and load stats (left on the device), all on one stream
+with inputs already resident in HBM. W untimed warm-up steps, then exactly K
+timed steps between two device synchronisations; HIP events on the same
+stream time every call of every timed step.
+
+Default workload: the Mixtral-8x7B-shaped layer (T=4096, H=4096, E=8, top-2,
+d_ff=14336, bf16 with fp32 accumulation), random weights and inputs from the
+seeded generator. Prints one JSON line:
+  value        tokens/s of the whole layer (T*K / elapsed)
+  roofline     the dominant kernel, the bf16 MFMA grouped GEMM (launched twice
+               per step: up and down projections, 2*rows*H*F flops each),
+               against the dense bf16 MFMA peak of 2500 TFLOP/s
+  kernels      per-call average ms and the achieved fraction of its roofline
+  cpu_baseline the float64 CPU oracle on a bounded sample of the same workload
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+FP32_PEAK_TFLOPS = 157.3
+CPU_TARGET_S = 15.0
+DOMINANT_KERNEL = "gemm_bf16_kernel"
+PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_mixtral_8x7b_pmc.md")
+GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc", "ffn.hip")
+
+
+def algorithmic_work(cfg, counts=None):
+    """Bytes / flops each step must move or compute (per call).
+
+    route:    x once + Wg + bias + ids/weights out
+    dispatch: ids in, x once, xs out, perm + inv out, counts + offsets out
+    ffn:      4*rows*H*F + 4*T*H*Fs flops (the up and down projections)
+    combine:  ys in, inv + weights in, shared rows in, out
+    """
+    T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    b = 2 if cfg.dtype == "bf16" else 4
+    rows = T * k
+    route = T * H * b + E * H * b + (4 * E if cfg.bias_amp else 0) + 8 * rows
+    dispatch = 4 * rows + T * H * b + rows * H * b + 8 * rows + 4 * (2 * E + 1)
+    ffn_flops = 4 * rows * H * F + 4 * T * H * Fs
+    live = E if counts is None else int((counts > 0).sum())
+    ffn_bytes = 2 * H * F * b * live + 2 * H * Fs * b + 2 * rows * H * b
+    combine = rows * H * b + 8 * rows + (T * H * b if Fs else 0) + T * H * b
+    return dict(route_bytes=route, dispatch_bytes=dispatch, ffn_flops=ffn_flops,
+                ffn_weight_bytes=ffn_bytes, combine_bytes=combine)
+
+
+def read_traffic():
+    """HBM bytes per launch of the dominant kernel from the committed PMC summary,
+    or None if missing or if the kernel source changed since it was taken."""
+    try:
+        text = open(PMC_SUMMARY).read()
+    except OSError:
+        return None
+    m_src = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not (m_src and m_b):
+        return None
+    cur = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    if cur != m_src.group(1):
+        return None
+    return float(m_b.group(1))
+
+
+def cpu_baseline(cfg, L, n_tokens):
+    """The oracle as it stands on the first n_tokens tokens of the same layer."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+
+    Ls = dict(L)
+    Ls["x"] = L["x"][:n_tokens]
+    t0 = time.perf_counter()
+    r = oracle.layer(Ls, cfg.k)
+    oracle.load_stats(r["counts"], n_tokens, cfg.k, cfg.cf)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    return {"value": n_tokens / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n_tokens} of {cfg.T} tokens of the same layer through the whole "
+                      f"float64 oracle (route, dispatch, FFN, combine, stats); {dt:.1f} s",
+            "seconds": dt}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="mixtral_8x7b")
+    ap.add_argument("--cpu-tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs the MoE layer on one GPU only (no expert parallelism "
+              "or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_05_amd as moe
+    from synth import get_config, make_layer
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    moe.lib()  # fail loudly if the HIP library is missing
+    cfg = get_config(args.workload)
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    L = make_layer(cfg)
+
+    def dev(a):
+        if a is None:
+            return None
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+        return torch.from_numpy(a).cuda()
+
+    x, wg, bias = dev(L["x"]), dev(L["wg"]), dev(L["bias"])
+    w1, w2, ws1, ws2 = dev(L["w1"]), dev(L["w2"]), dev(L["ws1"]), dev(L["ws2"])
+    T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+    rows = T * k
+    dt_code = 1 if cfg.dtype == "bf16" else 0
+    dtype = x.dtype
+    # every buffer allocated once, outside the timed region
+    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    dsp = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
+               offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
+               perm=torch.empty(rows, dtype=torch.int32, device="cuda"),
+               inv=torch.empty(rows, dtype=torch.int32, device="cuda"),
+               xs=torch.empty((rows, H), dtype=dtype, device="cuda"))
+    ws_d = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, E, k)), dtype=torch.uint8,
+                       device="cuda")
+    ws_f = torch.empty(max(1, moe.moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dt_code)),
+                       dtype=torch.uint8, device="cuda")
+    ys = torch.empty((rows, H), dtype=dtype, device="cuda")
+    ysh = torch.empty((T, H), dtype=dtype, device="cuda") if Fs else None
+    out = torch.empty((T, H), dtype=dtype, device="cuda")
+    from sparse_mixture_experts_05_amd.binding import STATS_BYTES
+    st = torch.empty(STATS_BYTES, dtype=torch.uint8, device="cuda")
+    ovf = torch.empty(E, dtype=torch.int32, device="cuda")
+    strag = torch.empty(E, dtype=torch.int32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        moe.moe_route(x, wg, bias, k, topk_idx=idx, topk_w=wts, stream=stream)
+        if ev is not None:
+            ev[1].record(stream)
+        moe.moe_dispatch(idx, x, E, out=dsp, ws=ws_d, stream=stream)
+        if ev is not None:
+            ev[2].record(stream)
+        moe.moe_expert_ffn(dsp["xs"], dsp["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2, T=T, ys=ys,
+                           ysh=ysh, ws=ws_f, stream=stream)
+        if ev is not None:
+            ev[3].record(stream)
+        moe.moe_combine(ys, dsp["inv"], wts, ysh, out=out, stream=stream)
+        if ev is not None:
+            ev[4].record(stream)
+        moe.moe_load_stats(dsp["counts"], T, k, cfg.cf, stats=st, overflow=ovf,
+                           straggler_ids=strag, stream=stream, read_back=False)
+        if ev is not None:
+            ev[5].record(stream)
+
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+
+    names = ["route", "dispatch", "expert_ffn", "combine", "load_stats"]
+    per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
+                             for s in range(args.steps)])) for i, n in enumerate(names)}
+    counts = dsp["counts"].cpu().numpy()
+    work = algorithmic_work(cfg, counts)
+    ms_step = elapsed * 1e3 / args.steps
+    value = T * args.steps / elapsed
+
+    ffn_ms = per["expert_ffn"]
+    bf16 = cfg.dtype == "bf16"
+    peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+    # two launches of the same GEMM kernel per step, equal algorithmic flops each
+    per_launch_flops = work["ffn_flops"] / 2
+    per_launch_ms = ffn_ms / 2
+    achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
+    traffic = read_traffic()
+    kernels = {
+        "route": {"ms": per["route"], "GB/s": work["route_bytes"] / per["route"] / 1e6},
+        "dispatch": {"ms": per["dispatch"], "GB/s": work["dispatch_bytes"] / per["dispatch"] / 1e6},
+        "expert_ffn": {"ms": ffn_ms, "TFLOP/s": achieved * 1.0,
+                       "mfma_frac": achieved / peak,
+                       "weight_stream_GB/s": work["ffn_weight_bytes"] / ffn_ms / 1e6},
+        "combine": {"ms": per["combine"], "GB/s": work["combine_bytes"] / per["combine"] / 1e6},
+        "load_stats": {"ms": per["load_stats"]},
+    }
+    for n in ["route", "dispatch", "combine"]:
+        kernels[n]["hbm_frac"] = kernels[n]["GB/s"] / HBM_PEAK_GBS
+    result = {
+        "metric": "MoE layer tokens/sec at 1 GPU + MFMA util % (FFN) + HBM GB/s (route/dispatch)",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if bf16 else "f32",
+        "data": "synthetic (seeded Gaussian inputs and random-init weights)",
+        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k,
+                   "d_ff": F, "shared_d_ff": Fs, "routing_bias_amplitude": cfg.bias_amp,
+                   "capacity_factor": cfg.cf, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "kernel": DOMINANT_KERNEL, "achieved": achieved,
+                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": traffic},
+        "kernels": kernels,
+        "mfma_util_pct_ffn": 100.0 * achieved / peak,
+    }
+    if not args.no_cpu_baseline:
+        # a first small sample sizes a second one to about CPU_TARGET_S seconds
+        n = min(args.cpu_tokens, T)
+        print(f"[bench] cpu baseline on {n} tokens", file=sys.stderr, flush=True)
+        cb = cpu_baseline(cfg, L, n)
+        if cb["seconds"] < CPU_TARGET_S / 2 and n < T:
+            n2 = min(T, int(n * CPU_TARGET_S / max(cb["seconds"], 1e-3)))
+            print(f"[bench] cpu baseline on {n2} tokens", file=sys.stderr, flush=True)
+            cb = cpu_baseline(cfg, L, n2)
+        cb.pop("seconds")
+        result["cpu_baseline"] = cb
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
