@@ -120,6 +120,93 @@ __device__ bool find_tile(const GemmArgs& a, Tile& t) {
   return t.e >= 0;
 }
 
+// Blocked, XCD-aware tile order (large tiles). Groups are the E experts and
+// then the shared expert. Inside a group the tiles are visited in n-blocks of
+// GN column tiles; inside an n-block, row tile by row tile (so consecutive
+// tiles share the A rows and cycle through GN weight panels). Workgroups are
+// handed to the 8 XCDs round robin (workgroup g runs on XCD g % 8); XCD x
+// takes the contiguous run [x*C, (x+1)*C) of this order (C = ceil(total/8)),
+// so the ~32 tiles an XCD runs at once form a compact block whose operand
+// panels are shared in that XCD's L2.
+constexpr int kXcds = 8;
+constexpr int kBigWaves = 8;
+
+template <int BM, int BN, int GN>
+__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t) {
+  __shared__ int pre[257];
+  __shared__ int sel[4];
+  // Only the first 256 threads take part (the workgroup may be larger);
+  // every thread still meets every barrier.
+  const int tid = threadIdx.x;
+  const bool act = tid < 256;
+  const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
+  const int ntr = (a.routed.N + BN - 1) / BN;
+  const int nts = (a.shared.N + BN - 1) / BN;
+  // per-group tile counts (thread e: expert e; thread E: the shared group)
+  int off = 0, cnt = 0, tiles = 0;
+  if (!act) {
+  } else if (tid < a.E) {
+    off = min(max(a.offsets[tid], 0), a.rows);
+    cnt = min(max(a.offsets[tid + 1], off), a.rows) - off;
+    tiles = ((cnt + BM - 1) / BM) * ntr;
+  } else if (tid == a.E && a.shared_M > 0) {
+    cnt = a.shared_M;
+    tiles = ((cnt + BM - 1) / BM) * nts;
+  }
+  // inclusive scan over up to 257 groups (256 threads: group 256 = shared
+  // group when E == 256 is folded in by thread 255 below)
+  int extra = 0;
+  if (tid == 255 && a.E == 256 && a.shared_M > 0) extra = ((a.shared_M + BM - 1) / BM) * nts;
+  if (act) pre[tid] = tiles;
+  if (tid == 0) sel[0] = -1;
+  __syncthreads();
+  for (int d = 1; d < 256; d <<= 1) {
+    const int v = (act && tid >= d) ? pre[tid - d] : 0;
+    __syncthreads();
+    if (act) pre[tid] += v;
+    __syncthreads();
+  }
+  if (tid == 255) pre[256] = pre[255] + extra;
+  __syncthreads();
+  const int total = pre[ng <= 256 ? ng - 1 : 256];
+  const int C = (total + kXcds - 1) / kXcds;
+  const int g = blockIdx.x;
+  const int slot = g / kXcds;
+  if (slot >= C) return false;
+  const int q = (g % kXcds) * C + slot;
+  if (q >= total) return false;
+  // find the group of q (thread i checks group i; thread 255 also group 256)
+  auto check = [&](int grp, int incl, int excl, int c, int o) {
+    if (q >= excl && q < incl) {
+      const int nt_g = grp < a.E ? ntr : nts;
+      const int mt_g = (c + BM - 1) / BM;
+      const int local = q - excl;
+      const int blk = local / (mt_g * GN);
+      const int w = min(GN, nt_g - blk * GN);
+      const int li = local - blk * mt_g * GN;
+      const int mt = li / w, nt = blk * GN + li % w;
+      sel[0] = grp;
+      sel[1] = o + mt * BM;
+      sel[2] = min(BM, c - mt * BM);
+      sel[3] = nt * BN;
+    }
+  };
+  if (act && tid < ng) {
+    const int incl = pre[tid];
+    check(tid, incl, incl - tiles, cnt, off);
+  }
+  if (tid == 255 && ng == 257) check(256, pre[256], pre[255], a.shared_M, 0);
+  __syncthreads();
+  const int grp = sel[0];
+  if (grp < 0) return false;
+  t.group = grp < a.E ? 0 : 1;
+  t.e = grp < a.E ? grp : 0;
+  t.row0 = sel[1];
+  t.M = sel[2];
+  t.n0 = sel[3];
+  return true;
+}
+
 // ----------------------------------------------------------------- bf16 MFMA
 
 template <int BM, int BN, int WM, int WN>
@@ -250,6 +337,191 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
     }
 }
 
+// ----------------------------------------------------------------- bf16 MFMA, large tiles
+//
+// BM x BN tile (128 or 256 each), 4 waves in 2 x 2, each wave a (BM/2) x (BN/2)
+// block of 32x32x16 MFMAs. Operand tiles go straight from global memory into
+// LDS (global_load_lds_dwordx4: lane i of an instruction fills the 16-byte
+// slot i after the wave-uniform LDS base), two stages: the loads of k-step
+// kt+1 are in flight while k-step kt runs. A row of a staged tile is 64 bf16
+// = 8 chunks of 16 bytes; chunk c of row r sits in slot c ^ (r & 7), so the
+// lane that fills slot p of row r loads chunk p ^ (r & 7), and fragment
+// reads (32 consecutive rows, one chunk column) hit distinct banks.
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS hand-off only. __syncthreads() carries a release
+// fence that waits for every outstanding global load (vmcnt 0), which would
+// drain the next stage's prefetch; the staged loads are waited for explicitly.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// global_load_lds_dwordx4: lane i copies 16 bytes from its address g into
+// LDS at M0 + 16*i (M0 = the wave-uniform LDS address). Issued through asm so
+// the compiler's wait insertion does not treat every later LDS read as
+// aliasing the in-flight copy (which would drain the prefetch); completion is
+// tracked with explicit vmcnt waits (loads complete in issue order).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_uniform) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds_uniform))));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(m0)
+      : "memory");
+}
+
+// Large-tile kernel: BM x BN tile, NW waves in a 2 x (NW/2) grid, each wave a
+// (BM/2) x (BN/(NW/2)) block of 32x32x16 MFMAs. Two LDS stages of BK = 64.
+// Fragment registers are double buffered across the four 16-deep k slices of
+// a stage, and the one barrier per stage sits where every wave already holds
+// the old stage's last fragments in registers: after it the old stage is
+// refilled (k-step kt+2) and the first fragments of the new stage are read.
+template <int BM, int BN, int NW>
+__global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args) {
+  constexpr int BK = 64;
+  constexpr int ROWB = BK * 2;                  // 128 bytes = 8 chunks of 16
+  constexpr int WN_ = NW / 2;
+  constexpr int WTM = BM / 2, WTN = BN / WN_;
+  constexpr int SM = WTM / 32, SN = WTN / 32;
+  constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int ROWS_PER_INST = 64 * 16 / ROWB;   // 8 rows per load instruction
+  constexpr int A_INST = BM / ROWS_PER_INST / NW;  // per wave per stage
+  constexpr int B_INST = BN / ROWS_PER_INST / NW;
+  constexpr int NLD = A_INST + B_INST;
+  static_assert(A_INST >= 1 && B_INST >= 1 && SM >= 1 && SN >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+
+  Tile t;
+  if (!find_tile_blocked<BM, BN, 8>(args, t)) return;
+  const Group G = pick_group(args, t.group);
+  const int N = G.N, K = G.K;
+  const uint16_t* A = static_cast<const uint16_t*>(G.A) + (size_t)t.row0 * K;
+  const uint16_t* B = static_cast<const uint16_t*>(G.B) + (size_t)t.e * N * K + (size_t)t.n0 * K;
+  uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
+  const int M = t.M;
+  const int nvalid = N - t.n0;
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN_, wn = wave % WN_;
+
+  // Slot p of row r holds chunk p ^ ((r >> 1) & 7). A 128-bit LDS read is
+  // served 16 lanes at a time; the 16 consecutive rows of one such group then
+  // cover all 64 banks exactly once (row parity picks the half, the swizzle
+  // the 16-byte column). Lane i of a load instruction fills slot i & 7 of row
+  // r0 + (i >> 3), so it loads chunk (i & 7) ^ ((r >> 1) & 7).
+  const int lrow = lane >> 3;
+  const uint16_t* ga[A_INST];
+  const uint16_t* gb[B_INST];
+#pragma unroll
+  for (int j = 0; j < A_INST; ++j) {
+    const int r = (wave * A_INST + j) * ROWS_PER_INST + lrow;
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    ga[j] = A + (size_t)min(r, M - 1) * K + c * 8;
+  }
+#pragma unroll
+  for (int j = 0; j < B_INST; ++j) {
+    const int r = (wave * B_INST + j) * ROWS_PER_INST + lrow;
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    gb[j] = B + (size_t)min(r, nvalid - 1) * K + c * 8;
+  }
+  auto issue = [&](int kt) {
+    uint8_t* base = smem + (kt & 1) * STAGE;
+    const int k0 = kt * BK;
+#pragma unroll
+    for (int j = 0; j < A_INST; ++j)
+      lds_dma16(ga[j] + k0, base + (wave * A_INST + j) * ROWS_PER_INST * ROWB);
+#pragma unroll
+    for (int j = 0; j < B_INST; ++j)
+      lds_dma16(gb[j] + k0, base + BM * ROWB + (wave * B_INST + j) * ROWS_PER_INST * ROWB);
+  };
+
+  f32x16_t acc[SM][SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  int fa[SM], fb[SN];
+#pragma unroll
+  for (int i = 0; i < SM; ++i) fa[i] = (wm * WTM + i * 32 + (lane & 31)) * ROWB;
+#pragma unroll
+  for (int j = 0; j < SN; ++j) fb[j] = (BM + wn * WTN + j * 32 + (lane & 31)) * ROWB;
+  const int sw = (lane >> 1) & 7;  // == (row >> 1) & 7 for every fragment row of this lane
+  const int khalf = lane >> 5;
+
+  u32x4_t ca[SM], cb[SN], na[SM], nb[SN];
+  auto load_frags = [&](const uint8_t* st, int ks, u32x4_t (&fa_)[SM], u32x4_t (&fb_)[SN]) {
+    const int off = ((ks * 2 + khalf) ^ sw) << 4;
+#pragma unroll
+    for (int i = 0; i < SM; ++i) fa_[i] = ld16(st + fa[i] + off);
+#pragma unroll
+    for (int j = 0; j < SN; ++j) fb_[j] = ld16(st + fb[j] + off);
+  };
+  auto mma = [&](const u32x4_t (&fa_)[SM], const u32x4_t (&fb_)[SN]) {
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa_[i]), as_bf16x8(fb_[j]),
+                                                            acc[i][j], 0, 0, 0);
+  };
+
+  const int KT = K / BK;
+  issue(0);
+  if (KT > 1) {
+    issue(1);
+    wait_vmcnt<NLD>();
+  } else {
+    wait_vmcnt<0>();
+  }
+  lds_barrier();
+  load_frags(smem, 0, ca, cb);
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint8_t* st = smem + (kt & 1) * STAGE;
+    load_frags(st, 1, na, nb);
+    mma(ca, cb);
+    load_frags(st, 2, ca, cb);
+    mma(na, nb);
+    load_frags(st, 3, na, nb);
+    mma(ca, cb);
+    if (kt + 1 < KT) {
+      // stage kt+1 landed (own loads, then everyone's); stage kt fully in registers
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (kt + 2 < KT) issue(kt + 2);
+      load_frags(smem + ((kt + 1) & 1) * STAGE, 0, ca, cb);
+    }
+    mma(na, nb);
+  }
+
+  const bool gelu = args.gelu != 0;
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j) {
+      const int col = wn * WTN + j * 32 + (lane & 31);
+      if (col >= nvalid) continue;
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+        if (row < M) {
+          float y = acc[i][j][v];
+          if (gelu) y = gelu_erf(y);
+          C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
+        }
+      }
+    }
+}
+
 // ----------------------------------------------------------------- fp32 VALU
 
 __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs args) {
@@ -341,7 +613,12 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     return hipGetLastError();
   }
   if (small_segments) return run_bf16<32, 128, 1, 4>(a, rows, E, s);
-  return run_bf16<128, 128, 2, 2>(a, rows, E, s);
+  dim3 grid;
+  GemmArgs b = a;
+  grid_of<256, 256>(b, rows, E, grid);
+  grid.x = (grid.x + kXcds - 1) / kXcds * kXcds;  // every XCD gets the same slot count
+  hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves>), grid, dim3(kBigWaves * 64), 0, s, b);
+  return hipGetLastError();
 }
 
 }  // namespace
