@@ -36,6 +36,28 @@ __device__ __forceinline__ float gelu_erf(float a) {
   return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));
 }
 
+// erf by Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26 (Hastings' rational approximation): for x >= 0,
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x),  |error| <= 1.5e-7,
+// and erf(-x) = -erf(x). Branch free; used where the result is rounded to
+// bf16 (relative step 2^-8), far above the approximation error.
+__device__ __forceinline__ float erf_as7126(float x) {
+  const float ax = fabsf(x);
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, ax, 1.0f));
+  float p = fmaf(1.061405429f, t, -1.453152027f);
+  p = fmaf(p, t, 1.421413741f);
+  p = fmaf(p, t, -0.284496736f);
+  p = fmaf(p, t, 0.254829592f);
+  const float y = 1.0f - p * t * __expf(-ax * ax);
+  return copysignf(y, x);
+}
+
+// GeLU (erf form) for bf16 outputs.
+__device__ __forceinline__ float gelu_erf_fast(float a) {
+  return 0.5f * a * (1.0f + erf_as7126(a * 0.70710678118654752f));
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }

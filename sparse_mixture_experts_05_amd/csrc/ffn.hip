@@ -503,21 +503,31 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
     mma(na, nb);
   }
 
+  // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
+  // (v/4)*8 + (lane/32)*4 + v%4. Lanes 2m and 2m+1 (adjacent columns) swap
+  // one value per row pair with DPP, so each stores a bf16 pair (4 bytes):
+  // the even lane row r = R(v), the odd lane row r + 1. All lanes take part
+  // in the swap; only the stores are masked.
   const bool gelu = args.gelu != 0;
+  const bool odd = lane & 1;
 #pragma unroll
   for (int i = 0; i < SM; ++i)
 #pragma unroll
     for (int j = 0; j < SN; ++j) {
-      const int col = wn * WTN + j * 32 + (lane & 31);
-      if (col >= nvalid) continue;
+      const int col = wn * WTN + j * 32 + (lane & 31);  // this lane's column
+      const int pcol = col & ~1;                        // first column of the stored pair
+      const bool cok = pcol < nvalid;                   // N % 64 == 0: pairs are all or nothing
+      float y[16];
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-        if (row < M) {
-          float y = acc[i][j][v];
-          if (gelu) y = gelu_erf(y);
-          C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
-        }
+      for (int v = 0; v < 16; ++v) y[v] = gelu ? gelu_erf_fast(acc[i][j][v]) : acc[i][j][v];
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        const float send = odd ? y[v] : y[v + 1];
+        const float recv = __int_as_float(
+            __builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, false));
+        const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3) + (odd ? 1 : 0);
+        const uint32_t packed = odd ? pack_bf16x2(recv, y[v + 1]) : pack_bf16x2(y[v], recv);
+        if (cok && row < M) *reinterpret_cast<uint32_t*>(C + (size_t)row * N + pcol) = packed;
       }
     }
 }
