@@ -22,6 +22,8 @@
 // swizzled by row so fragment reads are bank-conflict free. Rows past the
 // segment end are clamped on load and masked on store.
 // fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
+#include <type_traits>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -121,19 +123,28 @@ __device__ bool find_tile(const GemmArgs& a, Tile& t) {
 }
 
 // Blocked, XCD-aware tile order (large tiles). Groups are the E experts and
-// then the shared expert. Inside a group the tiles are visited in n-blocks of
-// GN column tiles; inside an n-block, row tile by row tile (so consecutive
-// tiles share the A rows and cycle through GN weight panels). Workgroups are
-// handed to the 8 XCDs round robin (workgroup g runs on XCD g % 8); XCD x
-// takes the contiguous run [x*C, (x+1)*C) of this order (C = ceil(total/8)),
+// then the shared expert. A group with c rows has floor(c/BM) full row tiles
+// and, if BM does not divide c, one partial row tile.
+//
+// Full tiles come first. Inside a group they are visited in n-blocks of GN
+// column tiles, row tile by row tile inside an n-block (consecutive tiles
+// share A rows and cycle through GN weight panels). Workgroups are handed to
+// the 8 XCDs round robin (workgroup g runs on XCD g % 8); XCD x takes the
+// contiguous run [x*CF, (x+1)*CF) of the full-tile order (CF = ceil(F/8)),
 // so the ~32 tiles an XCD runs at once form a compact block whose operand
-// panels are shared in that XCD's L2.
+// panels its L2 shares.
+//
+// Partial tiles come last on every XCD (partial tile p on XCD p % 8), in
+// groups ordered by descending partial-tile rows (ties: lower group first).
+// They skip the 32-row sub-tiles past the segment end, so they are the short
+// tiles; running them last, longest first, packs the final round.
 constexpr int kXcds = 8;
 constexpr int kBigWaves = 8;
 
 template <int BM, int BN, int GN>
 __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t) {
-  __shared__ int pre[257];
+  __shared__ int pf[257], pp[257];
+  __shared__ int prow[257], sgrp[257];
   __shared__ int sel[4];
   // Only the first 256 threads take part (the workgroup may be larger);
   // every thread still meets every barrier.
@@ -142,60 +153,126 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t) {
   const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
   const int ntr = (a.routed.N + BN - 1) / BN;
   const int nts = (a.shared.N + BN - 1) / BN;
-  // per-group tile counts (thread e: expert e; thread E: the shared group)
-  int off = 0, cnt = 0, tiles = 0;
-  if (!act) {
-  } else if (tid < a.E) {
-    off = min(max(a.offsets[tid], 0), a.rows);
-    cnt = min(max(a.offsets[tid + 1], off), a.rows) - off;
-    tiles = ((cnt + BM - 1) / BM) * ntr;
-  } else if (tid == a.E && a.shared_M > 0) {
-    cnt = a.shared_M;
-    tiles = ((cnt + BM - 1) / BM) * nts;
+  // thread e: expert e; thread E: the shared group; thread 255 also carries
+  // the shared group as group 256 when E == 256
+  auto rows_of = [&](int grp, int& off, int& cnt) {
+    if (grp < a.E) {
+      off = min(max(a.offsets[grp], 0), a.rows);
+      cnt = min(max(a.offsets[grp + 1], off), a.rows) - off;
+    } else {
+      off = 0;
+      cnt = a.shared_M;
+    }
+  };
+  int off = 0, cnt = 0, full = 0, part = 0;
+  if (act && tid < ng) {
+    rows_of(tid, off, cnt);
+    const int nt = tid < a.E ? ntr : nts;
+    full = (cnt / BM) * nt;
+    part = (cnt % BM) ? nt : 0;
   }
-  // inclusive scan over up to 257 groups (256 threads: group 256 = shared
-  // group when E == 256 is folded in by thread 255 below)
-  int extra = 0;
-  if (tid == 255 && a.E == 256 && a.shared_M > 0) extra = ((a.shared_M + BM - 1) / BM) * nts;
-  if (act) pre[tid] = tiles;
+  int xfull = 0, xpart = 0;
+  if (tid == 255 && ng == 257) {
+    xfull = (a.shared_M / BM) * nts;
+    xpart = (a.shared_M % BM) ? nts : 0;
+  }
+  if (act) prow[tid] = tid < ng ? cnt % BM : 0;
+  if (tid == 255) prow[256] = ng == 257 ? a.shared_M % BM : 0;
+  __syncthreads();
+  // rank of each group with a partial tile: descending rows, ties by id
+  auto rank_of = [&](int grp) {
+    const int r = prow[grp];
+    int k = 0;
+    for (int o = 0; o < ng; ++o) {
+      const int ro = prow[o];
+      k += (ro > r) || (ro == r && o < grp);
+    }
+    return k;
+  };
+  int myrank = -1, xrank = -1;
+  if (act && tid < ng) myrank = rank_of(tid);
+  if (tid == 255 && ng == 257) xrank = rank_of(256);
+  __syncthreads();
+  // pp is indexed by rank: partial tile counts in longest-first order
+  if (act) pp[tid] = 0;
+  if (tid == 255) pp[256] = 0;
+  __syncthreads();
+  if (myrank >= 0) {
+    pp[myrank] = part;
+    sgrp[myrank] = tid;
+  }
+  if (xrank >= 0) {
+    pp[xrank] = xpart;
+    sgrp[xrank] = 256;
+  }
+  if (act) pf[tid] = full;
   if (tid == 0) sel[0] = -1;
   __syncthreads();
+  if (tid == 255) xpart = pp[256];  // the scan below folds entry 256 in separately
+  __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {
-    const int v = (act && tid >= d) ? pre[tid - d] : 0;
+    const int vf = (act && tid >= d) ? pf[tid - d] : 0;
+    const int vp = (act && tid >= d) ? pp[tid - d] : 0;
     __syncthreads();
-    if (act) pre[tid] += v;
+    if (act) {
+      pf[tid] += vf;
+      pp[tid] += vp;
+    }
     __syncthreads();
   }
-  if (tid == 255) pre[256] = pre[255] + extra;
+  if (tid == 255) {
+    pf[256] = pf[255] + xfull;
+    pp[256] = pp[255] + xpart;
+  }
   __syncthreads();
-  const int total = pre[ng <= 256 ? ng - 1 : 256];
-  const int C = (total + kXcds - 1) / kXcds;
+  const int last = ng <= 256 ? ng - 1 : 256;
+  const int F = pf[last], P = pp[last];
+  const int CF = (F + kXcds - 1) / kXcds;
+  const int CP = (P + kXcds - 1) / kXcds;
   const int g = blockIdx.x;
-  const int slot = g / kXcds;
-  if (slot >= C) return false;
-  const int q = (g % kXcds) * C + slot;
-  if (q >= total) return false;
-  // find the group of q (thread i checks group i; thread 255 also group 256)
-  auto check = [&](int grp, int incl, int excl, int c, int o) {
-    if (q >= excl && q < incl) {
-      const int nt_g = grp < a.E ? ntr : nts;
-      const int mt_g = (c + BM - 1) / BM;
-      const int local = q - excl;
+  const int x = g % kXcds, slot = g / kXcds;
+  if (slot >= CF + CP) return false;
+  const bool is_full = slot < CF;
+  const int q = is_full ? x * CF + slot : (slot - CF) * kXcds + x;
+  if (q >= (is_full ? F : P)) return false;
+  auto check_full = [&](int grp, int f_incl, int f_excl) {
+    int o, c;
+    rows_of(grp, o, c);
+    const int nt_g = grp < a.E ? ntr : nts;
+    if (is_full && q >= f_excl && q < f_incl) {
+      const int mt_g = c / BM;  // full row tiles
+      const int local = q - f_excl;
       const int blk = local / (mt_g * GN);
       const int w = min(GN, nt_g - blk * GN);
       const int li = local - blk * mt_g * GN;
       const int mt = li / w, nt = blk * GN + li % w;
       sel[0] = grp;
       sel[1] = o + mt * BM;
-      sel[2] = min(BM, c - mt * BM);
+      sel[2] = BM;
       sel[3] = nt * BN;
     }
   };
+  auto check_part = [&](int grp, int p_incl, int p_excl) {
+    if (!is_full && q >= p_excl && q < p_incl) {
+      int o, c;
+      rows_of(grp, o, c);
+      const int mt = c / BM;  // the partial row tile
+      sel[0] = grp;
+      sel[1] = o + mt * BM;
+      sel[2] = c - mt * BM;
+      sel[3] = (q - p_excl) * BN;
+    }
+  };
+  // full tiles by group id; partial tiles by rank (sgrp maps rank -> group)
   if (act && tid < ng) {
-    const int incl = pre[tid];
-    check(tid, incl, incl - tiles, cnt, off);
+    check_full(tid, pf[tid], pf[tid] - full);
+    const int pcount = pp[tid] - (tid ? pp[tid - 1] : 0);
+    check_part(sgrp[tid], pp[tid], pp[tid] - pcount);
   }
-  if (tid == 255 && ng == 257) check(256, pre[256], pre[255], a.shared_M, 0);
+  if (tid == 255 && ng == 257) {
+    check_full(256, pf[256], pf[255]);
+    check_part(sgrp[256], pp[256], pp[255]);
+  }
   __syncthreads();
   const int grp = sel[0];
   if (grp < 0) return false;
@@ -458,50 +535,62 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
   const int sw = (lane >> 1) & 7;  // == (row >> 1) & 7 for every fragment row of this lane
   const int khalf = lane >> 5;
 
-  u32x4_t ca[SM], cb[SN], na[SM], nb[SN];
-  auto load_frags = [&](const uint8_t* st, int ks, u32x4_t (&fa_)[SM], u32x4_t (&fb_)[SN]) {
-    const int off = ((ks * 2 + khalf) ^ sw) << 4;
-#pragma unroll
-    for (int i = 0; i < SM; ++i) fa_[i] = ld16(st + fa[i] + off);
-#pragma unroll
-    for (int j = 0; j < SN; ++j) fb_[j] = ld16(st + fb[j] + off);
-  };
-  auto mma = [&](const u32x4_t (&fa_)[SM], const u32x4_t (&fb_)[SN]) {
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-      for (int j = 0; j < SN; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa_[i]), as_bf16x8(fb_[j]),
-                                                            acc[i][j], 0, 0, 0);
-  };
+  // Row sub-tiles of this wave that hold data (all of them except in a
+  // segment's last, partial row tile); empty ones skip reads and MFMAs.
+  const int nsub = min(SM, max(0, (M - wm * WTM + 31) / 32));
 
-  const int KT = K / BK;
-  issue(0);
-  if (KT > 1) {
-    issue(1);
-    wait_vmcnt<NLD>();
-  } else {
-    wait_vmcnt<0>();
-  }
-  lds_barrier();
-  load_frags(smem, 0, ca, cb);
-  for (int kt = 0; kt < KT; ++kt) {
-    const uint8_t* st = smem + (kt & 1) * STAGE;
-    load_frags(st, 1, na, nb);
-    mma(ca, cb);
-    load_frags(st, 2, ca, cb);
-    mma(na, nb);
-    load_frags(st, 3, na, nb);
-    mma(ca, cb);
-    if (kt + 1 < KT) {
-      // stage kt+1 landed (own loads, then everyone's); stage kt fully in registers
+  u32x4_t ca[SM], cb[SN], na[SM], nb[SN];
+  auto main_loop = [&](auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    auto load_frags = [&](const uint8_t* st, int ks, u32x4_t (&fa_)[SM], u32x4_t (&fb_)[SN]) {
+      const int off = ((ks * 2 + khalf) ^ sw) << 4;
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+        if (!PARTIAL || i < nsub) fa_[i] = ld16(st + fa[i] + off);
+#pragma unroll
+      for (int j = 0; j < SN; ++j) fb_[j] = ld16(st + fb[j] + off);
+    };
+    auto mma = [&](const u32x4_t (&fa_)[SM], const u32x4_t (&fb_)[SN]) {
+#pragma unroll
+      for (int i = 0; i < SM; ++i)
+        if (!PARTIAL || i < nsub)
+#pragma unroll
+          for (int j = 0; j < SN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa_[i]), as_bf16x8(fb_[j]),
+                                                                acc[i][j], 0, 0, 0);
+    };
+    const int KT = K / BK;
+    issue(0);
+    if (KT > 1) {
+      issue(1);
+      wait_vmcnt<NLD>();
+    } else {
       wait_vmcnt<0>();
-      lds_barrier();
-      if (kt + 2 < KT) issue(kt + 2);
-      load_frags(smem + ((kt + 1) & 1) * STAGE, 0, ca, cb);
     }
-    mma(na, nb);
-  }
+    lds_barrier();
+    load_frags(smem, 0, ca, cb);
+    for (int kt = 0; kt < KT; ++kt) {
+      const uint8_t* st = smem + (kt & 1) * STAGE;
+      load_frags(st, 1, na, nb);
+      mma(ca, cb);
+      load_frags(st, 2, ca, cb);
+      mma(na, nb);
+      load_frags(st, 3, na, nb);
+      mma(ca, cb);
+      if (kt + 1 < KT) {
+        // stage kt+1 landed (own loads, then everyone's); stage kt fully in registers
+        wait_vmcnt<0>();
+        lds_barrier();
+        if (kt + 2 < KT) issue(kt + 2);
+        load_frags(smem + ((kt + 1) & 1) * STAGE, 0, ca, cb);
+      }
+      mma(na, nb);
+    }
+  };
+  if (M == BM)
+    main_loop(std::integral_constant<bool, false>{});
+  else
+    main_loop(std::integral_constant<bool, true>{});
 
   // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
   // (v/4)*8 + (lane/32)*4 + v%4. Lanes 2m and 2m+1 (adjacent columns) swap
@@ -626,7 +715,8 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
   dim3 grid;
   GemmArgs b = a;
   grid_of<256, 256>(b, rows, E, grid);
-  grid.x = (grid.x + kXcds - 1) / kXcds * kXcds;  // every XCD gets the same slot count
+  // full and partial runs are each rounded up per XCD: at most 2*8 extra slots
+  grid.x = (grid.x + 2 * kXcds + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves>), grid, dim3(kBigWaves * 64), 0, s, b);
   return hipGetLastError();
 }
