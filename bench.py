@@ -148,6 +148,8 @@ def main():
                perm=torch.empty(rows, dtype=torch.int32, device="cuda"),
                inv=torch.empty(rows, dtype=torch.int32, device="cuda"),
                xs=torch.empty((rows, H), dtype=dtype, device="cuda"))
+    ws_r = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, k, dt_code)),
+                       dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, E, k)), dtype=torch.uint8,
                        device="cuda")
     ws_f = torch.empty(max(1, moe.moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dt_code)),
@@ -164,7 +166,7 @@ def main():
     def step(ev=None):
         if ev is not None:
             ev[0].record(stream)
-        moe.moe_route(x, wg, bias, k, topk_idx=idx, topk_w=wts, stream=stream)
+        moe.moe_route(x, wg, bias, k, topk_idx=idx, topk_w=wts, ws=ws_r, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         moe.moe_dispatch(idx, x, E, out=dsp, ws=ws_d, stream=stream)

@@ -90,9 +90,16 @@ typedef struct {
  * bias     [E]   fp32 or NULL   device, read (NULL = no routing bias)
  * topk_idx [T,k] int32          device, written
  * topk_w   [T,k] fp32           device, written
+ * ws / ws_bytes: device workspace of at least moe_route_workspace_bytes(T,H,E,k,dtype)
  */
 int moe_route(const void* x, const void* wg, const float* bias, int T, int H, int E, int k,
-              int dtype, int32_t* topk_idx, float* topk_w, void* stream);
+              int dtype, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+              void* stream);
+
+/* Workspace bytes moe_route needs for (T, H, E, k, dtype): 0 when the scores
+ * fit the one-launch path (then ws may be NULL); few tokens (T < 2048) use
+ * partial score tiles in the workspace. 0 also on unsupported sizes. */
+size_t moe_route_workspace_bytes(int T, int H, int E, int k, int dtype);
 
 /* Workspace bytes moe_dispatch needs for (T, E, k); 0 on unsupported sizes. */
 size_t moe_dispatch_workspace_bytes(int T, int E, int k);
@@ -131,7 +138,9 @@ size_t moe_expert_ffn_workspace_bytes(int rows, int T, int H, int E, int F, int 
  * w1 [E,F,H], w2 [E,H,F]; x [T,H], ws1 [Fs,H], ws2 [H,Fs] (NULL / Fs = 0: no shared expert)
  * ys [rows,H], ysh [T,H] (NULL when Fs = 0): device, written.
  * In bf16 mode h is rounded to bf16 before the second Linear (fp32 accumulation
- * in both); ys and ysh are rounded to bf16.
+ * in both); ys and ysh are rounded to bf16; erf is evaluated with Abramowitz &
+ * Stegun formula 7.1.26 (|error| <= 1.5e-7, far below the bf16 step of h). fp32
+ * mode uses the device library's erff.
  * ws / ws_bytes: device workspace of at least moe_expert_ffn_workspace_bytes(...)
  */
 int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H, int F,

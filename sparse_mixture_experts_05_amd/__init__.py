@@ -7,8 +7,10 @@ kernels; this package only marshals tensors, sizes and the current stream.
 """
 from .binding import (MoEError, lib, moe_combine, moe_dispatch, moe_expert_ffn,
                       moe_layer_forward, moe_load_stats, moe_route, moe_status_string,
-                      moe_dispatch_workspace_bytes, moe_expert_ffn_workspace_bytes)
+                      moe_dispatch_workspace_bytes, moe_expert_ffn_workspace_bytes,
+                      moe_route_workspace_bytes)
 
 __all__ = ["MoEError", "lib", "moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine",
            "moe_load_stats", "moe_layer_forward", "moe_status_string",
-           "moe_dispatch_workspace_bytes", "moe_expert_ffn_workspace_bytes"]
+           "moe_dispatch_workspace_bytes", "moe_expert_ffn_workspace_bytes",
+           "moe_route_workspace_bytes"]

@@ -21,7 +21,8 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 _vp, _i, _sz, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
 
 SIGNATURES = {
-    "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp]),
+    "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_dispatch_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
@@ -102,7 +103,11 @@ def _stream(stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
-def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, stream=None):
+def moe_route_workspace_bytes(T: int, H: int, E: int, k: int, dtype_code: int) -> int:
+    return lib().moe_route_workspace_bytes(T, H, E, k, dtype_code)
+
+
+def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, ws=None, stream=None):
     """Top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
     T, H = x.shape
     E = wg.shape[0]
@@ -111,10 +116,15 @@ def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, stream=None):
     if topk_w is None:
         topk_w = torch.empty((T, k), dtype=torch.float32, device=x.device)
     dt = _dtype_code(x)
+    nbytes = moe_route_workspace_bytes(T, H, E, k, dt)
+    if nbytes > 0:
+        ws = _workspace(nbytes, x.device, ws)
+    ws_ptr = _dev(ws, "ws") if ws is not None else None
+    ws_len = ws.numel() if ws is not None else 0
     _check("moe_route", lib().moe_route(
         _dev(x, "x"), _dev(wg, "wg", x.dtype), _dev(bias, "bias", torch.float32), T, H, E, k, dt,
         _dev(topk_idx, "topk_idx", torch.int32), _dev(topk_w, "topk_w", torch.float32),
-        _stream(stream)))
+        ws_ptr, ws_len, _stream(stream)))
     return topk_idx, topk_w
 
 

@@ -7,8 +7,10 @@
 
 namespace moe {
 
+size_t route_ws_bytes(int T, int H, int E, bool bf16);
 hipError_t launch_route(const void* x, const void* wg, const float* bias, int T, int H, int E,
-                        int k, bool bf16, int32_t* topk_idx, float* topk_w, hipStream_t s);
+                        int k, bool bf16, int32_t* topk_idx, float* topk_w, void* ws,
+                        hipStream_t s);
 
 int dispatch_blocks(int T);
 size_t dispatch_ws_bytes(int T, int E);

@@ -45,13 +45,21 @@ const char* moe_status_string(int status) {
   }
 }
 
+size_t moe_route_workspace_bytes(int T, int H, int E, int k, int dtype) {
+  if (!dtype_ok(dtype) || check_tokens(T, H, E, k) != MOE_OK) return 0;
+  return moe::route_ws_bytes(T, H, E, dtype == MOE_BF16);
+}
+
 int moe_route(const void* x, const void* wg, const float* bias, int T, int H, int E, int k,
-              int dtype, int32_t* topk_idx, float* topk_w, void* stream) {
+              int dtype, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
+              void* stream) {
   if (!x || !wg || !topk_idx || !topk_w || !dtype_ok(dtype)) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
+  const size_t need = moe::route_ws_bytes(T, H, E, dtype == MOE_BF16);
+  if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_route(x, wg, bias, T, H, E, k, dtype == MOE_BF16, topk_idx, topk_w,
-                                    as_stream(stream)));
+                                    ws, as_stream(stream)));
 }
 
 size_t moe_dispatch_workspace_bytes(int T, int E, int k) {

@@ -143,6 +143,47 @@ __device__ __forceinline__ void topk_phase(const float* sc, int BT, int t0, int 
   }
 }
 
+// K loop of the score tiles: a ring of D register buffers keeps the operand
+// loads of the next D-1 k-steps in flight while one step runs on the matrix
+// cores (the loop is unrolled by D so every ring index is static).
+template <int MC, int NCW, int D>
+__device__ __forceinline__ void mfma_ring(const uint16_t* const (&arow)[MC],
+                                          const uint16_t* const (&brow)[NCW], int s0, int nsteps,
+                                          int stride, f32x4_t (&acc)[MC][NCW]) {
+  u32x4_t ra[D][MC], rb[D][NCW];
+#pragma unroll
+  for (int u = 0; u < D; ++u) {
+    const int s = s0 + u * stride;
+    if (s < nsteps) {
+#pragma unroll
+      for (int r = 0; r < MC; ++r) ra[u][r] = ld16(arow[r] + s * 32);
+#pragma unroll
+      for (int c = 0; c < NCW; ++c) rb[u][c] = ld16(brow[c] + s * 32);
+    }
+  }
+  for (int base = s0; base < nsteps; base += D * stride) {
+#pragma unroll
+    for (int u = 0; u < D; ++u) {
+      const int s = base + u * stride;
+      if (s < nsteps) {
+#pragma unroll
+        for (int r = 0; r < MC; ++r)
+#pragma unroll
+          for (int c = 0; c < NCW; ++c)
+            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[u][r]),
+                                                                as_bf16x8(rb[u][c]), acc[r][c], 0, 0, 0);
+        const int sn = s + D * stride;
+        if (sn < nsteps) {
+#pragma unroll
+          for (int r = 0; r < MC; ++r) ra[u][r] = ld16(arow[r] + sn * 32);
+#pragma unroll
+          for (int c = 0; c < NCW; ++c) rb[u][c] = ld16(brow[c] + sn * 32);
+        }
+      }
+    }
+  }
+}
+
 // bf16 scores with MFMA. MC: 16-token row chunks per workgroup; NCW: 16-expert
 // column chunks per wave; KSPLIT: 1 = each wave owns NCW column chunks over
 // all of H, 4 = the 4 waves split the K steps (interleaved) and the partial
@@ -177,20 +218,7 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
   if (active) {
     const int nsteps = H / 32;
     const int s0 = KSPLIT == 4 ? wave : 0;
-    for (int s = s0; s < nsteps; s += KSPLIT) {
-      const int kk = s * 32;
-      u32x4_t a[MC], b[NCW];
-#pragma unroll
-      for (int r = 0; r < MC; ++r) a[r] = ld16(arow[r] + kk);
-#pragma unroll
-      for (int c = 0; c < NCW; ++c) b[c] = ld16(brow[c] + kk);
-#pragma unroll
-      for (int r = 0; r < MC; ++r)
-#pragma unroll
-        for (int c = 0; c < NCW; ++c)
-          acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[r]), as_bf16x8(b[c]),
-                                                              acc[r][c], 0, 0, 0);
-    }
+    mfma_ring<MC, NCW, (MC + NCW <= 4 ? 8 : 4)>(arow, brow, s0, nsteps, KSPLIT, acc);
   }
   // D layout of 16x16: lane holds column lane%16, rows (lane/16)*4 + v.
   if (KSPLIT == 1) {
@@ -257,6 +285,63 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
   topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w);
 }
 
+
+// Few tokens (decode-like): one workgroup per 16 tokens cannot stream Wg fast
+// enough, so the scores are computed in two launches. Phase 1: one wavefront
+// per (16 tokens, 16 experts, K slice) writes a partial score tile into the
+// workspace ws[ks][t][e]. Phase 2: one wavefront per token sums its K slices
+// in a fixed order (ks ascending), adds the bias and runs the top-k.
+__global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __restrict__ x,
+                                                           const uint16_t* __restrict__ wg,
+                                                           int T, int H, int E, int ksteps,
+                                                           float* __restrict__ ws) {
+  const int lane = threadIdx.x;
+  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16, ks = blockIdx.z;
+  const int r16 = lane & 15, kq = (lane >> 4) * 8;
+  const int s0 = ks * ksteps;
+  const uint16_t* const arow[1] = {x + (size_t)min(t0 + r16, T - 1) * H + kq + s0 * 32};
+  const uint16_t* const brow[1] = {wg + (size_t)min(e0 + r16, E - 1) * H + kq + s0 * 32};
+  f32x4_t acc[1][1] = {{f32x4_t{0.f, 0.f, 0.f, 0.f}}};
+  mfma_ring<1, 1, 8>(arow, brow, 0, ksteps, 1, acc);
+  const int e = e0 + r16;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    const int t = t0 + (lane >> 4) * 4 + v;
+    if (t < T && e < E) ws[((size_t)ks * T + t) * E + e] = acc[0][0][v];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __restrict__ ws,
+                                                                const float* __restrict__ bias,
+                                                                int T, int E, int k, int nks,
+                                                                int32_t* __restrict__ topk_idx,
+                                                                float* __restrict__ topk_w) {
+  constexpr int BT = kThreads / kWave;  // 4 tokens per workgroup
+  __shared__ float sc[BT * kLogitStride];
+  const int t0 = blockIdx.x * BT;
+  for (int p = threadIdx.x; p < BT * E; p += kThreads) {
+    const int t = p / E, e = p % E;
+    if (t0 + t < T) {
+      float s = 0.0f;
+      for (int q = 0; q < nks; ++q) s += ws[((size_t)q * T + t0 + t) * E + e];
+      sc[t * kLogitStride + e] = s;
+    }
+  }
+  __syncthreads();
+  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w);
+}
+
+// K slices for the two-phase path: enough wavefronts to spread the Wg read
+// over the chip (about 1024), a power of two that divides H/32.
+int route_kslices(int T, int H, int E) {
+  const int tiles = ((T + 15) / 16) * ((E + 15) / 16);
+  int ks = 1;
+  while (ks * 2 * tiles <= 1024 && (H / 32) % (ks * 2) == 0 && ks * 2 <= 64) ks *= 2;
+  return ks;
+}
+
+bool route_two_phase(int T, bool bf16) { return bf16 && T < 2048; }
+
 template <int MC, int NCW, int KSPLIT>
 hipError_t launch_bf16(const void* x, const void* wg, const float* bias, int T, int H, int E,
                        int k, int32_t* idx, float* w, hipStream_t s) {
@@ -288,8 +373,27 @@ hipError_t launch_bf16_mc(const void* x, const void* wg, const float* bias, int 
 
 }  // namespace
 
+size_t route_ws_bytes(int T, int H, int E, bool bf16) {
+  if (!route_two_phase(T, bf16)) return 0;
+  const size_t b = (size_t)route_kslices(T, H, E) * T * E * sizeof(float);
+  return (b + 255) & ~size_t(255);
+}
+
 hipError_t launch_route(const void* x, const void* wg, const float* bias, int T, int H, int E,
-                        int k, bool bf16, int32_t* topk_idx, float* topk_w, hipStream_t s) {
+                        int k, bool bf16, int32_t* topk_idx, float* topk_w, void* ws,
+                        hipStream_t s) {
+  if (route_two_phase(T, bf16)) {
+    const int nks = route_kslices(T, H, E);
+    const dim3 grid((T + 15) / 16, (E + 15) / 16, nks);
+    hipLaunchKernelGGL(route_partial_kernel, grid, dim3(64), 0, s, static_cast<const uint16_t*>(x),
+                       static_cast<const uint16_t*>(wg), T, H, E, (H / 32) / nks,
+                       static_cast<float*>(ws));
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(kThreads), 0, s,
+                       static_cast<const float*>(ws), bias, T, E, k, nks, topk_idx, topk_w);
+    return hipGetLastError();
+  }
   if (!bf16) {
     const int grid = (T + 15) / 16;
     hipLaunchKernelGGL(route_f32_kernel, dim3(grid), dim3(kThreads), 0, s,
