@@ -35,6 +35,7 @@ HBM_PEAK_GBS = 8000.0
 BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 CPU_TARGET_S = 15.0
+CALIB_BYTES = 512 << 20
 DOMINANT_KERNEL = "gemm_bf16_kernel"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_mixtral_8x7b_pmc.md")
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc", "ffn.hip")
@@ -106,6 +107,8 @@ def main():
     ap.add_argument("--workload", default="mixtral_8x7b")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="end with a plain 512 MiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -246,6 +249,15 @@ def main():
         "kernels": kernels,
         "mfma_util_pct_ffn": 100.0 * achieved / peak,
     }
+    if args.copy_calibration:
+        # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
+        # readings convert those counters to bytes for the kernels above
+        src = torch.ones(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     if not args.no_cpu_baseline:
         # a first small sample sizes a second one to about CPU_TARGET_S seconds
         n = min(args.cpu_tokens, T)
