@@ -107,6 +107,8 @@ def main():
     ap.add_argument("--workload", default="mixtral_8x7b")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the five calls captured in one HIP graph")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain 512 MiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -192,13 +194,28 @@ def main():
         step()
     torch.cuda.synchronize()
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    if args.graph:
+        # per-call times from an eager pass; the timed steps are graph replays
+        for s_ in range(args.steps):
+            step(events[s_])
+        torch.cuda.synchronize()
+        graph = moe.MoELayerGraph(wg, bias, w1, w2, k, T, ws1=ws1, ws2=ws2, capacity_factor=cfg.cf)
+        graph.x.copy_(x)
+        for _ in range(args.warmup):
+            graph.graph.replay()
+        torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
-        step(events[s])
+        if args.graph:
+            graph.graph.replay()
+        else:
+            step(events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    if args.graph:
+        dsp = graph.dsp
 
     names = ["route", "dispatch", "expert_ffn", "combine", "load_stats"]
     per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
@@ -242,7 +259,8 @@ def main():
         "data": "synthetic (seeded Gaussian inputs and random-init weights)",
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k,
                    "d_ff": F, "shared_d_ff": Fs, "routing_bias_amplitude": cfg.bias_amp,
-                   "capacity_factor": cfg.cf, "parallelism": "single GPU"},
+                   "capacity_factor": cfg.cf, "parallelism": "single GPU",
+                   "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "mfma", "kernel": DOMINANT_KERNEL, "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic},

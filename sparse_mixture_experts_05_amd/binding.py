@@ -238,3 +238,72 @@ def moe_layer_forward(x, wg, bias, w1, w2, k: int, ws1=None, ws2=None, stream=No
                              T=x.shape[0], stream=stream)
     out = moe_combine(ys, d["inv"], w, ysh, stream=stream)
     return dict(topk_idx=idx, topk_w=w, ys=ys, ysh=ysh, out=out, **d)
+
+
+class MoELayerGraph:
+    """The five calls captured once into a HIP graph (torch.cuda.CUDAGraph on ROCm)
+    and replayed: one graph launch instead of ~10 kernel launches per layer,
+    the decode-latency use of graph replay the lpqz.cn MoE blog describes (its
+    section 4.3, graph capture of the per-token MoE inference).
+
+    All buffers are allocated once here; ``run(x)`` copies x into the static
+    input buffer and replays. The library never allocates, synchronises or
+    clears memory with memset, so its launches are capture-safe.
+    """
+
+    def __init__(self, wg, bias, w1, w2, k: int, T: int, ws1=None, ws2=None,
+                 capacity_factor: float = 1.25):
+        E, H = wg.shape
+        F = w1.shape[1]
+        Fs = 0 if ws1 is None else ws1.shape[0]
+        dev, dtype = wg.device, wg.dtype
+        dt = _dtype_code(wg)
+        self.k, self.T, self.cf = k, T, capacity_factor
+        self.wg, self.bias, self.w1, self.w2, self.ws1, self.ws2 = wg, bias, w1, w2, ws1, ws2
+        self.x = torch.zeros((T, H), dtype=dtype, device=dev)
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.w = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.dsp = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+                        offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                        perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+                        inv=torch.empty(T * k, dtype=torch.int32, device=dev),
+                        xs=torch.empty((T * k, H), dtype=dtype, device=dev))
+        self.ws_r = torch.empty(max(1, moe_route_workspace_bytes(T, H, E, k, dt)),
+                                dtype=torch.uint8, device=dev)
+        self.ws_d = torch.empty(max(1, moe_dispatch_workspace_bytes(T, E, k)), dtype=torch.uint8,
+                                device=dev)
+        self.ws_f = torch.empty(max(1, moe_expert_ffn_workspace_bytes(T * k, T, H, E, F, Fs, dt)),
+                                dtype=torch.uint8, device=dev)
+        self.ys = torch.empty((T * k, H), dtype=dtype, device=dev)
+        self.ysh = torch.empty((T, H), dtype=dtype, device=dev) if Fs else None
+        self.out = torch.empty((T, H), dtype=dtype, device=dev)
+        self.stats = torch.empty(STATS_BYTES, dtype=torch.uint8, device=dev)
+        self.overflow = torch.empty(E, dtype=torch.int32, device=dev)
+        self.stragglers = torch.empty(E, dtype=torch.int32, device=dev)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self._layer()  # one eager pass on a side stream before capture
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self._layer()
+        torch.cuda.synchronize()
+
+    def _layer(self):
+        moe_route(self.x, self.wg, self.bias, self.k, topk_idx=self.idx, topk_w=self.w,
+                  ws=self.ws_r)
+        moe_dispatch(self.idx, self.x, self.wg.shape[0], out=self.dsp, ws=self.ws_d)
+        moe_expert_ffn(self.dsp["xs"], self.dsp["offsets"], self.w1, self.w2, x=self.x,
+                       ws1=self.ws1, ws2=self.ws2, T=self.T, ys=self.ys, ysh=self.ysh,
+                       ws=self.ws_f)
+        moe_combine(self.ys, self.dsp["inv"], self.w, self.ysh, out=self.out)
+        moe_load_stats(self.dsp["counts"], self.T, self.k, self.cf, stats=self.stats,
+                       overflow=self.overflow, straggler_ids=self.stragglers, read_back=False)
+
+    def run(self, x):
+        """Copy x into the static input and replay; returns the static output tensor."""
+        self.x.copy_(x)
+        self.graph.replay()
+        return self.out
