@@ -18,8 +18,11 @@ Sources (the three web pages this layer is built from):
   [DIAG] "Kimi K3 专家路由不均衡诊断" (bjdmk.com.cn): section 3 diagnostics
         listing (MoERouteDiagnostics: histogram with add.at, capacity
         int(T*k/E*cf), overflow max(0, c - cap), drop rate, Gini, max/min skew,
-        stragglers c > cap) and section 4.2, the biased score
-        Score_i = Softmax(Logits_i + B_i).
+        stragglers c > cap); section 4.1, the statistics f_i (share of the
+        tokens routed to expert i) and P_i (mean router probability) of the
+        auxiliary balance term; section 4.2, the biased score
+        Score_i = Softmax(Logits_i + B_i) and the rule that nudges B_i down for
+        an overloaded expert and up for an idle one.
   [BLOG] "lpqz.cn MoE engineering blog": section 3.1, expert = two Linear
         layers with GeLU; the dispatcher groups tokens by expert id, runs each
         expert on its group and scatters results back to the original order.
@@ -32,7 +35,10 @@ Readings where the pages are silent or garbled (each listed in the design doc):
   * no Linear biases anywhere; weights use the [out, in] layout;
   * capacity drops are counted, never applied to the output;
   * the shared expert has weight 1 and is added to every token;
-  * the residual add that follows the combine is not part of the layer output.
+  * the residual add that follows the combine is not part of the layer output;
+  * the bias rule compares each expert's count with the mean count; the step
+    gamma is a caller's parameter (the page gives no value); f_i divides by
+    the total count, so the f_i sum to 1 like the P_i.
 
 Parity pins: every function here is pinned in tests/test_oracle_pins.py
 against closed forms, hand-worked fixtures, brute force or library special
@@ -41,6 +47,7 @@ cases. None is "parity unpinned".
 from __future__ import annotations
 
 import math
+from fractions import Fraction
 
 import numpy as np
 from scipy.special import erf as _erf
@@ -253,6 +260,55 @@ def load_stats(counts, T: int, k: int, cf: float) -> dict:
                 load_skew_ratio=float(mx) / (float(mn) + 1e-5), gini=gini,
                 drop_rate=float(dropped) / float(assignments),
                 overflow=overflow, straggler_ids=stragglers)
+
+
+# ---------------------------------------------------------------- next: dynamic bias, aux statistics
+
+def load_fraction(counts) -> np.ndarray:
+    """f_i = c_i / sum_e c_e, the share of the routed assignments that expert i
+    received ([DIAG] section 4.1, the f_i of the auxiliary balance term). With
+    one step's counts the denominator is T*k. All zeros when nothing was routed.
+    Returns float64 [E]."""
+    c = np.asarray(counts, dtype=np.int64)
+    total = int(c.sum())
+    if total == 0:
+        return np.zeros(c.size, dtype=np.float64)
+    return c.astype(np.float64) / float(total)
+
+
+def prob_mean(p) -> np.ndarray:
+    """P_i = mean over the T tokens of the router probability p[t, i]
+    ([DIAG] section 4.1, the P_i of the auxiliary balance term). p is the full
+    softmax over all E experts that route() returns, i.e. of Logits + B.
+    Returns float64 [E]."""
+    p = np.asarray(p, dtype=np.float64)
+    return p.sum(axis=0) / p.shape[0]
+
+
+def bias_update(bias, counts, gamma):
+    """One step of the dynamic routing-bias rule ([DIAG] section 4.2).
+
+    An expert whose load is above the mean load sum(c)/E is overloaded: its
+    bias drops by gamma. One below the mean is idle: its bias rises by gamma.
+    One exactly at the mean keeps its bias. The counts may be one step's or
+    summed over a window of steps; the rule only compares each count with
+    their mean (exactly, in integers). Computed in float64 on the float32
+    inputs, rounded once to float32. Returns float32 [E].
+    """
+    b = widen(np.asarray(bias, dtype=np.float32))
+    g = float(np.float32(gamma))
+    c = [int(v) for v in np.asarray(counts).tolist()]
+    E = len(c)
+    mean = Fraction(sum(c), E)
+    out = np.empty(E, dtype=np.float64)
+    for e in range(E):
+        if c[e] > mean:
+            out[e] = b[e] - g
+        elif c[e] < mean:
+            out[e] = b[e] + g
+        else:
+            out[e] = b[e]
+    return out.astype(np.float32)
 
 
 def gini_page_formula(counts) -> float:

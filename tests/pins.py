@@ -363,4 +363,96 @@ def check_stats_strict_straggler_and_overflow():
     assert O.load_stats(c, 30, 2, 1.0)["straggler_ids"] == []
 
 
+# ------------------------------------------------------------------ dynamic bias, aux statistics
+
+def check_bias_update_closed_forms():
+    """Loads above the mean lose gamma, below the mean gain gamma, at the mean keep B."""
+    b = np.array([1.0, 2.0, 3.0, 4.0], dtype=np.float32)
+    got = O.bias_update(b, [3, 1, 2, 2], 0.5)        # mean 2
+    assert got.dtype == np.float32 and got.tolist() == [0.5, 2.5, 3.0, 4.0]
+    got = O.bias_update(b, [8, 0, 0, 0], 0.25)       # one hot expert
+    assert got.tolist() == [0.75, 2.25, 3.25, 4.25]
+    assert O.bias_update(b, [5, 5, 5, 5], 0.5).tolist() == b.tolist()   # balanced
+    assert O.bias_update(b, [0, 0, 0, 0], 0.5).tolist() == b.tolist()   # nothing routed
+    # mean 7/3 is not an integer: 2 < 7/3 < 3
+    assert O.bias_update(np.zeros(3, np.float32), [2, 3, 2], 1.0).tolist() == [1.0, -1.0, 1.0]
+
+
+def check_bias_update_float32_rounding():
+    """The result is B -/+ gamma rounded once to float32: 1 + 2^-25 rounds back to 1,
+    and 2^24 + 1 is not representable either."""
+    b = np.array([1.0, 16777216.0], dtype=np.float32)
+    got = O.bias_update(b, [0, 4], 2.0 ** -25)
+    assert got.tolist() == [1.0, 16777216.0]
+    got = O.bias_update(b, [0, 4], 2.0 ** -23)
+    assert got.tolist() == [1.0 + 2.0 ** -23, 16777216.0]
+
+
+def check_bias_update_balances_a_constant_batch():
+    """Scores equal to the bias alone (x = 0): every token picks the same top-k,
+    so the chosen experts are overloaded and the rest idle; repeated updates
+    must rotate the choice until every expert has been chosen (the rule's purpose)."""
+    E, k, T, H = 6, 2, 12, 4
+    bias = np.array([0.6, 0.5, 0.4, 0.3, 0.2, 0.1], dtype=np.float32)
+    x = np.zeros((T, H))
+    wg = np.zeros((E, H))
+    seen = set()
+    for _ in range(20):
+        idx, _, _, _ = O.route(x, wg, bias, k)
+        c = np.bincount(idx.ravel(), minlength=E)
+        seen.update(idx[0].tolist())
+        new = O.bias_update(bias, c, 0.25)
+        hot = c > T * k / E
+        assert (new[hot] < bias[hot]).all() and (new[~hot] > bias[~hot]).all()
+        bias = new
+    assert seen == set(range(E))
+
+
+def check_load_fraction_closed_forms():
+    """f_i = c_i / sum c: sums to 1; one step's counts give c_i / (T*k)."""
+    assert O.load_fraction([3, 1, 2, 2]).tolist() == [0.375, 0.125, 0.25, 0.25]
+    assert O.load_fraction([0, 0, 0]).tolist() == [0.0, 0.0, 0.0]
+    T, E, k = 40, 8, 3
+    idx = np.stack([_rng(40, t).permutation(E)[:k] for t in range(T)])
+    c = np.bincount(idx.ravel(), minlength=E)
+    f = O.load_fraction(c)
+    assert int(c.sum()) == T * k
+    for fe, ce in zip(f.tolist(), c.tolist()):      # each is c_i/(T*k) rounded once
+        assert fe == float(Fraction(int(ce), T * k))
+    assert abs(f.sum() - 1.0) <= 8 * np.finfo(float).eps
+
+
+def check_prob_mean_closed_form():
+    """Token 0 has scores ln(1..4) so p = (0.1, 0.2, 0.3, 0.4); token 1 has equal
+    scores so p = 1/4 each. P = their average."""
+    E, H = 4, 8
+    wg = np.zeros((E, H))
+    wg[:, 0] = np.log(np.arange(1, E + 1))
+    x = np.zeros((2, H))
+    x[0, 0] = 1.0
+    _, _, _, p = O.route(x, wg, None, 2)
+    np.testing.assert_allclose(O.prob_mean(p), [0.175, 0.225, 0.275, 0.325], rtol=0, atol=1e-15)
+    # the same with the scores carried by the bias (B inside the softmax)
+    _, _, _, p = O.route(np.zeros((3, H)), wg, np.log(np.arange(1, E + 1)).astype(np.float32), 1)
+    np.testing.assert_allclose(O.prob_mean(p), [0.1, 0.2, 0.3, 0.4], rtol=1e-7)
+
+
+def check_prob_mean_k_equals_E_matches_weights():
+    """k = E: the renormalised weights are the softmax itself, so P_i is the mean
+    weight the router gave expert i (scipy softmax gives the same)."""
+    T, E, H = 30, 5, 16
+    x = _rng(41).standard_normal((T, H))
+    wg = _rng(42).standard_normal((E, H))
+    b = _rng(43).standard_normal(E).astype(np.float32)
+    idx, w, s, p = O.route(x, wg, b, E)
+    P = O.prob_mean(p)
+    Pw = np.zeros(E)
+    for t in range(T):
+        for j in range(E):
+            Pw[idx[t, j]] += float(w[t, j]) / T
+    np.testing.assert_allclose(P, Pw, atol=1e-7)
+    np.testing.assert_allclose(P, scipy.special.softmax(x @ wg.T + b, axis=1).mean(0), atol=1e-12)
+    assert abs(P.sum() - 1.0) < 1e-12
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

@@ -138,10 +138,57 @@ def m_straggler_ge(mp):
     mp.setattr(O, "load_stats", load_stats)
 
 
+_bias_update, _load_fraction, _prob_mean = O.bias_update, O.load_fraction, O.prob_mean
+
+
+def m_bias_update_sign_flipped(mp):
+    mp.setattr(O, "bias_update", lambda b, c, g: _bias_update(b, c, -g))
+
+
+def m_bias_update_mean_floor(mp):
+    """Compare with the mean rounded down (integer division) instead of the exact mean."""
+    def bias_update(b, c, g):
+        c = [int(v) for v in c]
+        m = sum(c) // len(c)
+        b = np.asarray(b, dtype=np.float64)
+        return np.array([b[e] - g if c[e] > m else b[e] + g if c[e] < m else b[e]
+                         for e in range(len(c))], dtype=np.float32)
+    mp.setattr(O, "bias_update", bias_update)
+
+
+def m_bias_update_in_float64(mp):
+    """Result left in float64 (no rounding to the float32 bias)."""
+    def bias_update(b, c, g):
+        c = [int(v) for v in c]
+        b = np.asarray(b, dtype=np.float64)
+        E = len(c)
+        return np.array([b[e] - g if c[e] * E > sum(c) else b[e] + g if c[e] * E < sum(c) else b[e]
+                         for e in range(E)])
+    mp.setattr(O, "bias_update", bias_update)
+
+
+def m_load_fraction_per_token(mp):
+    """f_i = c_i / T (tokens) instead of c_i / (T*k) (assignments)."""
+    def load_fraction(c):
+        c = np.asarray(c, dtype=np.int64)
+        return _load_fraction(c) * 2 if c.sum() else _load_fraction(c)
+    mp.setattr(O, "load_fraction", load_fraction)
+
+
+def m_prob_mean_is_sum(mp):
+    mp.setattr(O, "prob_mean", lambda p: np.asarray(p).sum(axis=0))
+
+
+def m_prob_mean_first_token(mp):
+    mp.setattr(O, "prob_mean", lambda p: np.asarray(p, dtype=np.float64)[0].copy())
+
+
 MUTATIONS = [m_no_renormalise, m_select_smallest, m_bias_selection_only, m_ties_to_higher_id,
              m_unstable_dispatch, m_offsets_inclusive, m_gelu_tanh, m_gelu_dropped, m_gelu_sign,
              m_w2_layout_misread, m_w1_layout_misread, m_combine_drops_shared, m_combine_weights_swapped, m_capacity_ceil,
-             m_gini_index_from_zero, m_straggler_ge]
+             m_gini_index_from_zero, m_straggler_ge, m_bias_update_sign_flipped,
+             m_bias_update_mean_floor, m_bias_update_in_float64, m_load_fraction_per_token,
+             m_prob_mean_is_sum, m_prob_mean_first_token]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
