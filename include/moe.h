@@ -9,6 +9,9 @@
  *                  (plus the optional always-on shared expert)
  *   moe_combine    weighted sum of each token's k expert rows (+ shared row)
  *   moe_load_stats capacity, overflow / drops, skew, Gini, stragglers
+ * and, after the layer, the routing-bias feedback of the next step:
+ *   moe_bias_update dynamic bias B from the expert counts, load fractions f_i
+ *   (the mean router probabilities P_i are an optional output of moe_route)
  *
  * Sources of the method (three web pages; cited by title and section):
  *   [K3]   "hncyxsy.com Kimi K3 fine-grained MoE" article: router listing
@@ -88,17 +91,29 @@ typedef struct {
  * x        [T,H] dtype          device, read
  * wg       [E,H] dtype          device, read
  * bias     [E]   fp32 or NULL   device, read (NULL = no routing bias)
+ *   prob_mean[e] = (1/T) sum_t p[t,e], p[t,e] = exp(s[t,e] - m) / sum_e' exp(s[t,e'] - m)
+ *               (the P_i of [DIAG] section 4.1: mean router probability of the
+ *                biased softmax over all E experts; fp32 sums per workgroup in
+ *                token order, summed over workgroups in double in a fixed
+ *                order, so repeated calls give the same bits)
+ * x        [T,H] dtype          device, read
+ * wg       [E,H] dtype          device, read
+ * bias     [E]   fp32 or NULL   device, read (NULL = no routing bias)
  * topk_idx [T,k] int32          device, written
  * topk_w   [T,k] fp32           device, written
+ * prob_mean [E]  fp32 or NULL   device, written (NULL = not computed)
  * ws / ws_bytes: device workspace of at least moe_route_workspace_bytes(T,H,E,k,dtype)
+ *          (NULL / 0 allowed when prob_mean is NULL and the query's score part is 0)
  */
 int moe_route(const void* x, const void* wg, const float* bias, int T, int H, int E, int k,
-              int dtype, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
-              void* stream);
+              int dtype, int32_t* topk_idx, float* topk_w, float* prob_mean, void* ws,
+              size_t ws_bytes, void* stream);
 
-/* Workspace bytes moe_route needs for (T, H, E, k, dtype): 0 when the scores
- * fit the one-launch path (then ws may be NULL); few tokens (T < 2048) use
- * partial score tiles in the workspace. 0 also on unsupported sizes. */
+/* Workspace bytes moe_route needs for (T, H, E, k, dtype) with prob_mean
+ * requested: partial score tiles when few tokens (T < 2048, bf16) take the
+ * two-launch path, plus one row of E partial probability sums per workgroup.
+ * Without prob_mean only the score part is needed, which is 0 for T >= 2048
+ * or fp32. Returns 0 on unsupported sizes. */
 size_t moe_route_workspace_bytes(int T, int H, int E, int k, int dtype);
 
 /* Workspace bytes moe_dispatch needs for (T, E, k); 0 on unsupported sizes. */
@@ -172,6 +187,26 @@ int moe_combine(const void* ys, const int32_t* inv, const float* topk_w, const v
 int moe_load_stats(const int32_t* counts, int T, int E, int k, double capacity_factor,
                    moe_load_stats_t* stats, int32_t* overflow, int32_t* straggler_ids,
                    void* stream);
+
+/*
+ * moe_bias_update - one step of the dynamic routing bias ([DIAG] section 4.2:
+ * lower the bias of an overloaded expert by a small step, raise that of an
+ * idle one) and the load fractions of [DIAG] section 4.1.
+ *   mean = sum_e counts[e] / E (compared exactly: counts[e]*E vs sum)
+ *   bias[e] <- bias[e] - gamma  if counts[e] > mean   (fp32 arithmetic)
+ *              bias[e] + gamma  if counts[e] < mean
+ *              bias[e]          otherwise
+ *   load_frac[e] = counts[e] / sum_e' counts[e'] (double division, rounded
+ *                  to fp32; 0 when the sum is 0)
+ * counts    [E] int32 >= 0  device, read (one step's counts from moe_dispatch,
+ *                           or counts summed by the caller over a window)
+ * bias      [E] fp32        device, read and written in place
+ * load_frac [E] fp32 or NULL device, written
+ * gamma: finite, >= 0. 1 <= E <= 256.
+ * The bias feeds the next moe_route; calls on one stream keep that order.
+ */
+int moe_bias_update(const int32_t* counts, int E, float gamma, float* bias, float* load_frac,
+                    void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* moe_status_string(int status);

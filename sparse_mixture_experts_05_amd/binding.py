@@ -21,7 +21,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
 _vp, _i, _sz, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
 
 SIGNATURES = {
-    "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "moe_route": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _sz, _vp]),
     "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_dispatch_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
@@ -30,6 +30,7 @@ SIGNATURES = {
                             _vp, _vp, _sz, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "moe_load_stats": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
+    "moe_bias_update": (_i, [_vp, _i, ctypes.c_float, _vp, _vp, _vp]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
 }
 
@@ -107,8 +108,12 @@ def moe_route_workspace_bytes(T: int, H: int, E: int, k: int, dtype_code: int) -
     return lib().moe_route_workspace_bytes(T, H, E, k, dtype_code)
 
 
-def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, ws=None, stream=None):
-    """Top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k])."""
+def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, ws=None, stream=None,
+              prob_mean=None):
+    """Top-k routing: returns (topk_idx int32 [T,k], topk_w fp32 [T,k]).
+
+    prob_mean: optional fp32 [E] device tensor that receives the mean router
+    probability of every expert over the T tokens."""
     T, H = x.shape
     E = wg.shape[0]
     if topk_idx is None:
@@ -124,8 +129,21 @@ def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, ws=None, stream=N
     _check("moe_route", lib().moe_route(
         _dev(x, "x"), _dev(wg, "wg", x.dtype), _dev(bias, "bias", torch.float32), T, H, E, k, dt,
         _dev(topk_idx, "topk_idx", torch.int32), _dev(topk_w, "topk_w", torch.float32),
-        ws_ptr, ws_len, _stream(stream)))
+        _dev(prob_mean, "prob_mean", torch.float32), ws_ptr, ws_len, _stream(stream)))
     return topk_idx, topk_w
+
+
+def moe_bias_update(counts, bias, gamma: float, load_frac=None, stream=None):
+    """Dynamic routing-bias step in place on ``bias`` (fp32 [E]) from the expert
+    counts (int32 [E]); writes the load fractions into ``load_frac`` if given.
+    Returns load_frac."""
+    E = counts.shape[0]
+    if bias.shape[0] != E or (load_frac is not None and load_frac.shape[0] != E):
+        raise ValueError("counts, bias and load_frac must all have E entries")
+    _check("moe_bias_update", lib().moe_bias_update(
+        _dev(counts, "counts", torch.int32), E, float(gamma), _dev(bias, "bias", torch.float32),
+        _dev(load_frac, "load_frac", torch.float32), _stream(stream)))
+    return load_frac
 
 
 def moe_dispatch_workspace_bytes(T: int, E: int, k: int) -> int:
@@ -229,10 +247,12 @@ def moe_load_stats(counts, T: int, k: int, capacity_factor: float, stats=None, o
     return d
 
 
-def moe_layer_forward(x, wg, bias, w1, w2, k: int, ws1=None, ws2=None, stream=None):
-    """All five steps on one stream (no host synchronisation). Returns a dict."""
+def moe_layer_forward(x, wg, bias, w1, w2, k: int, ws1=None, ws2=None, stream=None,
+                      prob_mean=None):
+    """All five steps on one stream (no host synchronisation). Returns a dict.
+    prob_mean (optional fp32 [E]) receives the mean router probabilities."""
     E = wg.shape[0]
-    idx, w = moe_route(x, wg, bias, k, stream=stream)
+    idx, w = moe_route(x, wg, bias, k, stream=stream, prob_mean=prob_mean)
     d = moe_dispatch(idx, x, E, stream=stream)
     ys, ysh = moe_expert_ffn(d["xs"], d["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2,
                              T=x.shape[0], stream=stream)
@@ -249,10 +269,15 @@ class MoELayerGraph:
     All buffers are allocated once here; ``run(x)`` copies x into the static
     input buffer and replays. The library never allocates, synchronises or
     clears memory with memset, so its launches are capture-safe.
+
+    With ``bias_gamma`` set (and a bias tensor given), every replay also ends
+    with the dynamic-bias step on ``bias`` in place and writes the mean router
+    probabilities ``prob_mean`` and load fractions ``load_frac``: the next
+    replay routes with the updated bias.
     """
 
     def __init__(self, wg, bias, w1, w2, k: int, T: int, ws1=None, ws2=None,
-                 capacity_factor: float = 1.25):
+                 capacity_factor: float = 1.25, bias_gamma: float | None = None):
         E, H = wg.shape
         F = w1.shape[1]
         Fs = 0 if ws1 is None else ws1.shape[0]
@@ -280,8 +305,14 @@ class MoELayerGraph:
         self.stats = torch.empty(STATS_BYTES, dtype=torch.uint8, device=dev)
         self.overflow = torch.empty(E, dtype=torch.int32, device=dev)
         self.stragglers = torch.empty(E, dtype=torch.int32, device=dev)
+        if bias_gamma is not None and bias is None:
+            raise ValueError("bias_gamma needs a bias tensor to update")
+        self.gamma = bias_gamma
+        self.prob_mean = torch.empty(E, dtype=torch.float32, device=dev) if bias_gamma is not None else None
+        self.load_frac = torch.empty(E, dtype=torch.float32, device=dev) if bias_gamma is not None else None
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
+        saved = None if bias is None else bias.clone()
         with torch.cuda.stream(side):
             self._layer()  # one eager pass on a side stream before capture
         torch.cuda.current_stream().wait_stream(side)
@@ -290,10 +321,13 @@ class MoELayerGraph:
         with torch.cuda.graph(self.graph):
             self._layer()
         torch.cuda.synchronize()
+        if saved is not None:
+            bias.copy_(saved)  # the warm-up pass must not have moved the bias
+            torch.cuda.synchronize()
 
     def _layer(self):
         moe_route(self.x, self.wg, self.bias, self.k, topk_idx=self.idx, topk_w=self.w,
-                  ws=self.ws_r)
+                  ws=self.ws_r, prob_mean=self.prob_mean)
         moe_dispatch(self.idx, self.x, self.wg.shape[0], out=self.dsp, ws=self.ws_d)
         moe_expert_ffn(self.dsp["xs"], self.dsp["offsets"], self.w1, self.w2, x=self.x,
                        ws1=self.ws1, ws2=self.ws2, T=self.T, ys=self.ys, ysh=self.ysh,
@@ -301,6 +335,8 @@ class MoELayerGraph:
         moe_combine(self.ys, self.dsp["inv"], self.w, self.ysh, out=self.out)
         moe_load_stats(self.dsp["counts"], self.T, self.k, self.cf, stats=self.stats,
                        overflow=self.overflow, straggler_ids=self.stragglers, read_back=False)
+        if self.gamma is not None:
+            moe_bias_update(self.dsp["counts"], self.bias, self.gamma, load_frac=self.load_frac)
 
     def run(self, x):
         """Copy x into the static input and replay; returns the static output tensor."""

@@ -20,7 +20,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-SOURCES = ["route.hip", "dispatch.hip", "ffn.hip", "combine.hip", "stats.hip", "moe_api.cpp"]
+SOURCES = ["route.hip", "dispatch.hip", "ffn.hip", "combine.hip", "stats.hip", "bias.hip", "moe_api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -7,10 +7,10 @@
 
 namespace moe {
 
-size_t route_ws_bytes(int T, int H, int E, bool bf16);
+size_t route_ws_bytes(int T, int H, int E, bool bf16, bool prob);
 hipError_t launch_route(const void* x, const void* wg, const float* bias, int T, int H, int E,
-                        int k, bool bf16, int32_t* topk_idx, float* topk_w, void* ws,
-                        hipStream_t s);
+                        int k, bool bf16, int32_t* topk_idx, float* topk_w, float* prob_mean,
+                        void* ws, hipStream_t s);
 
 int dispatch_blocks(int T);
 size_t dispatch_ws_bytes(int T, int E);
@@ -31,5 +31,8 @@ hipError_t launch_combine(const void* ys, const int32_t* inv, const float* topk_
 hipError_t launch_load_stats(const int32_t* counts, int T, int E, int k, double cf,
                              void* stats, int32_t* overflow, int32_t* straggler_ids,
                              hipStream_t s);
+
+hipError_t launch_bias_update(const int32_t* counts, int E, float gamma, float* bias,
+                              float* load_frac, hipStream_t s);
 
 }  // namespace moe

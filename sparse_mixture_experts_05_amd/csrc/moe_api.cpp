@@ -47,19 +47,19 @@ const char* moe_status_string(int status) {
 
 size_t moe_route_workspace_bytes(int T, int H, int E, int k, int dtype) {
   if (!dtype_ok(dtype) || check_tokens(T, H, E, k) != MOE_OK) return 0;
-  return moe::route_ws_bytes(T, H, E, dtype == MOE_BF16);
+  return moe::route_ws_bytes(T, H, E, dtype == MOE_BF16, true);
 }
 
 int moe_route(const void* x, const void* wg, const float* bias, int T, int H, int E, int k,
-              int dtype, int32_t* topk_idx, float* topk_w, void* ws, size_t ws_bytes,
-              void* stream) {
+              int dtype, int32_t* topk_idx, float* topk_w, float* prob_mean, void* ws,
+              size_t ws_bytes, void* stream) {
   if (!x || !wg || !topk_idx || !topk_w || !dtype_ok(dtype)) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
-  const size_t need = moe::route_ws_bytes(T, H, E, dtype == MOE_BF16);
+  const size_t need = moe::route_ws_bytes(T, H, E, dtype == MOE_BF16, prob_mean != nullptr);
   if (need > 0 && (!ws || ws_bytes < need)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_route(x, wg, bias, T, H, E, k, dtype == MOE_BF16, topk_idx, topk_w,
-                                    ws, as_stream(stream)));
+                                    prob_mean, ws, as_stream(stream)));
 }
 
 size_t moe_dispatch_workspace_bytes(int T, int E, int k) {
@@ -125,6 +125,14 @@ int moe_load_stats(const int32_t* counts, int T, int E, int k, double capacity_f
   if (st != MOE_OK) return st;
   return from_hip(moe::launch_load_stats(counts, T, E, k, capacity_factor, stats, overflow,
                                          straggler_ids, as_stream(stream)));
+}
+
+int moe_bias_update(const int32_t* counts, int E, float gamma, float* bias, float* load_frac,
+                    void* stream) {
+  if (!counts || !bias || E < 1 || !std::isfinite(gamma) || gamma < 0.0f)
+    return MOE_ERR_INVALID_ARG;
+  if (E > kMaxExperts) return MOE_ERR_UNSUPPORTED;
+  return from_hip(moe::launch_bias_update(counts, E, gamma, bias, load_frac, as_stream(stream)));
 }
 
 }  // extern "C"

@@ -62,6 +62,19 @@ __device__ __forceinline__ void wave_argmax(float& v, int& i) {
   take_better(v, i, v1, i1);
 }
 
+// Sum over the 64 lanes with the same exchange pattern as wave_argmax. Each
+// step adds a lane's value and its partner's, and fp addition is commutative,
+// so every lane ends with the same bits.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
+         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+}
+
 // Best live slot of this lane. Slots that are out of range or already taken
 // are dead and never win (a NaN score is read as -inf, so every live slot
 // beats every dead one and the k ids are always distinct and < E).
@@ -81,10 +94,14 @@ __device__ __forceinline__ void lane_best(const float (&v)[4], unsigned alive, i
 }
 
 // Phase 2: scores of BT tokens are in LDS (row-major, kLogitStride).
-__device__ __forceinline__ void topk_phase(const float* sc, int BT, int t0, int T, int E, int k,
+// When pp is not null, the full softmax p[t, e] = exp(s_e - m) / sum_e' exp(s_e' - m)
+// of every token is also summed over the workgroup's tokens (per wave in
+// token order, then the 4 waves in order) and pp[e] receives the sum. The
+// score tile is reused for that reduction, so sc is clobbered.
+__device__ __forceinline__ void topk_phase(float* sc, int BT, int t0, int T, int E, int k,
                                            const float* __restrict__ bias,
                                            int32_t* __restrict__ topk_idx,
-                                           float* __restrict__ topk_w) {
+                                           float* __restrict__ topk_w, float* __restrict__ pp) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float b[4];
 #pragma unroll
@@ -92,6 +109,7 @@ __device__ __forceinline__ void topk_phase(const float* sc, int BT, int t0, int 
     const int e = lane + 64 * q;
     b[q] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
   }
+  float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
   for (int t = wave; t < BT; t += kThreads / kWave) {
     const int tok = t0 + t;
     if (tok >= T) break;
@@ -124,6 +142,21 @@ __device__ __forceinline__ void topk_phase(const float* sc, int BT, int t0, int 
       }
     }
     const float m = sv[0];
+    if (pp != nullptr) {
+      // dead slots hold -inf and give 0; a token whose scores are all -inf or
+      // NaN has no distribution and adds nothing
+      float z[4], zs = 0.0f;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        z[q] = m > -INFINITY ? expf(v[q] - m) : 0.0f;
+        zs += z[q];
+      }
+      const float Z = wave_sum(zs);
+      if (Z > 0.0f) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) pacc[q] += z[q] / Z;
+      }
+    }
     float ex[8];
     float sum = 0.0f;
 #pragma unroll
@@ -140,6 +173,28 @@ __device__ __forceinline__ void topk_phase(const float* sc, int BT, int t0, int 
         topk_w[(size_t)tok * k + j] = ex[j] / sum;
       }
     }
+  }
+  if (pp != nullptr) {
+    __syncthreads();  // every wave is done with the score tile
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int e = lane + 64 * q;
+      if (e < E) sc[wave * kMaxE + e] = pacc[q];
+    }
+    __syncthreads();
+    for (int e = threadIdx.x; e < E; e += kThreads)
+      pp[e] = ((sc[e] + sc[kMaxE + e]) + sc[2 * kMaxE + e]) + sc[3 * kMaxE + e];
+  }
+}
+
+// P[e] = (sum over workgroups b, ascending, of part[b][e]) / T, in double.
+__global__ __launch_bounds__(kThreads) void prob_mean_kernel(const float* __restrict__ part,
+                                                             int nb, int T, int E,
+                                                             float* __restrict__ prob_mean) {
+  for (int e = threadIdx.x; e < E; e += kThreads) {
+    double s = 0.0;
+    for (int b = 0; b < nb; ++b) s += (double)part[(size_t)b * E + e];
+    prob_mean[e] = (float)(s / (double)T);
   }
 }
 
@@ -192,8 +247,9 @@ template <int MC, int NCW, int KSPLIT>
 __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const float* __restrict__ bias, int T, int H, int E, int k, int32_t* __restrict__ topk_idx,
-    float* __restrict__ topk_w) {
+    float* __restrict__ topk_w, float* __restrict__ ppart) {
   constexpr int BT = MC * 16;
+  static_assert(BT * kLogitStride >= 4 * kMaxE, "score tile too small for the probability sums");
   __shared__ float sc[BT * kLogitStride];
   __shared__ float part[KSPLIT == 4 ? 4 * BT * 48 : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -257,13 +313,15 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
     }
     __syncthreads();
   }
-  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w);
+  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w,
+             ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 // fp32 scores with plain dot products (small fp32 layers).
 __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     const float* __restrict__ x, const float* __restrict__ wg, const float* __restrict__ bias,
-    int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w) {
+    int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
+    float* __restrict__ ppart) {
   constexpr int BT = 16;
   __shared__ float sc[BT * kLogitStride];
   const int t0 = blockIdx.x * BT;
@@ -282,7 +340,8 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     sc[t * kLogitStride + e] = s;
   }
   __syncthreads();
-  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w);
+  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w,
+             ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 
@@ -315,7 +374,8 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __r
                                                                 const float* __restrict__ bias,
                                                                 int T, int E, int k, int nks,
                                                                 int32_t* __restrict__ topk_idx,
-                                                                float* __restrict__ topk_w) {
+                                                                float* __restrict__ topk_w,
+                                                                float* __restrict__ ppart) {
   constexpr int BT = kThreads / kWave;  // 4 tokens per workgroup
   __shared__ float sc[BT * kLogitStride];
   const int t0 = blockIdx.x * BT;
@@ -328,7 +388,8 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __r
     }
   }
   __syncthreads();
-  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w);
+  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w,
+             ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 // K slices for the two-phase path: enough wavefronts to spread the Wg read
@@ -344,67 +405,95 @@ bool route_two_phase(int T, bool bf16) { return bf16 && T < 2048; }
 
 template <int MC, int NCW, int KSPLIT>
 hipError_t launch_bf16(const void* x, const void* wg, const float* bias, int T, int H, int E,
-                       int k, int32_t* idx, float* w, hipStream_t s) {
+                       int k, int32_t* idx, float* w, float* pp, hipStream_t s) {
   const int grid = (T + MC * 16 - 1) / (MC * 16);
   hipLaunchKernelGGL((route_bf16_kernel<MC, NCW, KSPLIT>), dim3(grid), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, T,
-                     H, E, k, idx, w);
+                     H, E, k, idx, w, pp);
   return hipGetLastError();
 }
 
 template <int MC>
 hipError_t launch_bf16_mc(const void* x, const void* wg, const float* bias, int T, int H, int E,
-                          int k, int32_t* idx, float* w, hipStream_t s) {
+                          int k, int32_t* idx, float* w, float* pp, hipStream_t s) {
   const int nc = (E + 15) / 16;
   if (nc < 4) {
     switch (nc) {
-      case 1: return launch_bf16<MC, 1, 4>(x, wg, bias, T, H, E, k, idx, w, s);
-      case 2: return launch_bf16<MC, 2, 4>(x, wg, bias, T, H, E, k, idx, w, s);
-      default: return launch_bf16<MC, 3, 4>(x, wg, bias, T, H, E, k, idx, w, s);
+      case 1: return launch_bf16<MC, 1, 4>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+      case 2: return launch_bf16<MC, 2, 4>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+      default: return launch_bf16<MC, 3, 4>(x, wg, bias, T, H, E, k, idx, w, pp, s);
     }
   }
   switch ((nc + 3) / 4) {
-    case 1: return launch_bf16<MC, 1, 1>(x, wg, bias, T, H, E, k, idx, w, s);
-    case 2: return launch_bf16<MC, 2, 1>(x, wg, bias, T, H, E, k, idx, w, s);
-    case 3: return launch_bf16<MC, 3, 1>(x, wg, bias, T, H, E, k, idx, w, s);
-    default: return launch_bf16<MC, 4, 1>(x, wg, bias, T, H, E, k, idx, w, s);
+    case 1: return launch_bf16<MC, 1, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+    case 2: return launch_bf16<MC, 2, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+    case 3: return launch_bf16<MC, 3, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+    default: return launch_bf16<MC, 4, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
   }
+}
+
+// Tokens per workgroup of the one-launch bf16 path: as many as keep >= 256
+// workgroups (one per CU).
+int bf16_tokens_per_block(int T) { return T >= 64 * 256 ? 64 : T >= 32 * 256 ? 32 : 16; }
+
+// Workgroups of the launch that runs the top-k (one partial probability row each).
+int topk_blocks(int T, bool bf16) {
+  if (route_two_phase(T, bf16)) return (T + 3) / 4;
+  const int bt = bf16 ? bf16_tokens_per_block(T) : 16;
+  return (T + bt - 1) / bt;
+}
+
+size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
+
+size_t scores_ws_bytes(int T, int H, int E, bool bf16) {
+  if (!route_two_phase(T, bf16)) return 0;
+  return align256((size_t)route_kslices(T, H, E) * T * E * sizeof(float));
 }
 
 }  // namespace
 
-size_t route_ws_bytes(int T, int H, int E, bool bf16) {
-  if (!route_two_phase(T, bf16)) return 0;
-  const size_t b = (size_t)route_kslices(T, H, E) * T * E * sizeof(float);
-  return (b + 255) & ~size_t(255);
+size_t route_ws_bytes(int T, int H, int E, bool bf16, bool prob) {
+  size_t b = scores_ws_bytes(T, H, E, bf16);
+  if (prob) b += align256((size_t)topk_blocks(T, bf16) * E * sizeof(float));
+  return b;
 }
 
 hipError_t launch_route(const void* x, const void* wg, const float* bias, int T, int H, int E,
-                        int k, bool bf16, int32_t* topk_idx, float* topk_w, void* ws,
-                        hipStream_t s) {
+                        int k, bool bf16, int32_t* topk_idx, float* topk_w, float* prob_mean,
+                        void* ws, hipStream_t s) {
+  // partial probability sums sit after the partial score tiles
+  float* pp = prob_mean == nullptr
+                  ? nullptr
+                  : reinterpret_cast<float*>(static_cast<char*>(ws) + scores_ws_bytes(T, H, E, bf16));
+  hipError_t err = hipSuccess;
   if (route_two_phase(T, bf16)) {
     const int nks = route_kslices(T, H, E);
     const dim3 grid((T + 15) / 16, (E + 15) / 16, nks);
     hipLaunchKernelGGL(route_partial_kernel, grid, dim3(64), 0, s, static_cast<const uint16_t*>(x),
                        static_cast<const uint16_t*>(wg), T, H, E, (H / 32) / nks,
                        static_cast<float*>(ws));
-    hipError_t err = hipGetLastError();
+    err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(kThreads), 0, s,
-                       static_cast<const float*>(ws), bias, T, E, k, nks, topk_idx, topk_w);
-    return hipGetLastError();
-  }
-  if (!bf16) {
+                       static_cast<const float*>(ws), bias, T, E, k, nks, topk_idx, topk_w, pp);
+    err = hipGetLastError();
+  } else if (!bf16) {
     const int grid = (T + 15) / 16;
     hipLaunchKernelGGL(route_f32_kernel, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const float*>(x), static_cast<const float*>(wg), bias, T, H, E,
-                       k, topk_idx, topk_w);
-    return hipGetLastError();
+                       k, topk_idx, topk_w, pp);
+    err = hipGetLastError();
+  } else {
+    switch (bf16_tokens_per_block(T)) {
+      case 64: err = launch_bf16_mc<4>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
+      case 32: err = launch_bf16_mc<2>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
+      default: err = launch_bf16_mc<1>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
+    }
   }
-  // Tokens per workgroup: as many as keep >= 256 workgroups (one per CU).
-  if (T >= 64 * 256) return launch_bf16_mc<4>(x, wg, bias, T, H, E, k, topk_idx, topk_w, s);
-  if (T >= 32 * 256) return launch_bf16_mc<2>(x, wg, bias, T, H, E, k, topk_idx, topk_w, s);
-  return launch_bf16_mc<1>(x, wg, bias, T, H, E, k, topk_idx, topk_w, s);
+  if (err != hipSuccess || prob_mean == nullptr) return err;
+  hipLaunchKernelGGL(prob_mean_kernel, dim3(1), dim3(kThreads), 0, s, pp, topk_blocks(T, bf16), T,
+                     E, prob_mean);
+  return hipGetLastError();
 }
 
 }  // namespace moe

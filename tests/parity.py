@@ -7,6 +7,9 @@ CPU oracle:
              field, the straggler list and overflow, and the double fields
              gini / load_skew_ratio / drop_rate (same IEEE operations);
   topk_w:    max |diff| <= TOL_W;
+  prob_mean: |diff| <= TOL_P * P_oracle per expert (mean router probability);
+  bias update and load fractions (one step from the GPU's counts, on the
+             layer's bias or a zero bias): bit-exact;
   ys, out:   fp32 layers max |diff| <= 1e-4; bf16 layers relative L2 error
              <= 2e-2 against the float64 oracle (which never rounds to bf16).
 With ``sample`` (token ids) the FFN and combine outputs are checked on those
@@ -19,11 +22,13 @@ import numpy as np
 import torch
 
 import oracle
-from sparse_mixture_experts_05_amd import moe_layer_forward, moe_load_stats
+from sparse_mixture_experts_05_amd import moe_bias_update, moe_layer_forward, moe_load_stats
 
 TOL_W = 1e-4
 TOL_F32_ABS = 1e-4
 TOL_BF16_REL_L2 = 2e-2
+TOL_P = 1e-4          # relative, per expert (fp32 softmax and sums vs float64)
+GAMMA = 1e-3          # bias step used by the parity runs (rounded to fp32 by both sides)
 
 
 def to_dev(a):
@@ -45,11 +50,17 @@ def to_host(t):
 def run_layer(cfg, L, sample=None):
     """All five steps on the GPU; returns host copies (ys/out on ``sample`` rows)."""
     d = {k: to_dev(v) for k, v in L.items()}
+    pm = torch.empty(cfg.E, dtype=torch.float32, device="cuda")
     r = moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"], cfg.k,
-                          ws1=d["ws1"], ws2=d["ws2"])
+                          ws1=d["ws1"], ws2=d["ws2"], prob_mean=pm)
     st = moe_load_stats(r["counts"], cfg.T, cfg.k, cfg.cf)
+    b = d["bias"].clone() if d["bias"] is not None else torch.zeros(cfg.E, dtype=torch.float32,
+                                                                     device="cuda")
+    frac = torch.empty(cfg.E, dtype=torch.float32, device="cuda")
+    moe_bias_update(r["counts"], b, GAMMA, load_frac=frac)
     torch.cuda.synchronize()
     got = {k: to_host(r[k]) for k in ["topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "xs"]}
+    got["prob_mean"], got["bias_next"], got["load_frac"] = to_host(pm), to_host(b), to_host(frac)
     if sample is None:
         got["ys"], got["out"] = to_host(r["ys"]), to_host(r["out"])
         got["ysh"] = to_host(r["ysh"])
@@ -87,16 +98,26 @@ def check_layer(cfg, L, got, sample=None) -> dict:
     T, k, E = cfg.T, cfg.k, cfg.E
     bf16 = cfg.dtype == "bf16"
     report = {}
-    idx, w, _, _ = oracle.route(L["x"], L["wg"], L["bias"], k)
+    idx, w, _, p = oracle.route(L["x"], L["wg"], L["bias"], k)
     bad = int((got["topk_idx"] != idx).any(axis=1).sum())
     assert bad == 0, f"topk_idx differs on {bad} tokens"
     werr = float(np.abs(got["topk_w"] - w).max())
     report["topk_w_max_abs"] = werr
     assert werr <= TOL_W, f"topk_w max abs {werr:.3e} > {TOL_W}"
+    P = oracle.prob_mean(p)
+    del p
+    perr = float((np.abs(got["prob_mean"].astype(np.float64) - P) / P).max())
+    report["prob_mean_max_rel"] = perr
+    assert perr <= TOL_P, f"prob_mean max rel {perr:.3e} > {TOL_P}"
 
     counts, offsets, perm, inv, _ = oracle.dispatch(idx, np.empty((T, 0)), E)
     for name, ref in [("counts", counts), ("offsets", offsets), ("perm", perm), ("inv", inv)]:
         assert np.array_equal(got[name], ref), f"{name} differs"
+    b0 = L["bias"] if L["bias"] is not None else np.zeros(E, dtype=np.float32)
+    b_ref = oracle.bias_update(b0, counts, GAMMA)
+    assert np.array_equal(got["bias_next"].view(np.uint32), b_ref.view(np.uint32)), "bias update differs"
+    f_ref = oracle.load_fraction(counts).astype(np.float32)
+    assert np.array_equal(got["load_frac"].view(np.uint32), f_ref.view(np.uint32)), "load_frac differs"
     tok = perm // k
     for a in range(0, perm.size, 65536):
         assert np.array_equal(got["xs"][a:a + 65536], L["x"][tok[a:a + 65536]]), "xs differs"

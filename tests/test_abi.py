@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_five_steps():
     names = declared_functions()
     for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_load_stats",
-              "moe_status_string", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
+              "moe_bias_update", "moe_status_string", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
               "moe_expert_ffn_workspace_bytes"]:
         assert n in names
 
@@ -51,31 +51,48 @@ def test_stats_struct_size():
 def test_route_validation():
     L = moe.lib()
     # null pointers
-    assert L.moe_route(None, FAKE, None, 4, 64, 8, 2, 1, FAKE, FAKE, None, 0, None) == -1
-    assert L.moe_route(FAKE, FAKE, None, 4, 64, 8, 2, 1, None, FAKE, None, 0, None) == -1
+    assert L.moe_route(None, FAKE, None, 4, 64, 8, 2, 1, FAKE, FAKE, None, None, 0, None) == -1
+    assert L.moe_route(FAKE, FAKE, None, 4, 64, 8, 2, 1, None, FAKE, None, None, 0, None) == -1
     # bad dtype, non-positive sizes
-    assert L.moe_route(FAKE, FAKE, None, 4, 64, 8, 2, 7, FAKE, FAKE, None, 0, None) == -1
-    assert L.moe_route(FAKE, FAKE, None, 0, 64, 8, 2, 1, FAKE, FAKE, None, 0, None) == -1
-    assert L.moe_route(FAKE, FAKE, None, 4, 64, 8, 0, 1, FAKE, FAKE, None, 0, None) == -1
+    assert L.moe_route(FAKE, FAKE, None, 4, 64, 8, 2, 7, FAKE, FAKE, None, None, 0, None) == -1
+    assert L.moe_route(FAKE, FAKE, None, 0, 64, 8, 2, 1, FAKE, FAKE, None, None, 0, None) == -1
+    assert L.moe_route(FAKE, FAKE, None, 4, 64, 8, 0, 1, FAKE, FAKE, None, None, 0, None) == -1
     # unsupported shapes: E > 256, k > 8, k > E, H % 64, T*k >= 2^31
-    assert L.moe_route(FAKE, FAKE, None, 4, 64, 257, 2, 1, FAKE, FAKE, None, 0, None) == -2
-    assert L.moe_route(FAKE, FAKE, None, 4, 64, 64, 9, 1, FAKE, FAKE, None, 0, None) == -2
-    assert L.moe_route(FAKE, FAKE, None, 4, 64, 4, 5, 1, FAKE, FAKE, None, 0, None) == -2
-    assert L.moe_route(FAKE, FAKE, None, 4, 96, 8, 2, 1, FAKE, FAKE, None, 0, None) == -2
-    assert L.moe_route(FAKE, FAKE, None, 1 << 28, 64, 64, 8, 1, FAKE, FAKE, None, 0, None) == -2
+    assert L.moe_route(FAKE, FAKE, None, 4, 64, 257, 2, 1, FAKE, FAKE, None, None, 0, None) == -2
+    assert L.moe_route(FAKE, FAKE, None, 4, 64, 64, 9, 1, FAKE, FAKE, None, None, 0, None) == -2
+    assert L.moe_route(FAKE, FAKE, None, 4, 64, 4, 5, 1, FAKE, FAKE, None, None, 0, None) == -2
+    assert L.moe_route(FAKE, FAKE, None, 4, 96, 8, 2, 1, FAKE, FAKE, None, None, 0, None) == -2
+    assert L.moe_route(FAKE, FAKE, None, 1 << 28, 64, 64, 8, 1, FAKE, FAKE, None, None, 0, None) == -2
 
 
 def test_route_workspace():
     L = moe.lib()
-    # decode-sized batches use the two-launch path and need a workspace
+    # decode-sized batches use the two-launch path and need a workspace for the
+    # score tiles; the query also covers the per-workgroup probability sums
     need = L.moe_route_workspace_bytes(16, 4096, 128, 8, 1)
-    assert need >= 16 * 128 * 4 and need % 256 == 0
-    assert L.moe_route(FAKE, FAKE, None, 16, 4096, 128, 8, 1, FAKE, FAKE, None, 0, None) == -3
-    assert L.moe_route(FAKE, FAKE, None, 16, 4096, 128, 8, 1, FAKE, FAKE, FAKE, need - 1, None) == -3
-    # large batches do not
-    assert L.moe_route_workspace_bytes(4096, 4096, 128, 8, 1) == 0
-    assert L.moe_route_workspace_bytes(64, 256, 8, 2, 0) == 0
+    assert need >= 16 * 128 * 4 + 4 * 128 * 4 and need % 256 == 0
+    assert L.moe_route(FAKE, FAKE, None, 16, 4096, 128, 8, 1, FAKE, FAKE, None, None, 0, None) == -3
+    assert L.moe_route(FAKE, FAKE, None, 16, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE, need - 1, None) == -3
+    # large batches only need it for the mean probabilities: one row of E
+    # floats per workgroup of 16 tokens (T = 4096, bf16) or 16 tokens (fp32)
+    assert L.moe_route_workspace_bytes(4096, 4096, 128, 8, 1) == 256 * 128 * 4
+    assert L.moe_route_workspace_bytes(64, 256, 8, 2, 0) == 256
+    assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, None, 0, None) == -3
+    assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE,
+                       256 * 128 * 4 - 1, None) == -3
     assert L.moe_route_workspace_bytes(16, 4096, 300, 8, 1) == 0
+
+
+def test_bias_update_validation():
+    L = moe.lib()
+    f = ctypes.c_float
+    assert L.moe_bias_update(None, 8, f(0.01), FAKE, None, None) == -1
+    assert L.moe_bias_update(FAKE, 8, f(0.01), None, None, None) == -1
+    assert L.moe_bias_update(FAKE, 0, f(0.01), FAKE, None, None) == -1
+    assert L.moe_bias_update(FAKE, 8, f(-0.01), FAKE, None, None) == -1
+    assert L.moe_bias_update(FAKE, 8, f(float("nan")), FAKE, None, None) == -1
+    assert L.moe_bias_update(FAKE, 8, f(float("inf")), FAKE, None, None) == -1
+    assert L.moe_bias_update(FAKE, 257, f(0.01), FAKE, None, None) == -2
 
 
 def test_dispatch_validation_and_workspace():

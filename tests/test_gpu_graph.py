@@ -35,3 +35,37 @@ def test_graph_replays_match_eager(name):
         assert np.array_equal(idx_g, to_host(eager["topk_idx"])), rep
         assert np.array_equal(counts_g, to_host(eager["counts"])), rep
         assert np.array_equal(out_g, to_host(eager["out"])), rep
+
+
+def test_graph_with_bias_feedback_matches_eager_loop():
+    """The graph with the dynamic-bias step: each replay routes with the bias the
+    previous replay wrote. An eager loop on its own bias copy must give the same
+    bias, mean probabilities, load fractions and output after every step."""
+    cfg = get_config("decode@T32")
+    L = make_layer(cfg)
+    d = {k: to_dev(v) for k, v in L.items()}
+    E = cfg.E
+    gamma = 0.05
+    b_graph = torch.zeros(E, dtype=torch.float32, device="cuda")
+    b_eager = torch.zeros(E, dtype=torch.float32, device="cuda")
+    print("\n[gpu] graph with bias feedback decode@T32", flush=True)
+    g = moe.MoELayerGraph(d["wg"], b_graph, d["w1"], d["w2"], cfg.k, cfg.T, ws1=d["ws1"],
+                          ws2=d["ws2"], capacity_factor=cfg.cf, bias_gamma=gamma)
+    assert (to_host(b_graph) == 0).all()          # warm-up did not move the bias
+    pm = torch.empty(E, dtype=torch.float32, device="cuda")
+    frac = torch.empty(E, dtype=torch.float32, device="cuda")
+    moved = 0
+    for rep in range(5):
+        xr = to_dev(redraw_rows(cfg, np.arange(cfg.T), 200 + rep))
+        out_g = to_host(g.run(xr).clone())
+        torch.cuda.synchronize()
+        r = moe.moe_layer_forward(xr, d["wg"], b_eager, d["w1"], d["w2"], cfg.k, ws1=d["ws1"],
+                                  ws2=d["ws2"], prob_mean=pm)
+        moe.moe_bias_update(r["counts"], b_eager, gamma, load_frac=frac)
+        torch.cuda.synchronize()
+        assert np.array_equal(out_g, to_host(r["out"])), rep
+        assert np.array_equal(to_host(g.prob_mean), to_host(pm)), rep
+        assert np.array_equal(to_host(g.load_frac), to_host(frac)), rep
+        assert np.array_equal(to_host(b_graph), to_host(b_eager)), rep
+        moved = max(moved, int((to_host(b_graph) != 0).sum()))
+    assert moved > 0
