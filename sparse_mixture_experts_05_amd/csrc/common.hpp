@@ -63,4 +63,35 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_
 __device__ __forceinline__ u32x4_t ld16(const void* p) { return *reinterpret_cast<const u32x4_t*>(p); }
 __device__ __forceinline__ void st16(void* p, u32x4_t v) { *reinterpret_cast<u32x4_t*>(p) = v; }
 
+// Wait until at most N global loads of this wave are outstanding (they
+// complete in issue order).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// Workgroup barrier for LDS hand-off only. __syncthreads() carries a release
+// fence that waits for every outstanding global load (vmcnt 0), which would
+// drain the next stage's prefetch; the staged loads are waited for explicitly.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// global_load_lds_dwordx4: lane i copies 16 bytes from its address g into
+// LDS at M0 + 16*i (M0 = the wave-uniform LDS address). Issued through asm so
+// the compiler's wait insertion does not treat every later LDS read as
+// aliasing the in-flight copy (which would drain the prefetch); completion is
+// tracked with explicit vmcnt waits (loads complete in issue order).
+__device__ __forceinline__ void lds_dma16(const void* g, void* lds_uniform) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds_uniform))));
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(g), "s"(m0)
+      : "memory");
+}
+
 }  // namespace moe

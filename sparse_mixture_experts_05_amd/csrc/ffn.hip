@@ -425,35 +425,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
 // lane that fills slot p of row r loads chunk p ^ (r & 7), and fragment
 // reads (32 consecutive rows, one chunk column) hit distinct banks.
 
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-// Workgroup barrier for LDS hand-off only. __syncthreads() carries a release
-// fence that waits for every outstanding global load (vmcnt 0), which would
-// drain the next stage's prefetch; the staged loads are waited for explicitly.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
-// global_load_lds_dwordx4: lane i copies 16 bytes from its address g into
-// LDS at M0 + 16*i (M0 = the wave-uniform LDS address). Issued through asm so
-// the compiler's wait insertion does not treat every later LDS read as
-// aliasing the in-flight copy (which would drain the prefetch); completion is
-// tracked with explicit vmcnt waits (loads complete in issue order).
-__device__ __forceinline__ void lds_dma16(const void* g, void* lds_uniform) {
-  const uint32_t m0 = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(
-      reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) uint8_t*)(lds_uniform))));
-  asm volatile(
-      "s_mov_b32 m0, %1\n\t"
-      "global_load_lds_dwordx4 %0, off"
-      :
-      : "v"(g), "s"(m0)
-      : "memory");
-}
-
 // Large-tile kernel: BM x BN tile, NW waves in a 2 x (NW/2) grid, each wave a
 // (BM/2) x (BN/(NW/2)) block of 32x32x16 MFMAs. Two LDS stages of BK = 64.
 // Fragment registers are double buffered across the four 16-deep k slices of

@@ -11,9 +11,8 @@
 //
 // Layout of the work: one workgroup of 256 threads owns BT tokens.
 //   phase 1: scores [BT x E] into LDS. bf16: MFMA 16x16x32 tiles (tokens x
-//            experts, K = H), fp32 accumulation, operands straight from
-//            global memory (x rows are shared by the 4 waves through L1,
-//            Wg comes from L2). fp32: plain dot products.
+//            experts, K = H), fp32 accumulation, operands staged in LDS by
+//            coalesced global -> LDS copies. fp32: plain dot products.
 //   phase 2: one wavefront per token; every lane holds up to 4 scores
 //            (E <= 256); k rounds of a wave-wide arg-max done in registers
 //            with DPP (quad_perm, row mirrors) and ds_swizzle, lanes 0/32
@@ -26,165 +25,202 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kMaxE = 256;
-constexpr int kLogitStride = kMaxE + 4;  // LDS row stride (floats) of the score tile
 
-__device__ __forceinline__ void take_better(float& v, int& i, float ov, int oi) {
-  if (ov > v || (ov == v && oi < i)) {
-    v = ov;
-    i = oi;
-  }
+// Row stride (floats) of a score tile of BT tokens. The top-k gives each
+// token G = 256/BT consecutive lanes; lane g of a token reads the columns
+// g, g + G, ..., so a stride of G (mod 64) puts the 64 lanes of a wave on 64
+// distinct banks.
+template <int BT>
+constexpr int tile_stride() { return kMaxE + kThreads / BT; }
+
+// ---------------------------------------------------------------- top-k
+// Every (score, expert) pair is one 64-bit key: the score's bits mapped to an
+// order-preserving unsigned integer in the high half, the complement of the
+// expert id in the low half. A larger key is a better entry: a higher score,
+// or an equal score with a lower id. A NaN score reads as -inf and -0 as +0
+// (they compare equal). Key 0 is below every real entry and marks an empty
+// slot, so the k chosen ids are always real, distinct and < E.
+__device__ __forceinline__ uint64_t topk_key(float s, int e) {
+  const uint32_t u = s == s ? (s == 0.0f ? 0u : __float_as_uint(s)) : __float_as_uint(-INFINITY);
+  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(~(uint32_t)e);
+}
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t o = (uint32_t)(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+__device__ __forceinline__ int key_expert(uint64_t key) { return (int)(~(uint32_t)key); }
+
+__device__ __forceinline__ void cswap(uint64_t& a, uint64_t& b) {  // a <- max, b <- min
+  const bool gt = a > b;
+  const uint64_t hi = gt ? a : b, lo = gt ? b : a;
+  a = hi;
+  b = lo;
 }
 
-template <int CTRL>
-__device__ __forceinline__ void dpp_step(float& v, int& i) {
-  const float ov = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-  const int oi = __builtin_amdgcn_update_dpp(0, i, CTRL, 0xF, 0xF, false);
-  take_better(v, i, ov, oi);
-}
-
-// All 64 lanes end with the wave's best (v, i).
-__device__ __forceinline__ void wave_argmax(float& v, int& i) {
-  dpp_step<0xB1>(v, i);   // quad_perm [1,0,3,2]: lane ^ 1
-  dpp_step<0x4E>(v, i);   // quad_perm [2,3,0,1]: lane ^ 2
-  dpp_step<0x141>(v, i);  // row_half_mirror: pairs the two quads of each 8
-  dpp_step<0x140>(v, i);  // row_mirror: pairs the two 8-lane halves of each row
-  {                       // ds_swizzle bit-mask mode, xor 16: pairs the rows of each 32
-    const float ov = __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-    const int oi = __builtin_amdgcn_ds_swizzle(i, 0x401F);
-    take_better(v, i, ov, oi);
-  }
-  const float v0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
-  const int i0 = __builtin_amdgcn_readlane(i, 0);
-  const float v1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-  const int i1 = __builtin_amdgcn_readlane(i, 32);
-  v = v0;
-  i = i0;
-  take_better(v, i, v1, i1);
-}
-
-// Sum over the 64 lanes with the same exchange pattern as wave_argmax. Each
-// step adds a lane's value and its partner's, and fp addition is commutative,
-// so every lane ends with the same bits.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0)) +
-         __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
-}
-
-// Best live slot of this lane. Slots that are out of range or already taken
-// are dead and never win (a NaN score is read as -inf, so every live slot
-// beats every dead one and the k ids are always distinct and < E).
-__device__ __forceinline__ void lane_best(const float (&v)[4], unsigned alive, int lane, float& bv,
-                                          int& bi) {
-  bv = -INFINITY;
-  bi = 0x7fffffff;
+// Sorts a bitonic sequence of N keys into descending order (half-cleaners).
+template <int N>
+__device__ __forceinline__ void bitonic_clean(uint64_t (&c)[N]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q)
-    if (alive & (1u << q)) {
-      const int i = lane + 64 * q;
-      if (v[q] > bv || bi == 0x7fffffff) {
-        bv = v[q];
-        bi = i;
-      }
-    }
+  for (int st = N / 2; st > 0; st >>= 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i)
+      if ((i & st) == 0) cswap(c[i], c[i + st]);
 }
 
-// Phase 2: scores of BT tokens are in LDS (row-major, kLogitStride).
-// When pp is not null, the full softmax p[t, e] = exp(s_e - m) / sum_e' exp(s_e' - m)
-// of every token is also summed over the workgroup's tokens (per wave in
-// token order, then the 4 waves in order) and pp[e] receives the sum. The
-// score tile is reused for that reduction, so sc is clobbered.
-__device__ __forceinline__ void topk_phase(float* sc, int BT, int t0, int T, int E, int k,
-                                           const float* __restrict__ bias,
-                                           int32_t* __restrict__ topk_idx,
-                                           float* __restrict__ topk_w, float* __restrict__ pp) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  float b[4];
+// Sorts N keys into descending order (bitonic sorting network).
+template <int N>
+__device__ __forceinline__ void bitonic_sort(uint64_t (&c)[N]) {
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int e = lane + 64 * q;
-    b[q] = (bias != nullptr && e < E) ? bias[e] : 0.0f;
-  }
-  float pacc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int t = wave; t < BT; t += kThreads / kWave) {
-    const int tok = t0 + t;
-    if (tok >= T) break;
-    float v[4];
-    unsigned alive = 0;
+  for (int size = 2; size <= N; size <<= 1)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      const float s = e < E ? sc[t * kLogitStride + e] + b[q] : -INFINITY;
-      v[q] = s == s ? s : -INFINITY;
-      if (e < E) alive |= 1u << q;
-    }
-    float bv;
-    int bi;
-    lane_best(v, alive, lane, bv, bi);
-    float sv[8];
-    int si[8];
+    for (int st = size / 2; st > 0; st >>= 1)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        float wv = bv;
-        int wi = bi;
-        wave_argmax(wv, wi);
-        sv[j] = wv;
-        si[j] = wi;
-        if ((wi & 63) == lane) {
-          alive &= ~(1u << (wi >> 6));
-          lane_best(v, alive, lane, bv, bi);
+      for (int i = 0; i < N; ++i)
+        if ((i & st) == 0) {
+          if ((i & size) == 0) cswap(c[i], c[i + st]);
+          else cswap(c[i + st], c[i]);
         }
-      }
+}
+
+// list <- the N largest of list and blk (both sorted descending): the
+// elementwise max of list and reversed blk is bitonic and holds them.
+template <int N>
+__device__ __forceinline__ void merge_top(uint64_t (&list)[N], const uint64_t (&blk)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) list[i] = list[i] > blk[N - 1 - i] ? list[i] : blk[N - 1 - i];
+  bitonic_clean<N>(list);
+}
+
+// Value of the partner lane of butterfly level L: xor 1, xor 2, the mirror
+// lane within 8, within 16 (DPP), xor 16 (ds_swizzle), xor 32 (bpermute).
+// Each level pairs two groups that the earlier levels already merged.
+template <int L>
+__device__ __forceinline__ uint32_t partner(uint32_t v) {
+  if constexpr (L == 0) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  if constexpr (L == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  if constexpr (L == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+  if constexpr (L == 3) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+  if constexpr (L == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  if constexpr (L == 5)
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ 32) * 4), (int)v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ uint64_t partner64(uint64_t v) {
+  return ((uint64_t)partner<L>((uint32_t)(v >> 32)) << 32) | partner<L>((uint32_t)v);
+}
+
+// Merge the lists of the G lanes of a token, levels 0 .. log2(G)-1; every
+// lane ends with the same list.
+template <int L, int G, int N>
+__device__ __forceinline__ void group_merge(uint64_t (&list)[N]) {
+  if constexpr ((1 << L) < G) {
+    uint64_t other[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) other[i] = partner64<L>(list[i]);
+    merge_top<N>(list, other);
+    group_merge<L + 1, G, N>(list);
+  }
+}
+
+// Sum over the G lanes of a token: each level adds a lane's value and its
+// partner's, and fp addition is commutative, so every lane gets the same bits.
+template <int L, int G>
+__device__ __forceinline__ float group_sum(float v) {
+  if constexpr ((1 << L) < G) return group_sum<L + 1, G>(v + __uint_as_float(partner<L>(__float_as_uint(v))));
+  return v;
+}
+
+// Top-k of the BT tokens whose scores (bias included) are in the LDS tile sc
+// (row stride tile_stride<BT>()). Token t of the tile uses lanes
+// [t*G, t*G + G); lane g scans the experts g, g + G, ... in blocks of KP,
+// sorts each block and merges it into its running list, then the G lists are
+// merged. KP >= k is a power of two.
+// When pp is not null, the full softmax p[t, e] = exp(s_e - m) / sum_e' exp(s_e' - m)
+// of every token overwrites its scores, and pp[e] receives the sum of p[t, e]
+// over the tile's tokens (t ascending).
+template <int BT, int KP>
+__device__ __forceinline__ void topk_tokens(float* sc, int t0, int T, int E, int k,
+                                            int32_t* __restrict__ topk_idx,
+                                            float* __restrict__ topk_w, float* __restrict__ pp) {
+  constexpr int G = kThreads / BT;
+  constexpr int S = tile_stride<BT>();
+  static_assert(G >= 1 && G <= 64 && BT * G == kThreads, "one group of lanes per token");
+  const int t = threadIdx.x / G, g = threadIdx.x % G;
+  const int tok = t0 + t;
+  float* row = sc + t * S;
+  const int nsub = (E + G - 1) / G;  // experts per lane
+
+  uint64_t list[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) list[i] = 0;
+  for (int i0 = 0; i0 < nsub; i0 += KP) {
+    uint64_t blk[KP];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+      const int e = g + G * (i0 + i);
+      blk[i] = (i0 + i < nsub && e < E) ? topk_key(row[e], e) : 0;
     }
-    const float m = sv[0];
-    if (pp != nullptr) {
-      // dead slots hold -inf and give 0; a token whose scores are all -inf or
-      // NaN has no distribution and adds nothing
-      float z[4], zs = 0.0f;
+    bitonic_sort<KP>(blk);
+    merge_top<KP>(list, blk);
+  }
+  group_merge<0, G, KP>(list);
+
+  // weights: exp(s_j - m) / sum over the k chosen, m = the best score
+  const float m = key_score(list[0]);
+  float ex[KP], sum = 0.0f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        z[q] = m > -INFINITY ? expf(v[q] - m) : 0.0f;
-        zs += z[q];
-      }
-      const float Z = wave_sum(zs);
-      if (Z > 0.0f) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) pacc[q] += z[q] / Z;
-      }
+  for (int j = 0; j < KP; ++j)
+    if (j < k) {
+      ex[j] = expf(key_score(list[j]) - m);
+      sum += ex[j];
     }
-    float ex[8];
-    float sum = 0.0f;
+  if (tok < T) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k) {
-        ex[j] = expf(sv[j] - m);
-        sum += ex[j];
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j < k && lane == j) {
-        topk_idx[(size_t)tok * k + j] = si[j];
+    for (int j = 0; j < KP; ++j)
+      if (j < k && j % G == g) {
+        topk_idx[(size_t)tok * k + j] = key_expert(list[j]);
         topk_w[(size_t)tok * k + j] = ex[j] / sum;
       }
-    }
   }
+
   if (pp != nullptr) {
-    __syncthreads();  // every wave is done with the score tile
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int e = lane + 64 * q;
-      if (e < E) sc[wave * kMaxE + e] = pacc[q];
+    // dead or NaN scores give 0; a token whose scores are all -inf or NaN has
+    // no distribution and adds nothing
+    float zs = 0.0f;
+    for (int i = 0; i < nsub; ++i) {
+      const int e = g + G * i;
+      if (e < E) {
+        const float v = row[e];
+        const float z = (m > -INFINITY && v == v) ? expf(v - m) : 0.0f;
+        row[e] = z;
+        zs += z;
+      }
+    }
+    const float Z = group_sum<0, G>(zs);
+    for (int i = 0; i < nsub; ++i) {
+      const int e = g + G * i;
+      if (e < E) row[e] = Z > 0.0f ? row[e] / Z : 0.0f;
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += kThreads)
-      pp[e] = ((sc[e] + sc[kMaxE + e]) + sc[2 * kMaxE + e]) + sc[3 * kMaxE + e];
+    const int nt = min(BT, T - t0);
+    for (int e = threadIdx.x; e < E; e += kThreads) {
+      float a = 0.0f;
+      for (int q = 0; q < nt; ++q) a += sc[q * S + e];
+      pp[e] = a;
+    }
   }
+}
+
+template <int BT>
+__device__ __forceinline__ void topk_phase(float* sc, int t0, int T, int E, int k,
+                                           int32_t* __restrict__ topk_idx,
+                                           float* __restrict__ topk_w, float* __restrict__ pp) {
+  if (k <= 1) topk_tokens<BT, 1>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else if (k <= 2) topk_tokens<BT, 2>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else if (k <= 4) topk_tokens<BT, 4>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else topk_tokens<BT, 8>(sc, t0, T, E, k, topk_idx, topk_w, pp);
 }
 
 // P[e] = (sum over workgroups b, ascending, of part[b][e]) / T, in double.
@@ -198,123 +234,182 @@ __global__ __launch_bounds__(kThreads) void prob_mean_kernel(const float* __rest
   }
 }
 
-// K loop of the score tiles: a ring of D register buffers keeps the operand
-// loads of the next D-1 k-steps in flight while one step runs on the matrix
-// cores (the loop is unrolled by D so every ring index is static).
-template <int MC, int NCW, int D>
-__device__ __forceinline__ void mfma_ring(const uint16_t* const (&arow)[MC],
-                                          const uint16_t* const (&brow)[NCW], int s0, int nsteps,
-                                          int stride, f32x4_t (&acc)[MC][NCW]) {
-  u32x4_t ra[D][MC], rb[D][NCW];
+// bf16 scores on MFMA 16x16x32 with operands staged in LDS. One workgroup
+// (4 waves) computes a BT x EP tile of scores: BT tokens and EP experts
+// starting at expert e0, over the K panels [kp0, kp1) of 64 elements.
+// A panel holds the BT token rows, then the EP expert rows (R rows in all, a
+// multiple of 32; rows past the data repeat a valid row and are never used),
+// 128 bytes each. Rows are copied global -> LDS with global_load_lds: one
+// instruction moves 8 rows, 8 consecutive lanes reading one whole 128-byte
+// line. NS stages of PPS panels rotate through LDS, so two stages are in
+// flight while one is multiplied. Chunk c (16 bytes) of LDS row r sits at
+// slot c ^ ((r >> 1) & 7): a 128-bit read by 16 lanes (16 consecutive rows,
+// one chunk) then touches 16 distinct 4-bank groups.
+// Work split: EP >= 64, wave w computes experts [w*EP/4, (w+1)*EP/4) over all
+// panels; EP < 64, wave w takes the panels p = w (mod 4) of every stage for
+// the whole tile and the 4 partial tiles are summed in a fixed order.
+template <int BT, int EP>
+struct RouteTile {
+  static constexpr int R = (BT + EP + 31) / 32 * 32;  // rows per panel
+  static constexpr int PB = R * 128;                  // panel bytes
+  static constexpr bool KSPLIT = EP < 64;
+  static constexpr int PPS_RAW = (40 * 1024) / PB < 1 ? 1 : (40 * 1024) / PB;
+  // panels per stage: a multiple of 4 when the waves split them, else <= 2
+  static constexpr int PPS = KSPLIT ? (PPS_RAW >= 8 ? 8 : 4) : (PPS_RAW > 2 ? 2 : PPS_RAW);
+  static constexpr int SB = PPS * PB;                 // stage bytes
+  static constexpr int NS = 3;                        // stages
+  static constexpr int NI = PPS * R / 32;             // DMA instructions per wave per stage
+  static constexpr int MC = BT / 16;                  // 16-row tiles per wave
+  static constexpr int NC = KSPLIT ? EP / 16 : EP / 64;  // 16-column tiles per wave
+  static constexpr int SC_BYTES = BT * tile_stride<BT>() * 4;
+  static constexpr int PART_BYTES = KSPLIT ? 4 * BT * EP * 4 : 0;
+  static constexpr int LDS = NS * SB > SC_BYTES + PART_BYTES ? NS * SB : SC_BYTES + PART_BYTES;
+  static_assert(PPS * R % 32 == 0, "whole DMA instructions per wave");
+  static_assert(NI < 32, "vmcnt range");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// The K loop of one tile; returns with every wave's accumulators complete and
+// the LDS free for reuse (after a barrier).
+template <int BT, int EP>
+__device__ __forceinline__ void score_tile(uint8_t* smem, const uint16_t* __restrict__ x,
+                                           const uint16_t* __restrict__ wg, int t0, int T, int e0,
+                                           int E, int H, int kp0, int kp1,
+                                           f32x4_t (&acc)[RouteTile<BT, EP>::MC][RouteTile<BT, EP>::NC]) {
+  using C = RouteTile<BT, EP>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int NST = (kp1 - kp0 + C::PPS - 1) / C::PPS;  // stages
+
+  // DMA plan of this lane: instruction q copies rows [8g, 8g+8) of panel pq[q].
+  const uint16_t* src[C::NI];
+  int pq[C::NI], dst[C::NI];
 #pragma unroll
-  for (int u = 0; u < D; ++u) {
-    const int s = s0 + u * stride;
-    if (s < nsteps) {
-#pragma unroll
-      for (int r = 0; r < MC; ++r) ra[u][r] = ld16(arow[r] + s * 32);
-#pragma unroll
-      for (int c = 0; c < NCW; ++c) rb[u][c] = ld16(brow[c] + s * 32);
-    }
+  for (int q = 0; q < C::NI; ++q) {
+    const int j = wave * C::NI + q;
+    const int p = j / (C::R / 8), g = j % (C::R / 8);
+    const int r = 8 * g + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    const uint16_t* row = r < BT ? x + (size_t)min(t0 + r, T - 1) * H
+                                 : wg + (size_t)min(e0 + r - BT, E - 1) * H;
+    src[q] = row + chunk * 8;
+    pq[q] = p;
+    dst[q] = p * C::PB + g * 1024;
   }
-  for (int base = s0; base < nsteps; base += D * stride) {
+  auto issue = [&](int st) {
+    uint8_t* base = smem + (st % C::NS) * C::SB;
 #pragma unroll
-    for (int u = 0; u < D; ++u) {
-      const int s = base + u * stride;
-      if (s < nsteps) {
+    for (int q = 0; q < C::NI; ++q)
+      lds_dma16(src[q] + (size_t)min(kp0 + st * C::PPS + pq[q], kp1 - 1) * 64, base + dst[q]);
+  };
+
 #pragma unroll
-        for (int r = 0; r < MC; ++r)
+  for (int m = 0; m < C::MC; ++m)
 #pragma unroll
-          for (int c = 0; c < NCW; ++c)
-            acc[r][c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ra[u][r]),
-                                                                as_bf16x8(rb[u][c]), acc[r][c], 0, 0, 0);
-        const int sn = s + D * stride;
-        if (sn < nsteps) {
+    for (int n = 0; n < C::NC; ++n) acc[m][n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // fragment of a 16-row tile: row lane%16, chunk ks*4 + lane/16 (a 32-deep k step)
+  const int fr = (lane & 15) * 128;
+  const int sw = (lane >> 1) & 7;
+  const int c0 = C::KSPLIT ? 0 : wave * (EP / 4);
+
 #pragma unroll
-          for (int r = 0; r < MC; ++r) ra[u][r] = ld16(arow[r] + sn * 32);
+  for (int st = 0; st < C::NS - 1; ++st)
+    if (st < NST) issue(st);
+  for (int st = 0; st < NST; ++st) {
+    if (st + C::NS - 2 < NST) wait_vmcnt<(C::NS - 2) * C::NI>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // stage st landed for every wave; stage st-1 is no longer read
+    if (st + C::NS - 1 < NST) issue(st + C::NS - 1);
+    const uint8_t* base = smem + (st % C::NS) * C::SB;
 #pragma unroll
-          for (int c = 0; c < NCW; ++c) rb[u][c] = ld16(brow[c] + sn * 32);
-        }
+    for (int p = 0; p < C::PPS; ++p) {
+      if (C::KSPLIT && (p & 3) != wave) continue;
+      if (kp0 + st * C::PPS + p >= kp1) continue;
+      const uint8_t* pan = base + p * C::PB;
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        const int slot = ((ks * 4 + (lane >> 4)) ^ sw) * 16;
+        u32x4_t a[C::MC], b[C::NC];
+#pragma unroll
+        for (int m = 0; m < C::MC; ++m)
+          a[m] = *reinterpret_cast<const u32x4_t*>(pan + m * 16 * 128 + fr + slot);
+#pragma unroll
+        for (int n = 0; n < C::NC; ++n)
+          b[n] = *reinterpret_cast<const u32x4_t*>(pan + (BT + c0 + n * 16) * 128 + fr + slot);
+#pragma unroll
+        for (int m = 0; m < C::MC; ++m)
+#pragma unroll
+          for (int n = 0; n < C::NC; ++n)
+            acc[m][n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a[m]), as_bf16x8(b[n]),
+                                                                acc[m][n], 0, 0, 0);
       }
     }
   }
+  __syncthreads();  // every wave is done with the stages
 }
 
-// bf16 scores with MFMA. MC: 16-token row chunks per workgroup; NCW: 16-expert
-// column chunks per wave; KSPLIT: 1 = each wave owns NCW column chunks over
-// all of H, 4 = the 4 waves split the K steps (interleaved) and the partial
-// tiles are summed in a fixed order.
-template <int MC, int NCW, int KSPLIT>
+// Scores of the tile plus the bias into LDS (row-major, tile_stride<BT>()),
+// columns < ncol. D layout of 16x16: lane holds column lane%16, rows
+// (lane/16)*4 + v.
+template <int BT, int EP>
+__device__ __forceinline__ void scores_to_lds(uint8_t* smem, int ncol, const float* __restrict__ bias,
+                                              const f32x4_t (&acc)[RouteTile<BT, EP>::MC][RouteTile<BT, EP>::NC]) {
+  using C = RouteTile<BT, EP>;
+  constexpr int S = tile_stride<BT>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  float* sc = reinterpret_cast<float*>(smem);
+  if (!C::KSPLIT) {
+    const int c0 = wave * (EP / 4);
+#pragma unroll
+    for (int m = 0; m < C::MC; ++m)
+#pragma unroll
+      for (int n = 0; n < C::NC; ++n) {
+        const int col = c0 + n * 16 + (lane & 15);
+        const float b = (bias != nullptr && col < ncol) ? bias[col] : 0.0f;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = m * 16 + (lane >> 4) * 4 + v;
+          if (col < ncol) sc[row * S + col] = bias != nullptr ? acc[m][n][v] + b : acc[m][n][v];
+        }
+      }
+  } else {
+    float* part = reinterpret_cast<float*>(smem + C::SC_BYTES);
+#pragma unroll
+    for (int m = 0; m < C::MC; ++m)
+#pragma unroll
+      for (int n = 0; n < C::NC; ++n)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int row = m * 16 + (lane >> 4) * 4 + v;
+          part[(wave * BT + row) * EP + n * 16 + (lane & 15)] = acc[m][n][v];
+        }
+    __syncthreads();
+    for (int q = threadIdx.x; q < BT * ncol; q += kThreads) {
+      const int row = q / ncol, col = q % ncol;
+      float v = part[(0 * BT + row) * EP + col];
+      v += part[(1 * BT + row) * EP + col];
+      v += part[(2 * BT + row) * EP + col];
+      v += part[(3 * BT + row) * EP + col];
+      sc[row * S + col] = bias != nullptr ? v + bias[col] : v;
+    }
+  }
+  __syncthreads();
+}
+
+// One launch: BT tokens x all E experts (EP >= E) over all of H, then top-k.
+template <int BT, int EP>
 __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const float* __restrict__ bias, int T, int H, int E, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ ppart) {
-  constexpr int BT = MC * 16;
-  static_assert(BT * kLogitStride >= 4 * kMaxE, "score tile too small for the probability sums");
-  __shared__ float sc[BT * kLogitStride];
-  __shared__ float part[KSPLIT == 4 ? 4 * BT * 48 : 1];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  using C = RouteTile<BT, EP>;
+  __shared__ __align__(16) uint8_t smem[C::LDS];
   const int t0 = blockIdx.x * BT;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int c0 = KSPLIT == 4 ? 0 : wave * NCW * 16;  // first expert column of this wave
-
-  const uint16_t* arow[MC];
-#pragma unroll
-  for (int r = 0; r < MC; ++r) arow[r] = x + (size_t)min(t0 + r * 16 + r16, T - 1) * H + kq;
-  const uint16_t* brow[NCW];
-#pragma unroll
-  for (int c = 0; c < NCW; ++c) brow[c] = wg + (size_t)min(c0 + c * 16 + r16, E - 1) * H + kq;
-
-  f32x4_t acc[MC][NCW];
-#pragma unroll
-  for (int r = 0; r < MC; ++r)
-#pragma unroll
-    for (int c = 0; c < NCW; ++c) acc[r][c] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const bool active = KSPLIT == 4 || c0 < E;
-  if (active) {
-    const int nsteps = H / 32;
-    const int s0 = KSPLIT == 4 ? wave : 0;
-    mfma_ring<MC, NCW, (MC + NCW <= 4 ? 8 : 4)>(arow, brow, s0, nsteps, KSPLIT, acc);
-  }
-  // D layout of 16x16: lane holds column lane%16, rows (lane/16)*4 + v.
-  if (KSPLIT == 1) {
-    if (active) {
-#pragma unroll
-      for (int r = 0; r < MC; ++r)
-#pragma unroll
-        for (int c = 0; c < NCW; ++c) {
-          const int col = c0 + c * 16 + r16;
-#pragma unroll
-          for (int v = 0; v < 4; ++v) {
-            const int row = r * 16 + (lane >> 4) * 4 + v;
-            if (col < E) sc[row * kLogitStride + col] = acc[r][c][v];
-          }
-        }
-    }
-    __syncthreads();
-  } else {
-#pragma unroll
-    for (int r = 0; r < MC; ++r)
-#pragma unroll
-      for (int c = 0; c < NCW; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const int row = r * 16 + (lane >> 4) * 4 + v;
-          part[(wave * BT + row) * 48 + c * 16 + r16] = acc[r][c][v];
-        }
-    __syncthreads();
-    for (int p = threadIdx.x; p < BT * E; p += kThreads) {
-      const int row = p / E, col = p % E;
-      float s = part[(0 * BT + row) * 48 + col];
-      s += part[(1 * BT + row) * 48 + col];
-      s += part[(2 * BT + row) * 48 + col];
-      s += part[(3 * BT + row) * 48 + col];
-      sc[row * kLogitStride + col] = s;
-    }
-    __syncthreads();
-  }
-  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w,
-             ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+  f32x4_t acc[C::MC][C::NC];
+  score_tile<BT, EP>(smem, x, wg, t0, T, 0, E, H, 0, H / 64, acc);
+  scores_to_lds<BT, EP>(smem, E, bias, acc);
+  topk_phase<BT>(reinterpret_cast<float*>(smem), t0, T, E, k, topk_idx, topk_w,
+                 ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 // fp32 scores with plain dot products (small fp32 layers).
@@ -323,7 +418,8 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     int T, int H, int E, int k, int32_t* __restrict__ topk_idx, float* __restrict__ topk_w,
     float* __restrict__ ppart) {
   constexpr int BT = 16;
-  __shared__ float sc[BT * kLogitStride];
+  constexpr int S = tile_stride<BT>();
+  __shared__ float sc[BT * S];
   const int t0 = blockIdx.x * BT;
   for (int p = threadIdx.x; p < BT * E; p += kThreads) {
     const int t = p / E, e = p % E;
@@ -337,32 +433,33 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
       s = fmaf(a.z, b.z, s);
       s = fmaf(a.w, b.w, s);
     }
-    sc[t * kLogitStride + e] = s;
+    sc[t * S + e] = bias != nullptr ? s + bias[e] : s;
   }
   __syncthreads();
-  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w,
-             ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+  topk_phase<BT>(sc, t0, T, E, k, topk_idx, topk_w,
+                 ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 
-// Few tokens (decode-like): one workgroup per 16 tokens cannot stream Wg fast
-// enough, so the scores are computed in two launches. Phase 1: one wavefront
-// per (16 tokens, 16 experts, K slice) writes a partial score tile into the
-// workspace ws[ks][t][e]. Phase 2: one wavefront per token sums its K slices
-// in a fixed order (ks ascending), adds the bias and runs the top-k.
-__global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __restrict__ x,
-                                                           const uint16_t* __restrict__ wg,
-                                                           int T, int H, int E, int ksteps,
-                                                           float* __restrict__ ws) {
-  const int lane = threadIdx.x;
-  const int t0 = blockIdx.x * 16, e0 = blockIdx.y * 16, ks = blockIdx.z;
-  const int r16 = lane & 15, kq = (lane >> 4) * 8;
-  const int s0 = ks * ksteps;
-  const uint16_t* const arow[1] = {x + (size_t)min(t0 + r16, T - 1) * H + kq + s0 * 32};
-  const uint16_t* const brow[1] = {wg + (size_t)min(e0 + r16, E - 1) * H + kq + s0 * 32};
-  f32x4_t acc[1][1] = {{f32x4_t{0.f, 0.f, 0.f, 0.f}}};
-  mfma_ring<1, 1, 8>(arow, brow, 0, ksteps, 1, acc);
-  const int e = e0 + r16;
+// Few tokens (bf16, T < 2048): one workgroup per 16 tokens would stream all
+// of Wg through a single CU, so the scores are computed in two launches.
+// Phase 1: workgroup (token block, 64-expert block, K slice) computes its
+// partial score tile and stores it in the workspace ws[ks][t][e]. Phase 2:
+// one wavefront per token sums its K slices in a fixed order (ks ascending),
+// adds the bias and runs the top-k.
+constexpr int kPartBT = 16, kPartEP = 64, kMaxSlices = 16;
+
+__global__ __launch_bounds__(kThreads) void route_partial_kernel(const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ wg,
+                                                                 int T, int H, int E, int kps,
+                                                                 float* __restrict__ ws) {
+  using C = RouteTile<kPartBT, kPartEP>;
+  __shared__ __align__(16) uint8_t smem[C::NS * C::SB];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t0 = blockIdx.x * kPartBT, e0 = blockIdx.y * kPartEP, ks = blockIdx.z;
+  f32x4_t acc[C::MC][C::NC];
+  score_tile<kPartBT, kPartEP>(smem, x, wg, t0, T, e0, E, H, ks * kps, (ks + 1) * kps, acc);
+  const int e = e0 + wave * (kPartEP / 4) + (lane & 15);
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
     const int t = t0 + (lane >> 4) * 4 + v;
@@ -370,6 +467,7 @@ __global__ __launch_bounds__(64) void route_partial_kernel(const uint16_t* __res
   }
 }
 
+template <int NKS>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __restrict__ ws,
                                                                 const float* __restrict__ bias,
                                                                 int T, int E, int k, int nks,
@@ -377,59 +475,57 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __r
                                                                 float* __restrict__ topk_w,
                                                                 float* __restrict__ ppart) {
   constexpr int BT = kThreads / kWave;  // 4 tokens per workgroup
-  __shared__ float sc[BT * kLogitStride];
+  constexpr int S = tile_stride<BT>();
+  __shared__ float sc[BT * S];
   const int t0 = blockIdx.x * BT;
   for (int p = threadIdx.x; p < BT * E; p += kThreads) {
     const int t = p / E, e = p % E;
     if (t0 + t < T) {
+      float v[NKS];
+#pragma unroll
+      for (int q = 0; q < NKS; ++q)  // all loads first, then the sum in slice order
+        v[q] = q < nks ? ws[((size_t)q * T + t0 + t) * E + e] : 0.0f;
       float s = 0.0f;
-      for (int q = 0; q < nks; ++q) s += ws[((size_t)q * T + t0 + t) * E + e];
-      sc[t * kLogitStride + e] = s;
+#pragma unroll
+      for (int q = 0; q < NKS; ++q)
+        if (q < nks) s += v[q];
+      sc[t * S + e] = bias != nullptr ? s + bias[e] : s;
     }
   }
   __syncthreads();
-  topk_phase(sc, BT, t0, T, E, k, bias, topk_idx, topk_w,
-             ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+  topk_phase<BT>(sc, t0, T, E, k, topk_idx, topk_w,
+                 ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
-// K slices for the two-phase path: enough wavefronts to spread the Wg read
-// over the chip (about 1024), a power of two that divides H/32.
+// K slices for the two-phase path: about 256 workgroups in phase 1, a power of
+// two (at most kMaxSlices) that divides the H/64 panels.
 int route_kslices(int T, int H, int E) {
-  const int tiles = ((T + 15) / 16) * ((E + 15) / 16);
+  const int tiles = ((T + kPartBT - 1) / kPartBT) * ((E + kPartEP - 1) / kPartEP);
   int ks = 1;
-  while (ks * 2 * tiles <= 1024 && (H / 32) % (ks * 2) == 0 && ks * 2 <= 64) ks *= 2;
+  while (ks * 2 * tiles <= 256 && (H / 64) % (ks * 2) == 0 && ks * 2 <= kMaxSlices) ks *= 2;
   return ks;
 }
 
 bool route_two_phase(int T, bool bf16) { return bf16 && T < 2048; }
 
-template <int MC, int NCW, int KSPLIT>
+template <int BT, int EP>
 hipError_t launch_bf16(const void* x, const void* wg, const float* bias, int T, int H, int E,
                        int k, int32_t* idx, float* w, float* pp, hipStream_t s) {
-  const int grid = (T + MC * 16 - 1) / (MC * 16);
-  hipLaunchKernelGGL((route_bf16_kernel<MC, NCW, KSPLIT>), dim3(grid), dim3(kThreads), 0, s,
+  const int grid = (T + BT - 1) / BT;
+  hipLaunchKernelGGL((route_bf16_kernel<BT, EP>), dim3(grid), dim3(kThreads), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, T,
                      H, E, k, idx, w, pp);
   return hipGetLastError();
 }
 
-template <int MC>
-hipError_t launch_bf16_mc(const void* x, const void* wg, const float* bias, int T, int H, int E,
+template <int BT>
+hipError_t launch_bf16_bt(const void* x, const void* wg, const float* bias, int T, int H, int E,
                           int k, int32_t* idx, float* w, float* pp, hipStream_t s) {
-  const int nc = (E + 15) / 16;
-  if (nc < 4) {
-    switch (nc) {
-      case 1: return launch_bf16<MC, 1, 4>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-      case 2: return launch_bf16<MC, 2, 4>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-      default: return launch_bf16<MC, 3, 4>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-    }
-  }
-  switch ((nc + 3) / 4) {
-    case 1: return launch_bf16<MC, 1, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-    case 2: return launch_bf16<MC, 2, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-    case 3: return launch_bf16<MC, 3, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-    default: return launch_bf16<MC, 4, 1>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-  }
+  if (E <= 16) return launch_bf16<BT, 16>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+  if (E <= 32) return launch_bf16<BT, 32>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+  if (E <= 64) return launch_bf16<BT, 64>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+  if (E <= 128) return launch_bf16<BT, 128>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+  return launch_bf16<BT, 256>(x, wg, bias, T, H, E, k, idx, w, pp, s);
 }
 
 // Tokens per workgroup of the one-launch bf16 path: as many as keep >= 256
@@ -468,13 +564,13 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
   hipError_t err = hipSuccess;
   if (route_two_phase(T, bf16)) {
     const int nks = route_kslices(T, H, E);
-    const dim3 grid((T + 15) / 16, (E + 15) / 16, nks);
-    hipLaunchKernelGGL(route_partial_kernel, grid, dim3(64), 0, s, static_cast<const uint16_t*>(x),
-                       static_cast<const uint16_t*>(wg), T, H, E, (H / 32) / nks,
-                       static_cast<float*>(ws));
+    const dim3 grid((T + kPartBT - 1) / kPartBT, (E + kPartEP - 1) / kPartEP, nks);
+    hipLaunchKernelGGL(route_partial_kernel, grid, dim3(kThreads), 0, s,
+                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, H, E,
+                       (H / 64) / nks, static_cast<float*>(ws));
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL(route_select_kernel, dim3((T + 3) / 4), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(route_select_kernel<kMaxSlices>, dim3((T + 3) / 4), dim3(kThreads), 0, s,
                        static_cast<const float*>(ws), bias, T, E, k, nks, topk_idx, topk_w, pp);
     err = hipGetLastError();
   } else if (!bf16) {
@@ -485,9 +581,9 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
     err = hipGetLastError();
   } else {
     switch (bf16_tokens_per_block(T)) {
-      case 64: err = launch_bf16_mc<4>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
-      case 32: err = launch_bf16_mc<2>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
-      default: err = launch_bf16_mc<1>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
+      case 64: err = launch_bf16_bt<64>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
+      case 32: err = launch_bf16_bt<32>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
+      default: err = launch_bf16_bt<16>(x, wg, bias, T, H, E, k, topk_idx, topk_w, pp, s); break;
     }
   }
   if (err != hipSuccess || prob_mean == nullptr) return err;

@@ -26,6 +26,8 @@ SMALL = [
     MoEConfig("ragged_n_bf16", T=1000, H=384, E=16, k=4, F=320, Fs=192, bias_amp=1.5),
     MoEConfig("mid_E256_skew", T=600, H=256, E=256, k=8, F=128, bias_amp=2.5),
     MoEConfig("route_mc2_T8200", T=8200, H=128, E=32, k=2, F=64, bias_amp=1.0),
+    MoEConfig("route_bt16_E64", T=2100, H=256, E=64, k=6, F=64, bias_amp=1.0),
+    MoEConfig("route_bt64_E12_H192", T=16400, H=192, E=12, k=3, F=64, bias_amp=1.0),
 ]
 
 FULL = ["mixtral_8x7b", "fine_grained_zipf", "heavy_skew",
