@@ -33,7 +33,9 @@ Readings where the pages are silent or garbled (each listed in the design doc):
   * top-k ids are in descending score order; ties go to the lower expert id;
   * GeLU is the erf form 0.5*a*(1+erf(a/sqrt(2)));
   * no Linear biases anywhere; weights use the [out, in] layout;
-  * capacity drops are counted, never applied to the output;
+  * capacity drops are counted by the statistics; the capacity-enforcing
+    dispatch keeps each expert's first cap assignments in token order and the
+    dropped ones add nothing (no renormalisation of the kept weights);
   * the shared expert has weight 1 and is added to every token;
   * the residual add that follows the combine is not part of the layer output;
   * the bias rule compares each expert's count with the mean count; the step
@@ -141,6 +143,45 @@ def dispatch(idx, x, E: int):
             inv.astype(np.int32), xs)
 
 
+def capacity(T: int, k: int, E: int, cf: float) -> int:
+    """int((T*k/E) * cf) in float64, in that order ([DIAG] section 3 listing)."""
+    return int(((T * k) / E) * cf)
+
+
+def dispatch_capped(idx, x, E: int, cap: int):
+    """Dispatch with the expert capacity enforced ([DIAG] section 3 counts the
+    assignments beyond an expert's capacity as dropped; section 5 describes
+    dropping them). Each expert keeps its first ``cap`` assignments in token
+    order (the stable order of dispatch()); later ones are dropped: they get
+    no buffer row and inv = -1. counts are the raw counts (before dropping);
+    offsets are those of the kept rows. Returns (counts, offsets, perm, inv, xs)
+    with perm and xs holding the kept rows only."""
+    idx = np.asarray(idx, dtype=np.int64)
+    T, k = idx.shape
+    flat = idx.reshape(-1)
+    counts = np.zeros(E, dtype=np.int64)
+    np.add.at(counts, flat, 1)
+    kept = np.minimum(counts, cap)
+    offsets = np.zeros(E + 1, dtype=np.int64)
+    for e in range(E):
+        offsets[e + 1] = offsets[e] + kept[e]
+    perm = np.empty(offsets[E], dtype=np.int64)
+    inv = np.full(T * k, -1, dtype=np.int64)
+    for e in range(E):
+        where = np.nonzero(flat == e)[0][:cap]     # the first cap, ascending assignment order
+        start = offsets[e]
+        perm[start:start + where.size] = where
+        inv[where] = np.arange(start, start + where.size)
+    xs = np.asarray(x)[perm // k]
+    return (counts.astype(np.int32), offsets.astype(np.int32), perm.astype(np.int32),
+            inv.astype(np.int32), xs)
+
+
+def kept_mask(inv) -> np.ndarray:
+    """True for assignments that kept a buffer row (inv >= 0)."""
+    return np.asarray(inv) >= 0
+
+
 # ---------------------------------------------------------------- step 3: experts
 
 def gelu_erf(a: np.ndarray) -> np.ndarray:
@@ -216,12 +257,18 @@ def layer(L: dict, k: int):
                 xs=xs, y=y, ysh=ysh, out=out)
 
 
-def layer_rows(L: dict, idx, w, tokens):
-    """Layer output for a sample of tokens, given their routing (idx, w)."""
+def layer_rows(L: dict, idx, w, tokens, keep=None):
+    """Layer output for a sample of tokens, given their routing (idx, w).
+
+    keep (optional bool [T, k]): assignments that were not dropped; a dropped
+    assignment adds nothing and the kept weights are not renormalised."""
     tokens = np.asarray(tokens)
     y = expert_outputs(L["x"], idx, L["w1"], L["w2"], tokens)
     ysh = shared_outputs(L["x"], L["ws1"], L["ws2"], tokens)
-    return combine(y, np.asarray(w)[tokens], ysh), y, ysh
+    wt = np.asarray(w, dtype=np.float64)[tokens]
+    if keep is not None:
+        wt = np.where(np.asarray(keep)[tokens], wt, 0.0)
+    return combine(y, wt, ysh), y, ysh
 
 
 # ---------------------------------------------------------------- step 5: load stats

@@ -363,6 +363,71 @@ def check_stats_strict_straggler_and_overflow():
     assert O.load_stats(c, 30, 2, 1.0)["straggler_ids"] == []
 
 
+# ------------------------------------------------------------------ capacity-enforced dispatch
+
+def check_dispatch_capped_hand_fixture():
+    cases = json.load(open(os.path.join(GOLDEN, "dispatch_capped_hand.json")))["cases"]
+    for c in cases:
+        if "cf" in c:
+            assert O.capacity(c["T"], c["k"], c["E"], c["cf"]) == c["cap"]
+        x = np.arange(c["T"], dtype=np.float64)[:, None] * np.ones((1, 3))
+        counts, offsets, perm, inv, xs = O.dispatch_capped(np.array(c["idx"]), x, c["E"], c["cap"])
+        assert counts.tolist() == c["counts"]
+        assert offsets.tolist() == c["offsets"]
+        assert perm.tolist() == c["perm"]
+        assert inv.tolist() == c["inv"]
+        assert xs[:, 0].astype(int).tolist() == c["xs_tokens"]
+
+
+def check_dispatch_capped_limits_and_prefix():
+    """cap >= max count: the plain dispatch; cap = 0: nothing kept; otherwise each
+    segment is the first cap rows of the plain segment, the dropped count is the
+    statistics' overflow sum, and the kept rows are min(c, cap) per expert."""
+    T, E, k = 97, 7, 3
+    idx = _random_topk(T, E, k, 31)
+    x = _rng(32).standard_normal((T, 5))
+    full = O.dispatch(idx, x, E)
+    big = O.dispatch_capped(idx, x, E, int(full[0].max()))
+    for a, b in zip(full, big):
+        assert np.array_equal(a, b)
+    c0 = O.dispatch_capped(idx, x, E, 0)
+    assert c0[1].tolist() == [0] * (E + 1) and c0[2].size == 0 and (c0[3] == -1).all()
+    for cap in [1, 5, 40, 41, 50]:
+        counts, offsets, perm, inv, xs = O.dispatch_capped(idx, x, E, cap)
+        assert np.array_equal(counts, full[0])
+        assert np.array_equal(np.diff(offsets), np.minimum(full[0], cap))
+        for e in range(E):
+            seg = perm[offsets[e]:offsets[e + 1]]
+            assert np.array_equal(seg, full[2][full[1][e]:full[1][e] + seg.size])
+        kept = inv >= 0
+        assert np.array_equal(perm[inv[kept]], np.nonzero(kept)[0])
+        cf = cap / (T * k / E)
+        st = O.load_stats(counts, T, k, cf)
+        if st["capacity"] == cap:
+            assert int((~kept).sum()) == st["dropped"]
+        assert np.array_equal(xs, x[perm // k])
+
+
+def check_layer_capped_drops_terms():
+    """A dropped assignment removes exactly its weighted expert output (no
+    renormalisation); dropping everything leaves the shared expert only."""
+    L = _small_layer(T=24, H=16, E=4, F=32, Fs=8)
+    k = 2
+    idx, w, _, _ = O.route(L["x"], L["wg"], L["bias"], k)
+    tokens = np.arange(24)
+    out_all, y, ysh = O.layer_rows(L, idx, w, tokens)
+    keep = np.ones((24, k), dtype=bool)
+    keep[3, 1] = False
+    keep[10, 0] = False
+    out_c, _, _ = O.layer_rows(L, idx, w, tokens, keep=keep)
+    want = out_all.copy()
+    want[3] -= float(w[3, 1]) * y[3, 1]
+    want[10] -= float(w[10, 0]) * y[10, 0]
+    np.testing.assert_allclose(out_c, want, rtol=0, atol=1e-12)
+    out_none, _, _ = O.layer_rows(L, idx, w, tokens, keep=np.zeros((24, k), dtype=bool))
+    np.testing.assert_allclose(out_none, ysh, rtol=0, atol=1e-15)
+
+
 # ------------------------------------------------------------------ dynamic bias, aux statistics
 
 def check_bias_update_closed_forms():

@@ -183,12 +183,50 @@ def m_prob_mean_first_token(mp):
     mp.setattr(O, "prob_mean", lambda p: np.asarray(p, dtype=np.float64)[0].copy())
 
 
+_dispatch_capped, _layer_rows = O.dispatch_capped, O.layer_rows
+
+
+def m_capped_keeps_last(mp):
+    """Keep the last cap assignments of each expert instead of the first."""
+    def dispatch_capped(idx, x, E, cap):
+        idx = np.asarray(idx)
+        T, k = idx.shape
+        rev = idx[::-1].copy()
+        counts, offsets, perm, inv, _ = _dispatch_capped(rev, x[::-1] if x is not None else x, E, cap)
+        a_rev = perm.astype(np.int64)
+        t = T - 1 - a_rev // k
+        perm2 = (t * k + a_rev % k).astype(np.int32)
+        for e in range(E):
+            a, b = offsets[e], offsets[e + 1]
+            perm2[a:b] = np.sort(perm2[a:b])
+        inv2 = np.full(T * k, -1, dtype=np.int32)
+        inv2[perm2] = np.arange(perm2.size)
+        return counts, offsets, perm2, inv2, np.asarray(x)[perm2 // k]
+    mp.setattr(O, "dispatch_capped", dispatch_capped)
+
+
+def m_capped_off_by_one(mp):
+    mp.setattr(O, "dispatch_capped", lambda idx, x, E, cap: _dispatch_capped(idx, x, E, cap + 1))
+
+
+def m_capped_renormalises(mp):
+    def layer_rows(L, idx, w, tokens, keep=None):
+        if keep is None:
+            return _layer_rows(L, idx, w, tokens)
+        wk = np.where(keep, np.asarray(w, dtype=np.float64), 0.0)
+        s = wk.sum(axis=1, keepdims=True)
+        wk = np.where(s > 0, wk / np.where(s > 0, s, 1.0), 0.0)
+        return _layer_rows(L, idx, wk, tokens, keep=keep)
+    mp.setattr(O, "layer_rows", layer_rows)
+
+
 MUTATIONS = [m_no_renormalise, m_select_smallest, m_bias_selection_only, m_ties_to_higher_id,
              m_unstable_dispatch, m_offsets_inclusive, m_gelu_tanh, m_gelu_dropped, m_gelu_sign,
              m_w2_layout_misread, m_w1_layout_misread, m_combine_drops_shared, m_combine_weights_swapped, m_capacity_ceil,
              m_gini_index_from_zero, m_straggler_ge, m_bias_update_sign_flipped,
              m_bias_update_mean_floor, m_bias_update_in_float64, m_load_fraction_per_token,
-             m_prob_mean_is_sum, m_prob_mean_first_token]
+             m_prob_mean_is_sum, m_prob_mean_first_token, m_capped_keeps_last,
+             m_capped_off_by_one, m_capped_renormalises]
 
 
 @pytest.mark.parametrize("mutate", MUTATIONS, ids=lambda f: f.__name__)
