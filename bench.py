@@ -28,6 +28,8 @@ import re
 import sys
 import time
 
+import numpy as np
+
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
@@ -41,23 +43,29 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_mixtral_8x7b_pmc.md")
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc", "ffn.hip")
 
 
-def algorithmic_work(cfg, counts=None):
+def algorithmic_work(cfg, counts=None, kept=None):
     """Bytes / flops each step must move or compute (per call).
 
     route:    x once + Wg + bias + ids/weights out
     dispatch: ids in, x once, xs out, perm + inv out, counts + offsets out
     ffn:      4*rows*H*F + 4*T*H*Fs flops (the up and down projections)
     combine:  ys in, inv + weights in, shared rows in, out
+    With capacity dropping, kept[e] is expert e's kept rows: rows = sum(kept)
+    (xs, the FFN and ys) and an expert is live if it kept a row.
     """
     T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
     b = 2 if cfg.dtype == "bf16" else 4
-    rows = T * k
-    route = T * H * b + E * H * b + (4 * E if cfg.bias_amp else 0) + 8 * rows
-    dispatch = 4 * rows + T * H * b + rows * H * b + 8 * rows + 4 * (2 * E + 1)
+    assign = T * k
+    rows = assign if kept is None else int(kept.sum())
+    route = T * H * b + E * H * b + (4 * E if cfg.bias_amp else 0) + 8 * assign
+    dispatch = 4 * assign + T * H * b + rows * H * b + 8 * assign + 4 * (2 * E + 1)
     ffn_flops = 4 * rows * H * F + 4 * T * H * Fs
-    live = E if counts is None else int((counts > 0).sum())
+    if kept is not None:
+        live = int((kept > 0).sum())
+    else:
+        live = E if counts is None else int((counts > 0).sum())
     ffn_bytes = 2 * H * F * b * live + 2 * H * Fs * b + 2 * rows * H * b
-    combine = rows * H * b + 8 * rows + (T * H * b if Fs else 0) + T * H * b
+    combine = rows * H * b + 8 * assign + (T * H * b if Fs else 0) + T * H * b
     return dict(route_bytes=route, dispatch_bytes=dispatch, ffn_flops=ffn_flops,
                 ffn_weight_bytes=ffn_bytes, combine_bytes=combine)
 
@@ -109,6 +117,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the five calls captured in one HIP graph")
+    ap.add_argument("--drop", action="store_true",
+                    help="enforce the expert capacity int(T*k/E*cf): dispatch drops the "
+                         "assignments past it (a variant, not the headline layer)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain 512 MiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -118,7 +129,6 @@ def main():
               "or collectives); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import sparse_mixture_experts_05_amd as moe
@@ -167,6 +177,7 @@ def main():
     ovf = torch.empty(E, dtype=torch.int32, device="cuda")
     strag = torch.empty(E, dtype=torch.int32, device="cuda")
     stream = torch.cuda.current_stream()
+    cap = moe.moe_capacity(T, k, E, cfg.cf) if args.drop else None
 
     def step(ev=None):
         if ev is not None:
@@ -174,7 +185,7 @@ def main():
         moe.moe_route(x, wg, bias, k, topk_idx=idx, topk_w=wts, ws=ws_r, stream=stream)
         if ev is not None:
             ev[1].record(stream)
-        moe.moe_dispatch(idx, x, E, out=dsp, ws=ws_d, stream=stream)
+        moe.moe_dispatch(idx, x, E, out=dsp, ws=ws_d, stream=stream, capacity=cap)
         if ev is not None:
             ev[2].record(stream)
         moe.moe_expert_ffn(dsp["xs"], dsp["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2, T=T, ys=ys,
@@ -199,7 +210,8 @@ def main():
         for s_ in range(args.steps):
             step(events[s_])
         torch.cuda.synchronize()
-        graph = moe.MoELayerGraph(wg, bias, w1, w2, k, T, ws1=ws1, ws2=ws2, capacity_factor=cfg.cf)
+        graph = moe.MoELayerGraph(wg, bias, w1, w2, k, T, ws1=ws1, ws2=ws2, capacity_factor=cfg.cf,
+                                  drop=args.drop)
         graph.x.copy_(x)
         for _ in range(args.warmup):
             graph.graph.replay()
@@ -221,7 +233,8 @@ def main():
     per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
                              for s in range(args.steps)])) for i, n in enumerate(names)}
     counts = dsp["counts"].cpu().numpy()
-    work = algorithmic_work(cfg, counts)
+    kept = np.diff(dsp["offsets"].cpu().numpy()) if args.drop else None
+    work = algorithmic_work(cfg, counts, kept)
     ms_step = elapsed * 1e3 / args.steps
     value = T * args.steps / elapsed
 
@@ -260,6 +273,7 @@ def main():
         "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k,
                    "d_ff": F, "shared_d_ff": Fs, "routing_bias_amplitude": cfg.bias_amp,
                    "capacity_factor": cfg.cf, "parallelism": "single GPU",
+                   "capacity_dropping": bool(args.drop),
                    "launch": "hip graph replay" if args.graph else "eager"},
         "roofline": {"bound": "mfma", "kernel": DOMINANT_KERNEL, "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,

@@ -5,6 +5,7 @@
  * The layer has five steps, one entry point each:
  *   moe_route      gate scores, softmax, top-k, renormalised weights
  *   moe_dispatch   expert histogram, offsets, stable permutation, row gather
+ *                  (moe_dispatch_capped: the same with each expert's capacity enforced)
  *   moe_expert_ffn grouped Linear -> erf-GeLU -> Linear over ragged segments
  *                  (plus the optional always-on shared expert)
  *   moe_combine    weighted sum of each token's k expert rows (+ shared row)
@@ -137,6 +138,26 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* xs,
                  void* ws, size_t ws_bytes, void* stream);
 
+/*
+ * moe_dispatch_capped - moe_dispatch with each expert's capacity enforced
+ * ([DIAG] section 3 counts the assignments past an expert's capacity
+ * int(T*k/E*cf); section 5 describes dropping them). Every expert keeps its
+ * first `capacity` assignments in token order (the order of moe_dispatch);
+ * the others are dropped: they get no buffer row and inv = -1.
+ *   counts[e]  = raw count, as in moe_dispatch (before dropping)
+ *   offsets[0] = 0, offsets[e+1] = offsets[e] + min(counts[e], capacity)
+ *   perm[p], xs[p] for p < offsets[E]: the kept rows, as in moe_dispatch
+ *                  (entries p >= offsets[E] are not written)
+ *   inv[t*k+j]  = the buffer row of a kept assignment, -1 for a dropped one
+ * moe_expert_ffn then runs on the kept rows (pass rows = T*k: an upper bound)
+ * and moe_combine skips the dropped assignments without renormalising the
+ * kept weights. capacity >= 0 (0 drops every assignment). Other arguments,
+ * the workspace and errors as moe_dispatch.
+ */
+int moe_dispatch_capped(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
+                        int capacity, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* inv, void* xs, void* ws, size_t ws_bytes, void* stream);
+
 /* Workspace bytes moe_expert_ffn needs; 0 on unsupported sizes. */
 size_t moe_expert_ffn_workspace_bytes(int rows, int T, int H, int E, int F, int Fs, int dtype);
 
@@ -149,7 +170,9 @@ size_t moe_expert_ffn_workspace_bytes(int rows, int T, int H, int E, int F, int 
  *     h      = GeLU(xs[p,:] . W1[e]^T)      GeLU(a) = 0.5*a*(1 + erf(a/sqrt(2)))
  *     ys[p,:] = h . W2[e]^T
  *   shared expert (when Fs > 0): ysh[t,:] = GeLU(x[t,:] . Ws1^T) . Ws2^T
- * xs [rows,H], offsets [E+1] (device, from moe_dispatch; offsets[E] == rows)
+ * xs [rows,H], offsets [E+1] (device, from moe_dispatch or moe_dispatch_capped;
+ *   offsets[E] <= rows: rows is an upper bound that sizes the launch and the
+ *   workspace, and ys rows past offsets[E] are not written)
  * w1 [E,F,H], w2 [E,H,F]; x [T,H], ws1 [Fs,H], ws2 [H,Fs] (NULL / Fs = 0: no shared expert)
  * ys [rows,H], ysh [T,H] (NULL when Fs = 0): device, written.
  * In bf16 mode h is rounded to bf16 before the second Linear (fp32 accumulation
@@ -168,6 +191,8 @@ int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int 
  * [BLOG] section 3.1 "scatter back to the original positions").
  *   out[t,:] = sum_{j=0..k-1} topk_w[t,j] * ys[inv[t*k+j],:]  (+ ysh[t,:])
  * summed in fp32, j ascending, shared row last; one write per token (no atomics).
+ * An assignment with inv < 0 (dropped by moe_dispatch_capped) adds nothing;
+ * the other weights are used as they are.
  * ys [T*k,H] dtype, inv [T*k] int32, topk_w [T,k] fp32, ysh [T,H] dtype or NULL: device, read
  * out [T,H] dtype: device, written
  */

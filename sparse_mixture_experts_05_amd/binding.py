@@ -25,6 +25,8 @@ SIGNATURES = {
     "moe_route_workspace_bytes": (_sz, [_i, _i, _i, _i, _i]),
     "moe_dispatch_workspace_bytes": (_sz, [_i, _i, _i]),
     "moe_dispatch": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "moe_dispatch_capped": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp,
+                                 _sz, _vp]),
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp,
                             _vp, _vp, _sz, _vp]),
@@ -162,8 +164,15 @@ def _workspace(nbytes: int, device, ws=None):
     return torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
 
 
-def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None):
-    """Returns dict(counts, offsets, perm, inv, xs)."""
+def moe_capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
+    """Expert capacity int((T*k/E) * cf), the same double operations as the
+    statistics kernel."""
+    return int(((T * k) / E) * float(capacity_factor))
+
+
+def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=None):
+    """Returns dict(counts, offsets, perm, inv, xs). With ``capacity`` (int >= 0)
+    each expert keeps its first ``capacity`` assignments (moe_dispatch_capped)."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
@@ -175,11 +184,17 @@ def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None):
                    xs=torch.empty((T * k, H), dtype=x.dtype, device=dev))
     nbytes = moe_dispatch_workspace_bytes(T, E, k)
     ws = _workspace(nbytes, dev, ws)
-    _check("moe_dispatch", lib().moe_dispatch(
-        _dev(topk_idx, "topk_idx", torch.int32), _dev(x, "x"), T, H, E, k, _dtype_code(x),
-        _dev(out["counts"], "counts", torch.int32), _dev(out["offsets"], "offsets", torch.int32),
-        _dev(out["perm"], "perm", torch.int32), _dev(out["inv"], "inv", torch.int32),
-        _dev(out["xs"], "xs", x.dtype), _dev(ws, "ws"), ws.numel(), _stream(stream)))
+    tail = (_dtype_code(x),
+            _dev(out["counts"], "counts", torch.int32), _dev(out["offsets"], "offsets", torch.int32),
+            _dev(out["perm"], "perm", torch.int32), _dev(out["inv"], "inv", torch.int32),
+            _dev(out["xs"], "xs", x.dtype), _dev(ws, "ws"), ws.numel(), _stream(stream))
+    if capacity is None:
+        _check("moe_dispatch", lib().moe_dispatch(
+            _dev(topk_idx, "topk_idx", torch.int32), _dev(x, "x"), T, H, E, k, *tail))
+    else:
+        _check("moe_dispatch_capped", lib().moe_dispatch_capped(
+            _dev(topk_idx, "topk_idx", torch.int32), _dev(x, "x"), T, H, E, k, int(capacity),
+            *tail))
     return out
 
 
@@ -248,12 +263,13 @@ def moe_load_stats(counts, T: int, k: int, capacity_factor: float, stats=None, o
 
 
 def moe_layer_forward(x, wg, bias, w1, w2, k: int, ws1=None, ws2=None, stream=None,
-                      prob_mean=None):
+                      prob_mean=None, capacity=None):
     """All five steps on one stream (no host synchronisation). Returns a dict.
-    prob_mean (optional fp32 [E]) receives the mean router probabilities."""
+    prob_mean (optional fp32 [E]) receives the mean router probabilities;
+    capacity (optional int) drops each expert's assignments past it."""
     E = wg.shape[0]
     idx, w = moe_route(x, wg, bias, k, stream=stream, prob_mean=prob_mean)
-    d = moe_dispatch(idx, x, E, stream=stream)
+    d = moe_dispatch(idx, x, E, stream=stream, capacity=capacity)
     ys, ysh = moe_expert_ffn(d["xs"], d["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2,
                              T=x.shape[0], stream=stream)
     out = moe_combine(ys, d["inv"], w, ysh, stream=stream)
@@ -270,20 +286,24 @@ class MoELayerGraph:
     input buffer and replays. The library never allocates, synchronises or
     clears memory with memset, so its launches are capture-safe.
 
-    With ``bias_gamma`` set (and a bias tensor given), every replay also ends
+    With ``drop``, dispatch enforces the expert capacity int(T*k/E*cf)
+    (moe_dispatch_capped). With ``bias_gamma`` set (and a bias tensor given),
+    every replay also ends
     with the dynamic-bias step on ``bias`` in place and writes the mean router
     probabilities ``prob_mean`` and load fractions ``load_frac``: the next
     replay routes with the updated bias.
     """
 
     def __init__(self, wg, bias, w1, w2, k: int, T: int, ws1=None, ws2=None,
-                 capacity_factor: float = 1.25, bias_gamma: float | None = None):
+                 capacity_factor: float = 1.25, bias_gamma: float | None = None,
+                 drop: bool = False):
         E, H = wg.shape
         F = w1.shape[1]
         Fs = 0 if ws1 is None else ws1.shape[0]
         dev, dtype = wg.device, wg.dtype
         dt = _dtype_code(wg)
         self.k, self.T, self.cf = k, T, capacity_factor
+        self.cap = moe_capacity(T, k, E, capacity_factor) if drop else None
         self.wg, self.bias, self.w1, self.w2, self.ws1, self.ws2 = wg, bias, w1, w2, ws1, ws2
         self.x = torch.zeros((T, H), dtype=dtype, device=dev)
         self.idx = torch.empty((T, k), dtype=torch.int32, device=dev)
@@ -328,7 +348,8 @@ class MoELayerGraph:
     def _layer(self):
         moe_route(self.x, self.wg, self.bias, self.k, topk_idx=self.idx, topk_w=self.w,
                   ws=self.ws_r, prob_mean=self.prob_mean)
-        moe_dispatch(self.idx, self.x, self.wg.shape[0], out=self.dsp, ws=self.ws_d)
+        moe_dispatch(self.idx, self.x, self.wg.shape[0], out=self.dsp, ws=self.ws_d,
+                     capacity=self.cap)
         moe_expert_ffn(self.dsp["xs"], self.dsp["offsets"], self.w1, self.w2, x=self.x,
                        ws1=self.ws1, ws2=self.ws2, T=self.T, ys=self.ys, ysh=self.ysh,
                        ws=self.ws_f)

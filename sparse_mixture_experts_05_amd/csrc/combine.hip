@@ -8,7 +8,9 @@
 //
 // One wavefront per token. The token's k buffer rows are found through inv
 // (a gather, so every output row is written exactly once: no atomics, and a
-// fixed summation order j = 0..k-1, then the shared row). 16-byte loads and
+// fixed summation order j = 0..k-1, then the shared row). An assignment that
+// a capacity dropped (inv < 0) is skipped; the other weights are kept as they
+// are (no renormalisation). 16-byte loads and
 // stores; fp32 accumulation in registers.
 #include "common.hpp"
 #include "kernels.hpp"
@@ -45,9 +47,12 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
   if (t >= T) return;
   int row[8];
   float wt[8];
+  bool keep[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    row[j] = j < k ? min(max(inv[(size_t)t * k + j], 0), T * k - 1) : 0;
+    const int r = j < k ? inv[(size_t)t * k + j] : -1;
+    keep[j] = r >= 0;  // a dropped assignment (inv < 0) adds nothing
+    row[j] = min(max(r, 0), T * k - 1);
     wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
   for (int c = lane; c < vpr; c += kWave) {
@@ -55,10 +60,10 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     uint4 v[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < k) v[j] = ys[(size_t)row[j] * vpr + c];
+      if (j < k && keep[j]) v[j] = ys[(size_t)row[j] * vpr + c];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      if (j < k) fma_bf16x8(acc, v[j], wt[j]);
+      if (j < k && keep[j]) fma_bf16x8(acc, v[j], wt[j]);
     if (ysh != nullptr) add_bf16x8(acc, ysh[(size_t)t * vpr + c]);
     uint4 o;
     o.x = pack_bf16x2(acc[0], acc[1]);
@@ -78,16 +83,19 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(
   if (t >= T) return;
   int row[8];
   float wt[8];
+  bool keep[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    row[j] = j < k ? min(max(inv[(size_t)t * k + j], 0), T * k - 1) : 0;
+    const int r = j < k ? inv[(size_t)t * k + j] : -1;
+    keep[j] = r >= 0;  // a dropped assignment (inv < 0) adds nothing
+    row[j] = min(max(r, 0), T * k - 1);
     wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
   for (int c = lane; c < vpr; c += kWave) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (j < k) {
+      if (j < k && keep[j]) {
         const float4 v = ys[(size_t)row[j] * vpr + c];
         acc.x = fmaf(wt[j], v.x, acc.x);
         acc.y = fmaf(wt[j], v.y, acc.y);

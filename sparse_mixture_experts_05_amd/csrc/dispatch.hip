@@ -20,6 +20,11 @@
 //             counters. Writes perm and inv (block 0 also counts and offsets).
 //   scatter - one wavefront per token: reads the token's row once with 16-byte
 //             loads and writes it to its k buffer rows.
+// With a capacity cap >= 0 ("Kimi K3 专家路由不均衡诊断" section 3 counts the
+// assignments past an expert's capacity, section 5 describes dropping them),
+// an assignment whose rank among its expert's assignments (token order) is
+// cap or more is dropped: inv = -1, no buffer row. offsets then describe the
+// kept rows (min(count, cap) per expert); counts stay the raw counts.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -49,11 +54,12 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
 }
 
 __global__ __launch_bounds__(kThreads) void rank_kernel(
-    const int32_t* __restrict__ idx, int T, int E, int k, int nb, const int32_t* __restrict__ blk,
-    int32_t* __restrict__ counts, int32_t* __restrict__ offsets, int32_t* __restrict__ perm,
-    int32_t* __restrict__ inv) {
-  __shared__ int tot[256];      // per-expert totals, then exclusive offsets
-  __shared__ int run[4][256];   // per-wave running positions
+    const int32_t* __restrict__ idx, int T, int E, int k, int nb, int cap,
+    const int32_t* __restrict__ blk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ perm, int32_t* __restrict__ inv) {
+  __shared__ int tot[256];      // per-expert kept totals, then inclusive scan
+  __shared__ int koff[256];     // exclusive offsets of the kept rows
+  __shared__ int run[4][256];   // per-wave running rank within the expert
   __shared__ int wcnt[4][256];  // per-wave counts
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
@@ -68,21 +74,23 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
       if (i < b) before += c;
     }
   }
-  tot[tid] = tid < E ? total : 0;
+  const int kept = cap < 0 ? total : min(total, cap);
+  tot[tid] = tid < E ? kept : 0;
   for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
   __syncthreads();
-  // Exclusive scan of the totals over experts (Hillis-Steele on 256 entries).
+  // Exclusive scan of the kept totals over experts (Hillis-Steele on 256 entries).
   for (int d = 1; d < 256; d <<= 1) {
     const int v = tid >= d ? tot[tid - d] : 0;
     __syncthreads();
     tot[tid] += v;
     __syncthreads();
   }
-  const int excl = tot[tid] - (tid < E ? total : 0);
+  const int excl = tot[tid] - (tid < E ? kept : 0);
+  koff[tid] = excl;
   if (b == 0 && tid < E) {
     counts[tid] = total;
     offsets[tid] = excl;
-    if (tid == E - 1) offsets[E] = excl + total;
+    if (tid == E - 1) offsets[E] = excl + kept;
   }
 
   // Per-wave counts of this block (order-free integer adds).
@@ -91,7 +99,7 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   for (int a = a0 + lane; a < a1; a += 64) atomicAdd(&wcnt[wave][expert_of(idx, a, E)], 1);
   __syncthreads();
   if (tid < E) {
-    int base = excl + before;
+    int base = before;  // rank of this block's first assignment within the expert
     for (int w = 0; w < 4; ++w) {
       run[w][tid] = base;
       base += wcnt[w][tid];
@@ -113,19 +121,25 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
       peers &= ((e >> bt) & 1) ? bal : ~bal;
     }
     const int rank = __popcll(peers & lt);
-    int pos = 0;
-    if (valid) pos = run[wave][e] + rank;
+    int r = 0;
+    if (valid) r = run[wave][e] + rank;  // rank within the expert, token order
     __builtin_amdgcn_wave_barrier();
-    if (valid && rank == 0) run[wave][e] = pos + __popcll(peers);
+    if (valid && rank == 0) run[wave][e] = r + __popcll(peers);
     __builtin_amdgcn_wave_barrier();
     if (valid) {
-      inv[a] = pos;
-      perm[pos] = a;
+      if (cap < 0 || r < cap) {
+        const int pos = koff[e] + r;
+        inv[a] = pos;
+        perm[pos] = a;
+      } else {
+        inv[a] = -1;
+      }
     }
   }
 }
 
-// One wavefront per token: read the row once, write it to its k buffer rows.
+// One wavefront per token: read the row once, write it to its k buffer rows
+// (dropped assignments, inv < 0, have none).
 template <typename V>
 __global__ __launch_bounds__(kThreads) void scatter_kernel(const V* __restrict__ x,
                                                            const int32_t* __restrict__ inv,
@@ -146,10 +160,12 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const V* __restrict__
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < k) {
-        V* d = xs + (size_t)dst[j] * vec_per_row;
+        if (dst[j] >= 0) {
+          V* d = xs + (size_t)dst[j] * vec_per_row;
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (c + u * kWave < vec_per_row) d[c + u * kWave] = v[u];
+          for (int u = 0; u < 4; ++u)
+            if (c + u * kWave < vec_per_row) d[c + u * kWave] = v[u];
+        }
       }
     }
   }
@@ -165,15 +181,15 @@ size_t dispatch_ws_bytes(int T, int E) {
 }
 
 hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
-                           bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int cap, bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, void* xs, void* ws, hipStream_t s) {
   const int nb = dispatch_blocks(T);
   int32_t* blk = static_cast<int32_t*>(ws);
   hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, blk);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, blk,
-                     counts, offsets, perm, inv);
+  hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, cap,
+                     blk, counts, offsets, perm, inv);
   err = hipGetLastError();
   if (err != hipSuccess) return err;
   const int row_bytes = H * (bf16 ? 2 : 4);

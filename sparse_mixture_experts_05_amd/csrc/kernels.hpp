@@ -15,7 +15,7 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
 int dispatch_blocks(int T);
 size_t dispatch_ws_bytes(int T, int E);
 hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
-                           bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
+                           int cap, bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, void* xs, void* ws, hipStream_t s);
 
 size_t ffn_ws_bytes(int rows, int T, int F, int Fs, bool bf16);

@@ -75,8 +75,21 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
   if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
-  return from_hip(moe::launch_dispatch(topk_idx, x, T, H, E, k, dtype == MOE_BF16, counts,
+  return from_hip(moe::launch_dispatch(topk_idx, x, T, H, E, k, -1, dtype == MOE_BF16, counts,
                                        offsets, perm, inv, xs, ws, as_stream(stream)));
+}
+
+int moe_dispatch_capped(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
+                        int capacity, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,
+                        int32_t* inv, void* xs, void* ws, size_t ws_bytes, void* stream) {
+  if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !xs || !dtype_ok(dtype) ||
+      capacity < 0)
+    return MOE_ERR_INVALID_ARG;
+  const int st = check_tokens(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  return from_hip(moe::launch_dispatch(topk_idx, x, T, H, E, k, capacity, dtype == MOE_BF16,
+                                       counts, offsets, perm, inv, xs, ws, as_stream(stream)));
 }
 
 static int check_ffn(int rows, int T, int H, int E, int F, int Fs, int dtype) {

@@ -26,7 +26,7 @@ def declared_functions():
 def test_header_declares_the_five_steps():
     names = declared_functions()
     for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_load_stats",
-              "moe_bias_update", "moe_status_string", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
+              "moe_dispatch_capped", "moe_bias_update", "moe_status_string", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
               "moe_expert_ffn_workspace_bytes"]:
         assert n in names
 
@@ -109,6 +109,31 @@ def test_dispatch_validation_and_workspace():
     bad = list(args)
     bad[4] = 0
     assert L.moe_dispatch(*bad, FAKE, need, None) == -1
+
+
+def test_dispatch_capped_validation():
+    L = moe.lib()
+    need = L.moe_dispatch_workspace_bytes(4096, 128, 8)
+    args = [FAKE, FAKE, 4096, 4096, 128, 8, 320, 1, FAKE, FAKE, FAKE, FAKE, FAKE]
+    assert L.moe_dispatch_capped(*args, None, need, None) == -3
+    assert L.moe_dispatch_capped(*args, FAKE, need - 1, None) == -3
+    bad = list(args)
+    bad[6] = -1  # negative capacity
+    assert L.moe_dispatch_capped(*bad, FAKE, need, None) == -1
+    bad = list(args)
+    bad[8] = None  # counts
+    assert L.moe_dispatch_capped(*bad, FAKE, need, None) == -1
+    bad = list(args)
+    bad[4] = 257  # E
+    assert L.moe_dispatch_capped(*bad, FAKE, need, None) == -2
+
+
+def test_capacity_formula_matches_the_statistics():
+    from oracle import capacity, load_stats
+    for T, k, E, cf in [(4096, 2, 8, 1.25), (4096, 8, 128, 1.25), (16384, 8, 256, 1.25),
+                        (1, 8, 128, 1.25), (37, 3, 5, 0.7)]:
+        assert moe.moe_capacity(T, k, E, cf) == capacity(T, k, E, cf)
+        assert moe.moe_capacity(T, k, E, cf) == load_stats([T * k] + [0] * (E - 1), T, k, cf)["capacity"]
 
 
 def test_ffn_validation_and_workspace():

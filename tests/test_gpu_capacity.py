@@ -1,0 +1,93 @@
+"""GPU parity of the capacity-enforced layer (moe_dispatch_capped + FFN + combine).
+
+Against the oracle's dispatch_capped and layer_rows(keep=...):
+  bit-exact: raw counts, kept offsets, the kept part of perm, inv (-1 for a
+             dropped assignment), the kept xs rows;
+  out:       fp32 max |diff| <= 1e-4, bf16 relative L2 <= 2e-2 (all tokens on
+             small layers, sampled tokens on the full-size ones).
+The capacity is int((T*k/E)*cf) unless a case gives it. The case is printed
+before each GPU step.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_05_amd as moe
+from synth import MoEConfig
+from tests.parity import TOL_BF16_REL_L2, TOL_F32_ABS, sample_tokens, to_dev, to_host
+from tests.support import conditioned_layer
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    ("tiny_fp32", None),
+    ("tiny_fp32", 0),
+    (MoEConfig("cap_mid_bf16", T=700, H=512, E=8, k=2, F=640, bias_amp=1.0), 150),
+    (MoEConfig("cap_skew_small_tiles", T=257, H=512, E=64, k=8, F=256, Fs=256, bias_amp=2.0), None),
+    (MoEConfig("cap_E256_skew", T=600, H=256, E=256, k=8, F=128, bias_amp=2.5), None),
+    ("fine_grained_zipf", None),
+    ("heavy_skew", None),
+    ("decode@T1", None),
+    ("decode@T32", None),
+    ("mixtral_8x7b", None),
+]
+
+
+def _name(c):
+    cfg, cap = c
+    n = cfg if isinstance(cfg, str) else cfg.name
+    return f"{n}-cap{'cf' if cap is None else cap}"
+
+
+@pytest.mark.parametrize("case", CASES, ids=_name)
+def test_capped_layer_parity(case):
+    spec, cap = case
+    cfg, L, redrawn = conditioned_layer(spec)
+    T, k, E = cfg.T, cfg.k, cfg.E
+    if cap is None:
+        cap = oracle.capacity(T, k, E, cfg.cf)
+        assert cap == moe.moe_capacity(T, k, E, cfg.cf)
+    idx, w, _, _ = oracle.route(L["x"], L["wg"], L["bias"], k)
+    counts, offsets, perm, inv, _ = oracle.dispatch_capped(idx, np.empty((T, 0)), E, cap)
+    keep = oracle.kept_mask(inv).reshape(T, k)
+    full = T * H_bytes(cfg) <= 64 * 1024 * 1024 and T <= 4096 and cfg.F * cfg.H <= 1 << 22
+    sample = None if full else sample_tokens(cfg, idx, n=32)
+    print(f"\n[gpu] capped {cfg.name}: T={T} E={E} k={k} cap={cap} kept={int(offsets[-1])}/{T * k} "
+          f"sample={'all' if sample is None else sample.size}", flush=True)
+
+    d = {kk: to_dev(v) for kk, v in L.items()}
+    r = moe.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"], k, ws1=d["ws1"],
+                              ws2=d["ws2"], capacity=cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(r["topk_idx"]), idx)
+    assert np.array_equal(to_host(r["counts"]), counts)
+    assert np.array_equal(to_host(r["offsets"]), offsets)
+    n = int(offsets[-1])
+    assert np.array_equal(to_host(r["perm"])[:n], perm)
+    assert np.array_equal(to_host(r["inv"]), inv)
+    xs = to_host(r["xs"][:n])
+    assert np.array_equal(xs, L["x"][perm // k])
+
+    tokens = np.arange(T) if sample is None else sample
+    out_ref, _, _ = oracle.layer_rows(L, idx, w, tokens, keep=keep)
+    got = oracle.widen(to_host(r["out"]))[tokens]
+    if cfg.dtype == "bf16":
+        err = float(np.linalg.norm(got - out_ref) / max(np.linalg.norm(out_ref), 1e-300))
+        print(f"[gpu] capped {cfg.name}: out rel L2 {err:.3e}", flush=True)
+        assert err <= TOL_BF16_REL_L2
+    else:
+        err = float(np.abs(got - out_ref).max())
+        print(f"[gpu] capped {cfg.name}: out max abs {err:.3e}", flush=True)
+        assert err <= TOL_F32_ABS
+    if cap == 0:
+        # everything dropped: the output is the shared expert alone (or zero)
+        if L["ws1"] is None:
+            assert not np.any(to_host(r["out"]).view(np.uint16 if cfg.dtype == "bf16" else np.uint32)
+                              & (0x7fff if cfg.dtype == "bf16" else 0x7fffffff))
+    del d, r
+    torch.cuda.empty_cache()
+
+
+def H_bytes(cfg):
+    return cfg.H * (2 if cfg.dtype == "bf16" else 4)
