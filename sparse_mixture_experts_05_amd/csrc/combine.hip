@@ -38,39 +38,56 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], uint4 v) {
   }
 }
 
-// bf16: each 16-byte vector holds 8 values.
+// bf16: each 16-byte vector holds 8 values. KM >= k (a power of two); U = 8/KM
+// column steps are loaded before any is summed, so about 8 16-byte loads per
+// lane are in flight whatever k is.
+template <int KM>
 __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     const uint4* __restrict__ ys, const int32_t* __restrict__ inv, const float* __restrict__ w,
     const uint4* __restrict__ ysh, int T, int vpr, int k, uint4* __restrict__ out) {
+  constexpr int U = 8 / KM;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
-  int row[8];
-  float wt[8];
-  bool keep[8];
+  int row[KM];
+  float wt[KM];
+  bool keep[KM];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < KM; ++j) {
     const int r = j < k ? inv[(size_t)t * k + j] : -1;
     keep[j] = r >= 0;  // a dropped assignment (inv < 0) adds nothing
     row[j] = min(max(r, 0), T * k - 1);
     wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
-  for (int c = lane; c < vpr; c += kWave) {
-    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    uint4 v[8];
+  for (int c0 = lane; c0 < vpr; c0 += U * kWave) {
+    uint4 v[U][KM], sh[U];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k && keep[j]) v[j] = ys[(size_t)row[j] * vpr + c];
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c < vpr) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (j < k && keep[j]) fma_bf16x8(acc, v[j], wt[j]);
-    if (ysh != nullptr) add_bf16x8(acc, ysh[(size_t)t * vpr + c]);
-    uint4 o;
-    o.x = pack_bf16x2(acc[0], acc[1]);
-    o.y = pack_bf16x2(acc[2], acc[3]);
-    o.z = pack_bf16x2(acc[4], acc[5]);
-    o.w = pack_bf16x2(acc[6], acc[7]);
-    out[(size_t)t * vpr + c] = o;
+        for (int j = 0; j < KM; ++j)
+          if (keep[j]) v[u][j] = ys[(size_t)row[j] * vpr + c];
+        if (ysh != nullptr) sh[u] = ysh[(size_t)t * vpr + c];
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int c = c0 + u * kWave;
+      if (c < vpr) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < KM; ++j)
+          if (keep[j]) fma_bf16x8(acc, v[u][j], wt[j]);
+        if (ysh != nullptr) add_bf16x8(acc, sh[u]);
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        out[(size_t)t * vpr + c] = o;
+      }
+    }
   }
 }
 
@@ -121,9 +138,13 @@ hipError_t launch_combine(const void* ys, const int32_t* inv, const float* topk_
                           hipStream_t s) {
   const int grid = (T + 3) / 4;
   if (bf16) {
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid), dim3(kThreads), 0, s,
-                       static_cast<const uint4*>(ys), inv, topk_w, static_cast<const uint4*>(ysh),
-                       T, H / 8, k, static_cast<uint4*>(out));
+    auto kern = k <= 1   ? combine_bf16_kernel<1>
+                : k <= 2 ? combine_bf16_kernel<2>
+                : k <= 4 ? combine_bf16_kernel<4>
+                         : combine_bf16_kernel<8>;
+    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint4*>(ys), inv,
+                       topk_w, static_cast<const uint4*>(ysh), T, H / 8, k,
+                       static_cast<uint4*>(out));
   } else {
     hipLaunchKernelGGL(combine_f32_kernel, dim3(grid), dim3(kThreads), 0, s,
                        static_cast<const float4*>(ys), inv, topk_w,

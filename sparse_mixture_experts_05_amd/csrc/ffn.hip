@@ -47,6 +47,7 @@ struct GemmArgs {
   int routed_tiles;  // grid share of the routed group: mtiles_max * ntiles
   int shared_M;      // 0 = no shared group
   int gelu;
+  float* part;       // split-K partial tiles of the last round (big kernel), or null
 };
 
 struct Tile {
@@ -55,6 +56,9 @@ struct Tile {
   int row0;   // first row of the tile in A / C
   int M;      // valid rows in this tile (<= BM)
   int n0;     // first column
+  int spl;    // K slices of this tile (1: the whole K in one workgroup)
+  int ks;     // this workgroup's slice
+  int unit0;  // partial-tile index of slice 0 (split tiles), else -1
 };
 
 // Field-wise select (a reference into the kernel arguments chosen at run time
@@ -138,11 +142,29 @@ __device__ bool find_tile(const GemmArgs& a, Tile& t) {
 // groups ordered by descending partial-tile rows (ties: lower group first).
 // They skip the 32-row sub-tiles past the segment end, so they are the short
 // tiles; running them last, longest first, packs the final round.
+//
+// Split K in the last round: an XCD runs S = CF + CP tiles, kSlots at a time.
+// When the last round holds tail = S mod kSlots tiles and that is at most half
+// a round, each of those tiles is cut into spl K slices (one workgroup each,
+// spl = kSlots / tail, at most kMaxSplit, and every slice keeps at least
+// kMinSliceStages K stages). A slice writes its fp32 partial tile to a.part;
+// a second launch (mode 1) sums the spl partials of each tail tile in slice
+// order and runs the epilogue. The partition depends only on the counts, so
+// results repeat bit for bit. Only long K qualifies (every group's K at least
+// kSplitMinK): a short tail tile does not repay the partial round trip and
+// the extra launch (measured on the fine-grained and heavy-skew layers).
 constexpr int kXcds = 8;
+constexpr int kSlots = 32;    // CUs per XCD: workgroups one round of an XCD runs
+constexpr int kMaxSplit = 8;
+constexpr int kMinSliceStages = 32;  // a slice writes a 256 KB partial: keep it worth it
+constexpr int kSplitMinK = 8192;
 constexpr int kBigWaves = 8;
+constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
 
+// mode 0: the tile (or K slice) workgroup blockIdx.x computes; mode 1: the
+// split tail tile workgroup blockIdx.x reduces. Returns false if none.
 template <int BM, int BN, int GN>
-__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t) {
+__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0) {
   __shared__ int pf[257], pp[257];
   __shared__ int prow[257], sgrp[257];
   __shared__ int sel[4];
@@ -229,8 +251,31 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t) {
   const int F = pf[last], P = pp[last];
   const int CF = (F + kXcds - 1) / kXcds;
   const int CP = (P + kXcds - 1) / kXcds;
+  const int S = CF + CP;
+  const int R = S / kSlots, tail = S - R * kSlots;
+  int spl = 1;
+  if (a.part != nullptr && tail > 0 && 2 * tail <= kSlots) {  // a.part: K long enough
+    int ktmin = a.routed.K / 64;
+    if (a.shared_M > 0) ktmin = min(ktmin, a.shared.K / 64);
+    spl = max(1, min(min(kSlots / tail, kMaxSplit), ktmin / kMinSliceStages));
+  }
   const int g = blockIdx.x;
-  const int x = g % kXcds, slot = g / kXcds;
+  const int x = g % kXcds;
+  int slot = g / kXcds, ks = 0, unit0 = -1;
+  if (mode == 0) {
+    if (spl > 1 && slot >= R * kSlots) {
+      const int u = slot - R * kSlots;
+      if (u >= tail * spl) return false;
+      const int tt = u / spl;
+      ks = u - tt * spl;
+      slot = R * kSlots + tt;
+      unit0 = x * kSlots + tt * spl;
+    }
+  } else {
+    if (spl <= 1 || slot >= tail) return false;
+    unit0 = x * kSlots + slot * spl;
+    slot = R * kSlots + slot;
+  }
   if (slot >= CF + CP) return false;
   const bool is_full = slot < CF;
   const int q = is_full ? x * CF + slot : (slot - CF) * kXcds + x;
@@ -281,6 +326,9 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t) {
   t.row0 = sel[1];
   t.M = sel[2];
   t.n0 = sel[3];
+  t.spl = unit0 >= 0 ? spl : 1;
+  t.ks = ks;
+  t.unit0 = unit0;
   return true;
 }
 
@@ -479,9 +527,12 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
     const int c = (lane & 7) ^ ((r >> 1) & 7);
     gb[j] = B + (size_t)min(r, nvalid - 1) * K + c * 8;
   }
+  // K stages of this workgroup: all of them, or one slice of a split tail tile
+  const int KT0 = K / BK;
+  const int kbase = t.ks * KT0 / t.spl, kend = (t.ks + 1) * KT0 / t.spl;
   auto issue = [&](int kt) {
     uint8_t* base = smem + (kt & 1) * STAGE;
-    const int k0 = kt * BK;
+    const int k0 = (kbase + kt) * BK;
 #pragma unroll
     for (int j = 0; j < A_INST; ++j)
       lds_dma16(ga[j] + k0, base + (wave * A_INST + j) * ROWS_PER_INST * ROWB);
@@ -530,7 +581,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa_[i]), as_bf16x8(fb_[j]),
                                                                 acc[i][j], 0, 0, 0);
     };
-    const int KT = K / BK;
+    const int KT = kend - kbase;
     issue(0);
     if (KT > 1) {
       issue(1);
@@ -563,6 +614,23 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
   else
     main_loop(std::integral_constant<bool, true>{});
 
+  if (t.unit0 >= 0) {
+    // one K slice of a split tail tile: the fp32 partial tile, row-major,
+    // goes to its slot; the reduce launch sums the slices and runs the epilogue
+    float* P = args.part + (size_t)(t.unit0 + t.ks) * BM * BN;
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int col = wn * WTN + j * 32 + (lane & 31);
+          P[(size_t)row * BN + col] = acc[i][j][v];
+        }
+    return;
+  }
+
   // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
   // (v/4)*8 + (lane/32)*4 + v%4. Lanes 2m and 2m+1 (adjacent columns) swap
   // one value per row pair with DPP, so each stores a bf16 pair (4 bytes):
@@ -590,6 +658,37 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
         if (cok && row < M) *reinterpret_cast<uint32_t*>(C + (size_t)row * N + pcol) = packed;
       }
     }
+}
+
+
+// Sums the K slices of each split tail tile (slice order) and runs the
+// epilogue of the big kernel: erf-GeLU if requested, bf16 rounding, rows past
+// the segment end and columns past N masked.
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void gemm_tail_reduce_kernel(GemmArgs args) {
+  Tile t;
+  if (!find_tile_blocked<BM, BN, 8>(args, t, 1)) return;
+  const Group G = pick_group(args, t.group);
+  const int N = G.N;
+  uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
+  const int nvalid = N - t.n0;
+  const bool gelu = args.gelu != 0;
+  const float* P = args.part + (size_t)t.unit0 * BM * BN;
+  for (int q = threadIdx.x; q < BM * BN / 2; q += kThreads) {
+    const int row = q / (BN / 2), col = (q % (BN / 2)) * 2;
+    if (row >= t.M || col >= nvalid) continue;
+    float y0 = 0.0f, y1 = 0.0f;
+    for (int ks = 0; ks < t.spl; ++ks) {
+      const float2 v = *reinterpret_cast<const float2*>(P + (size_t)ks * BM * BN + (size_t)row * BN + col);
+      y0 += v.x;
+      y1 += v.y;
+    }
+    if (gelu) {
+      y0 = gelu_erf_fast(y0);
+      y1 = gelu_erf_fast(y1);
+    }
+    *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) = pack_bf16x2(y0, y1);
+  }
 }
 
 // ----------------------------------------------------------------- fp32 VALU
@@ -686,17 +785,30 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
   dim3 grid;
   GemmArgs b = a;
   grid_of<256, 256>(b, rows, E, grid);
-  // full and partial runs are each rounded up per XCD: at most 2*8 extra slots
-  grid.x = (grid.x + 2 * kXcds + kXcds - 1) / kXcds * kXcds;
+  const bool long_k = b.routed.K >= kSplitMinK && (b.shared_M == 0 || b.shared.K >= kSplitMinK);
+  if (!long_k) b.part = nullptr;
+  // full and partial runs are each rounded up per XCD (at most 2*8 extra
+  // slots); a split last round adds at most one round of kSlots per XCD
+  grid.x = (grid.x + 2 * kXcds + kXcds - 1) / kXcds * kXcds + (b.part ? kXcds * kSlots : 0);
   hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves>), grid, dim3(kBigWaves * 64), 0, s, b);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || b.part == nullptr) return err;
+  hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>), dim3(kXcds * kSlots / 2), dim3(kThreads),
+                     0, s, b);
   return hipGetLastError();
 }
 
+// The big-tile path (bf16, enough rows per expert) also needs the split-K
+// partial tiles.
+bool big_tiles(int rows, int E, bool bf16) { return bf16 && (long long)rows >= 64LL * E; }
+
 }  // namespace
 
-size_t ffn_ws_bytes(int rows, int T, int F, int Fs, bool bf16) {
+size_t ffn_ws_bytes(int rows, int T, int E, int F, int Fs, bool bf16) {
   const size_t es = bf16 ? 2 : 4;
-  return align256((size_t)rows * F * es) + align256((size_t)T * Fs * es);
+  size_t b = align256((size_t)rows * F * es) + align256((size_t)T * Fs * es);
+  if (big_tiles(rows, E, bf16)) b += kPartTiles * 256 * 256 * sizeof(float);
+  return b;
 }
 
 hipError_t launch_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H,
@@ -706,9 +818,12 @@ hipError_t launch_expert_ffn(const void* xs, const int32_t* offsets, int rows, i
   const size_t es = bf16 ? 2 : 4;
   uint8_t* h = static_cast<uint8_t*>(ws);
   uint8_t* hs = h + align256((size_t)rows * F * es);
+  float* part = big_tiles(rows, E, bf16)
+                    ? reinterpret_cast<float*>(hs + align256((size_t)T * Fs * es))
+                    : nullptr;
   const bool shared = Fs > 0;
   // Few rows per expert on average: decode-like, weight-streaming bound.
-  const bool small_segments = (long long)rows < 64LL * E;
+  const bool small_segments = !big_tiles(rows, E, bf16) && bf16;
 
   GemmArgs up{};
   up.routed = Group{xs, w1, h, F, H};
@@ -718,6 +833,7 @@ hipError_t launch_expert_ffn(const void* xs, const int32_t* offsets, int rows, i
   up.rows = rows;
   up.shared_M = shared ? T : 0;
   up.gelu = 1;
+  up.part = part;
   hipError_t err = run_gemm(up, rows, E, bf16, small_segments, s);
   if (err != hipSuccess) return err;
 
@@ -729,6 +845,7 @@ hipError_t launch_expert_ffn(const void* xs, const int32_t* offsets, int rows, i
   down.rows = rows;
   down.shared_M = shared ? T : 0;
   down.gelu = 0;
+  down.part = part;
   return run_gemm(down, rows, E, bf16, small_segments, s);
 }
 

@@ -102,7 +102,7 @@ static int check_ffn(int rows, int T, int H, int E, int F, int Fs, int dtype) {
 
 size_t moe_expert_ffn_workspace_bytes(int rows, int T, int H, int E, int F, int Fs, int dtype) {
   if (check_ffn(rows, T, H, E, F, Fs, dtype) != MOE_OK) return 0;
-  return moe::ffn_ws_bytes(rows, T, F, Fs, dtype == MOE_BF16);
+  return moe::ffn_ws_bytes(rows, T, E, F, Fs, dtype == MOE_BF16);
 }
 
 int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H, int F,
@@ -113,7 +113,7 @@ int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int 
   const int st = check_ffn(rows, T, H, E, F, Fs, dtype);
   if (st != MOE_OK) return st;
   if (Fs > 0 && (!x || !ws1 || !ws2 || !ysh)) return MOE_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, F, Fs, dtype == MOE_BF16))
+  if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, E, F, Fs, dtype == MOE_BF16))
     return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_expert_ffn(xs, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T, Fs,
                                          dtype == MOE_BF16, ys, Fs > 0 ? ysh : nullptr, ws,
