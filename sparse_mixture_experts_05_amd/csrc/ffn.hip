@@ -334,18 +334,27 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0) {
 
 // ----------------------------------------------------------------- bf16 MFMA
 
+// Small-segment kernel (decode-like launches: few rows per expert, so the
+// cost is streaming the weights). BM x BN tile, 4 waves in WM x WN. The
+// operand rows are copied global -> LDS with global_load_lds (8 rows of 128
+// contiguous bytes per instruction) into a ring of NS stages of BK = 64, so
+// NS - 1 stages of weights are in flight per workgroup (two workgroups fit a
+// CU). Chunk c of row r sits at slot c ^ ((r >> 1) & 7): the 16 lanes served
+// together by a 128-bit read (16 consecutive rows, one chunk) hit 16
+// distinct 4-bank groups.
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
   constexpr int BK = 64;                      // bf16 elements per K step
   constexpr int ROWB = BK * 2;                // bytes per staged row (128)
   constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
   constexpr int SM = WTM / 32, SN = WTN / 32; // 32x32 sub-tiles per wave
-  constexpr int A_LD = BM * (ROWB / 16) / kThreads;  // 16-byte chunks per thread
-  constexpr int B_LD = BN * (ROWB / 16) / kThreads;
   constexpr int STAGE = (BM + BN) * ROWB;
+  constexpr int NS = 3;                                   // stages (2 workgroups per CU)
+  constexpr int NI = (BM + BN) / 8 / (kThreads / kWave);  // DMA instructions per wave per stage
   static_assert(WM * WN == 4, "4 waves");
-  static_assert(SM >= 1 && SN >= 1 && A_LD >= 1 && B_LD >= 1, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  static_assert(SM >= 1 && SN >= 1, "tile shape");
+  static_assert((BM + BN) % 32 == 0 && NI >= 1 && NI * (NS - 2) < 64, "whole DMA instructions");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
 
   Tile t;
   if (!find_tile<BM, BN>(args, t)) return;
@@ -359,22 +368,26 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
 
-  // Global source pointers and LDS destinations of this thread's chunks.
-  const uint16_t* ga[A_LD];
-  const uint16_t* gb[B_LD];
-  int la[A_LD], lb[B_LD];
+  // DMA plan: instruction q of this wave fills rows [8g, 8g + 8) of a stage
+  // (A rows first, then B rows); lane i takes row 8g + i/8, slot i%8.
+  const uint16_t* src[NI];
+  int dst[NI];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int q = tid + i * kThreads, r = q >> 3, c = q & 7;
-    ga[i] = A + (size_t)min(r, M - 1) * K + c * 8;
-    la[i] = r * ROWB + ((c ^ (r & 7)) << 4);
+  for (int q = 0; q < NI; ++q) {
+    const int g = wave * NI + q;
+    const int r = 8 * g + (lane >> 3);
+    const int chunk = (lane & 7) ^ ((r >> 1) & 7);
+    const uint16_t* row = r < BM ? A + (size_t)min(r, M - 1) * K
+                                 : B + (size_t)min(r - BM, N - t.n0 - 1) * K;
+    src[q] = row + chunk * 8;
+    dst[q] = g * 8 * ROWB;
   }
+  const int KT = K / BK;
+  auto issue = [&](int kt) {
+    uint8_t* base = smem + (kt % NS) * STAGE;
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int q = tid + i * kThreads, r = q >> 3, c = q & 7;
-    gb[i] = B + (size_t)min(r, N - t.n0 - 1) * K + c * 8;
-    lb[i] = BM * ROWB + r * ROWB + ((c ^ (r & 7)) << 4);
-  }
+    for (int q = 0; q < NI; ++q) lds_dma16(src[q] + kt * BK, base + dst[q]);
+  };
 
   f32x16_t acc[SM][SN];
 #pragma unroll
@@ -384,46 +397,32 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  u32x4_t ra[A_LD], rb[B_LD];
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) ra[i] = ld16(ga[i]);
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) rb[i] = ld16(gb[i]);
-#pragma unroll
-  for (int i = 0; i < A_LD; ++i) st16(smem + la[i], ra[i]);
-#pragma unroll
-  for (int i = 0; i < B_LD; ++i) st16(smem + lb[i], rb[i]);
-  __syncthreads();
-
   // Fragment rows (A: tile rows, B: tile columns) of this lane.
   int fa[SM], fb[SN];
 #pragma unroll
-  for (int i = 0; i < SM; ++i) fa[i] = wm * WTM + i * 32 + (lane & 31);
+  for (int i = 0; i < SM; ++i) fa[i] = (wm * WTM + i * 32 + (lane & 31)) * ROWB;
 #pragma unroll
-  for (int j = 0; j < SN; ++j) fb[j] = BM + wn * WTN + j * 32 + (lane & 31);
+  for (int j = 0; j < SN; ++j) fb[j] = (BM + wn * WTN + j * 32 + (lane & 31)) * ROWB;
+  const int sw = (lane >> 1) & 7;  // == (row >> 1) & 7 for every fragment row of this lane
   const int khalf = lane >> 5;
 
-  const int KT = K / BK;
+#pragma unroll
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < KT) issue(st);
   for (int kt = 0; kt < KT; ++kt) {
-    const int cur = (kt & 1) * STAGE;
-    const bool more = kt + 1 < KT;
-    if (more) {
-      const int k1 = (kt + 1) * BK;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) ra[i] = ld16(ga[i] + k1);
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) rb[i] = ld16(gb[i] + k1);
-    }
+    if (kt + NS - 2 < KT) wait_vmcnt<(NS - 2) * NI>();
+    else wait_vmcnt<0>();
+    lds_barrier();  // stage kt landed for every wave; stage kt-1 is no longer read
+    if (kt + NS - 1 < KT) issue(kt + NS - 1);
+    const uint8_t* cur = smem + (kt % NS) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      const int chunk = ks * 2 + khalf;
+      const int off = ((ks * 2 + khalf) ^ sw) << 4;
       u32x4_t fra[SM], frb[SN];
 #pragma unroll
-      for (int i = 0; i < SM; ++i)
-        fra[i] = ld16(smem + cur + fa[i] * ROWB + ((chunk ^ (fa[i] & 7)) << 4));
+      for (int i = 0; i < SM; ++i) fra[i] = ld16(cur + fa[i] + off);
 #pragma unroll
-      for (int j = 0; j < SN; ++j)
-        frb[j] = ld16(smem + cur + fb[j] * ROWB + ((chunk ^ (fb[j] & 7)) << 4));
+      for (int j = 0; j < SN; ++j) frb[j] = ld16(cur + fb[j] + off);
 #pragma unroll
       for (int i = 0; i < SM; ++i)
 #pragma unroll
@@ -431,14 +430,6 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fra[i]),
                                                               as_bf16x8(frb[j]), acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      const int nxt = ((kt + 1) & 1) * STAGE;
-#pragma unroll
-      for (int i = 0; i < A_LD; ++i) st16(smem + nxt + la[i], ra[i]);
-#pragma unroll
-      for (int i = 0; i < B_LD; ++i) st16(smem + nxt + lb[i], rb[i]);
-    }
-    __syncthreads();
   }
 
   // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
