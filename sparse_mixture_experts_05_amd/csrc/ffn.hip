@@ -164,7 +164,7 @@ constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
 // mode 0: the tile (or K slice) workgroup blockIdx.x computes; mode 1: the
 // split tail tile workgroup blockIdx.x reduces. Returns false if none.
 template <int BM, int BN, int GN>
-__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0) {
+__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int gid = -1) {
   __shared__ int pf[257], pp[257];
   __shared__ int prow[257], sgrp[257];
   __shared__ int sel[4];
@@ -259,7 +259,7 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0) {
     if (a.shared_M > 0) ktmin = min(ktmin, a.shared.K / 64);
     spl = max(1, min(min(kSlots / tail, kMaxSplit), ktmin / kMinSliceStages));
   }
-  const int g = blockIdx.x;
+  const int g = gid >= 0 ? gid : (int)blockIdx.x;
   const int x = g % kXcds;
   int slot = g / kXcds, ks = 0, unit0 = -1;
   if (mode == 0) {
@@ -654,26 +654,37 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
 
 // Sums the K slices of each split tail tile (slice order) and runs the
 // epilogue of the big kernel: erf-GeLU if requested, bf16 rounding, rows past
-// the segment end and columns past N masked.
+// the segment end and columns past N masked. kReduceParts workgroups share a
+// tile (BM / kReduceParts rows each), so the partials stream through many CUs.
+constexpr int kReduceParts = 8;
+
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void gemm_tail_reduce_kernel(GemmArgs args) {
   Tile t;
-  if (!find_tile_blocked<BM, BN, 8>(args, t, 1)) return;
+  if (!find_tile_blocked<BM, BN, 8>(args, t, 1, blockIdx.x / kReduceParts)) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N;
   uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
   const int nvalid = N - t.n0;
   const bool gelu = args.gelu != 0;
   const float* P = args.part + (size_t)t.unit0 * BM * BN;
-  for (int q = threadIdx.x; q < BM * BN / 2; q += kThreads) {
-    const int row = q / (BN / 2), col = (q % (BN / 2)) * 2;
+  constexpr int RR = BM / kReduceParts;  // rows of this workgroup
+  const int r0 = (blockIdx.x % kReduceParts) * RR;
+  for (int q = threadIdx.x; q < RR * BN / 2; q += kThreads) {
+    const int row = r0 + q / (BN / 2), col = (q % (BN / 2)) * 2;
     if (row >= t.M || col >= nvalid) continue;
+    float2 v[kMaxSplit];
+#pragma unroll
+    for (int ks = 0; ks < kMaxSplit; ++ks)  // all loads first, then the sum in slice order
+      if (ks < t.spl)
+        v[ks] = *reinterpret_cast<const float2*>(P + (size_t)ks * BM * BN + (size_t)row * BN + col);
     float y0 = 0.0f, y1 = 0.0f;
-    for (int ks = 0; ks < t.spl; ++ks) {
-      const float2 v = *reinterpret_cast<const float2*>(P + (size_t)ks * BM * BN + (size_t)row * BN + col);
-      y0 += v.x;
-      y1 += v.y;
-    }
+#pragma unroll
+    for (int ks = 0; ks < kMaxSplit; ++ks)
+      if (ks < t.spl) {
+        y0 += v[ks].x;
+        y1 += v[ks].y;
+      }
     if (gelu) {
       y0 = gelu_erf_fast(y0);
       y1 = gelu_erf_fast(y1);
@@ -784,8 +795,8 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
   hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves>), grid, dim3(kBigWaves * 64), 0, s, b);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || b.part == nullptr) return err;
-  hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>), dim3(kXcds * kSlots / 2), dim3(kThreads),
-                     0, s, b);
+  hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>),
+                     dim3(kXcds * kSlots / 2 * kReduceParts), dim3(kThreads), 0, s, b);
   return hipGetLastError();
 }
 
