@@ -161,13 +161,22 @@ constexpr int kSplitMinK = 8192;
 constexpr int kBigWaves = 8;
 constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
 
-// mode 0: the tile (or K slice) workgroup blockIdx.x computes; mode 1: the
-// split tail tile workgroup blockIdx.x reduces. Returns false if none.
-template <int BM, int BN, int GN>
-__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int gid = -1) {
-  __shared__ int pf[257], pp[257];
-  __shared__ int prow[257], sgrp[257];
-  __shared__ int sel[4];
+// Tables of the big-tile schedule (per workgroup, in LDS).
+struct SchedLds {
+  int pf[257], pp[257];    // inclusive scans: full tiles by group, partial tiles by rank
+  int prow[257], sgrp[257];  // partial-tile rows by group; group of each rank
+  int sel[4];              // the selected tile, broadcast
+};
+
+struct BigSched {
+  int F, P, CF, CP;  // full / partial tiles in all; per XCD
+  int R, tail, spl;  // whole rounds per XCD, tiles of the last round, K slices of those
+};
+
+// Computes the schedule of a big-tile launch: the same for every workgroup,
+// and for every tile a workgroup runs.
+template <int BM, int BN>
+__device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
   // Only the first 256 threads take part (the workgroup may be larger);
   // every thread still meets every barrier.
   const int tid = threadIdx.x;
@@ -198,15 +207,15 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int 
     xfull = (a.shared_M / BM) * nts;
     xpart = (a.shared_M % BM) ? nts : 0;
   }
-  if (act) prow[tid] = tid < ng ? cnt % BM : 0;
-  if (tid == 255) prow[256] = ng == 257 ? a.shared_M % BM : 0;
+  if (act) L.prow[tid] = tid < ng ? cnt % BM : 0;
+  if (tid == 255) L.prow[256] = ng == 257 ? a.shared_M % BM : 0;
   __syncthreads();
   // rank of each group with a partial tile: descending rows, ties by id
   auto rank_of = [&](int grp) {
-    const int r = prow[grp];
+    const int r = L.prow[grp];
     int k = 0;
     for (int o = 0; o < ng; ++o) {
-      const int ro = prow[o];
+      const int ro = L.prow[o];
       k += (ro > r) || (ro == r && o < grp);
     }
     return k;
@@ -216,52 +225,82 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int 
   if (tid == 255 && ng == 257) xrank = rank_of(256);
   __syncthreads();
   // pp is indexed by rank: partial tile counts in longest-first order
-  if (act) pp[tid] = 0;
-  if (tid == 255) pp[256] = 0;
+  if (act) L.pp[tid] = 0;
+  if (tid == 255) L.pp[256] = 0;
   __syncthreads();
   if (myrank >= 0) {
-    pp[myrank] = part;
-    sgrp[myrank] = tid;
+    L.pp[myrank] = part;
+    L.sgrp[myrank] = tid;
   }
   if (xrank >= 0) {
-    pp[xrank] = xpart;
-    sgrp[xrank] = 256;
+    L.pp[xrank] = xpart;
+    L.sgrp[xrank] = 256;
   }
-  if (act) pf[tid] = full;
-  if (tid == 0) sel[0] = -1;
+  if (act) L.pf[tid] = full;
+  if (tid == 0) L.sel[0] = -1;
   __syncthreads();
-  if (tid == 255) xpart = pp[256];  // the scan below folds entry 256 in separately
+  if (tid == 255) xpart = L.pp[256];  // the scan below folds entry 256 in separately
   __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {
-    const int vf = (act && tid >= d) ? pf[tid - d] : 0;
-    const int vp = (act && tid >= d) ? pp[tid - d] : 0;
+    const int vf = (act && tid >= d) ? L.pf[tid - d] : 0;
+    const int vp = (act && tid >= d) ? L.pp[tid - d] : 0;
     __syncthreads();
     if (act) {
-      pf[tid] += vf;
-      pp[tid] += vp;
+      L.pf[tid] += vf;
+      L.pp[tid] += vp;
     }
     __syncthreads();
   }
   if (tid == 255) {
-    pf[256] = pf[255] + xfull;
-    pp[256] = pp[255] + xpart;
+    L.pf[256] = L.pf[255] + xfull;
+    L.pp[256] = L.pp[255] + xpart;
   }
   __syncthreads();
   const int last = ng <= 256 ? ng - 1 : 256;
-  const int F = pf[last], P = pp[last];
+  const int F = L.pf[last], P = L.pp[last];
   const int CF = (F + kXcds - 1) / kXcds;
   const int CP = (P + kXcds - 1) / kXcds;
-  const int S = CF + CP;
-  const int R = S / kSlots, tail = S - R * kSlots;
+  const int slots = CF + CP;
+  const int R = slots / kSlots, tail = slots - R * kSlots;
   int spl = 1;
   if (a.part != nullptr && tail > 0 && 2 * tail <= kSlots) {  // a.part: K long enough
     int ktmin = a.routed.K / 64;
     if (a.shared_M > 0) ktmin = min(ktmin, a.shared.K / 64);
     spl = max(1, min(min(kSlots / tail, kMaxSplit), ktmin / kMinSliceStages));
   }
-  const int g = gid >= 0 ? gid : (int)blockIdx.x;
-  const int x = g % kXcds;
-  int slot = g / kXcds, ks = 0, unit0 = -1;
+  BigSched S;
+  S.F = F;
+  S.P = P;
+  S.CF = CF;
+  S.CP = CP;
+  S.R = R;
+  S.tail = tail;
+  S.spl = spl;
+  return S;
+}
+
+// Tile of logical slot `slot` on XCD x. mode 0: the tile (or K slice of a
+// split tail tile) to compute; mode 1: the split tail tile number `slot` to
+// reduce. Returns false if the slot holds none.
+template <int BM, int BN, int GN>
+__device__ bool big_tile(const GemmArgs& a, const BigSched& S, SchedLds& L, int x, int slot,
+                         int mode, Tile& t) {
+  const int tid = threadIdx.x;
+  const bool act = tid < 256;
+  const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
+  const int ntr = (a.routed.N + BN - 1) / BN;
+  const int nts = (a.shared.N + BN - 1) / BN;
+  auto rows_of = [&](int grp, int& off, int& cnt) {
+    if (grp < a.E) {
+      off = min(max(a.offsets[grp], 0), a.rows);
+      cnt = min(max(a.offsets[grp + 1], off), a.rows) - off;
+    } else {
+      off = 0;
+      cnt = a.shared_M;
+    }
+  };
+  const int F = S.F, P = S.P, CF = S.CF, CP = S.CP, R = S.R, tail = S.tail, spl = S.spl;
+  int ks = 0, unit0 = -1;
   if (mode == 0) {
     if (spl > 1 && slot >= R * kSlots) {
       const int u = slot - R * kSlots;
@@ -291,10 +330,10 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int 
       const int w = min(GN, nt_g - blk * GN);
       const int li = local - blk * mt_g * GN;
       const int mt = li / w, nt = blk * GN + li % w;
-      sel[0] = grp;
-      sel[1] = o + mt * BM;
-      sel[2] = BM;
-      sel[3] = nt * BN;
+      L.sel[0] = grp;
+      L.sel[1] = o + mt * BM;
+      L.sel[2] = BM;
+      L.sel[3] = nt * BN;
     }
   };
   auto check_part = [&](int grp, int p_incl, int p_excl) {
@@ -302,34 +341,50 @@ __device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int 
       int o, c;
       rows_of(grp, o, c);
       const int mt = c / BM;  // the partial row tile
-      sel[0] = grp;
-      sel[1] = o + mt * BM;
-      sel[2] = c - mt * BM;
-      sel[3] = (q - p_excl) * BN;
+      L.sel[0] = grp;
+      L.sel[1] = o + mt * BM;
+      L.sel[2] = c - mt * BM;
+      L.sel[3] = (q - p_excl) * BN;
     }
   };
   // full tiles by group id; partial tiles by rank (sgrp maps rank -> group)
+  __syncthreads();  // earlier readers of sel are done
+  if (tid == 0) L.sel[0] = -1;
+  __syncthreads();
   if (act && tid < ng) {
-    check_full(tid, pf[tid], pf[tid] - full);
-    const int pcount = pp[tid] - (tid ? pp[tid - 1] : 0);
-    check_part(sgrp[tid], pp[tid], pp[tid] - pcount);
+    int o_, c_;
+    rows_of(tid, o_, c_);
+    const int full = (c_ / BM) * (tid < a.E ? ntr : nts);
+    check_full(tid, L.pf[tid], L.pf[tid] - full);
+    const int pcount = L.pp[tid] - (tid ? L.pp[tid - 1] : 0);
+    check_part(L.sgrp[tid], L.pp[tid], L.pp[tid] - pcount);
   }
   if (tid == 255 && ng == 257) {
-    check_full(256, pf[256], pf[255]);
-    check_part(sgrp[256], pp[256], pp[255]);
+    check_full(256, L.pf[256], L.pf[255]);
+    check_part(L.sgrp[256], L.pp[256], L.pp[255]);
   }
   __syncthreads();
-  const int grp = sel[0];
+  const int grp = L.sel[0];
   if (grp < 0) return false;
   t.group = grp < a.E ? 0 : 1;
   t.e = grp < a.E ? grp : 0;
-  t.row0 = sel[1];
-  t.M = sel[2];
-  t.n0 = sel[3];
+  t.row0 = L.sel[1];
+  t.M = L.sel[2];
+  t.n0 = L.sel[3];
   t.spl = unit0 >= 0 ? spl : 1;
   t.ks = ks;
   t.unit0 = unit0;
   return true;
+}
+
+// The tile workgroup gid (default blockIdx.x) runs: schedule, then slot
+// gid / 8 on XCD gid % 8.
+template <int BM, int BN, int GN>
+__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int gid = -1) {
+  __shared__ SchedLds L;
+  const BigSched S = big_schedule<BM, BN>(a, L);
+  const int g = gid >= 0 ? gid : (int)blockIdx.x;
+  return big_tile<BM, BN, GN>(a, S, L, g % kXcds, g / kXcds, mode, t);
 }
 
 // ----------------------------------------------------------------- bf16 MFMA
