@@ -22,6 +22,7 @@
 // swizzled by row so fragment reads are bank-conflict free. Rows past the
 // segment end are clamped on load and masked on store.
 // fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
+#include <algorithm>
 #include <type_traits>
 
 #include "common.hpp"
@@ -406,7 +407,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
   constexpr int STAGE = (BM + BN) * ROWB;
   constexpr int NS = 3;                                   // stages (2 workgroups per CU)
   constexpr int NI = (BM + BN) / 8 / (kThreads / kWave);  // DMA instructions per wave per stage
-  static_assert(WM * WN == 4, "4 waves");
+  static_assert(WM * WN <= 4, "at most 4 computing waves");
   static_assert(SM >= 1 && SN >= 1, "tile shape");
   static_assert((BM + BN) % 32 == 0 && NI >= 1 && NI * (NS - 2) < 64, "whole DMA instructions");
   __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
@@ -421,7 +422,9 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
   const int M = t.M;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
+  // waves WM*WN .. 3 only take part in the copies (narrow tiles for few rows)
+  const bool computes = wave < WM * WN;
+  const int wm = computes ? wave / WN : 0, wn = computes ? wave % WN : 0;
 
   // DMA plan: instruction q of this wave fills rows [8g, 8g + 8) of a stage
   // (A rows first, then B rows); lane i takes row 8g + i/8, slot i%8.
@@ -472,6 +475,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
     const uint8_t* cur = smem + (kt % NS) * STAGE;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
+      if (!computes) break;
       const int off = ((ks * 2 + khalf) ^ sw) << 4;
       u32x4_t fra[SM], frb[SN];
 #pragma unroll
@@ -489,6 +493,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
 
   // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
   // (v/4)*8 + (lane/32)*4 + v%4 of each sub-tile.
+  if (!computes) return;
   const bool gelu = args.gelu != 0;
 #pragma unroll
   for (int i = 0; i < SM; ++i)
@@ -814,7 +819,8 @@ size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 template <int BM, int BN>
 void grid_of(GemmArgs& a, int rows, int E, dim3& grid) {
-  const int mt_max = rows / BM + E;  // sum_e ceil(c_e / BM) <= rows / BM + E
+  // sum_e ceil(c_e / BM) <= rows / BM + #{e : c_e > 0} <= rows / BM + min(E, rows)
+  const int mt_max = rows / BM + min(E, rows);
   a.routed_tiles = mt_max * ((a.routed.N + BN - 1) / BN);
   const int shared_tiles =
       a.shared_M > 0 ? ((a.shared_M + BM - 1) / BM) * ((a.shared.N + BN - 1) / BN) : 0;
@@ -838,7 +844,14 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kThreads), 0, s, b);
     return hipGetLastError();
   }
-  if (small_segments) return run_bf16<32, 128, 1, 4>(a, rows, E, s);
+  if (small_segments) {
+    // Fewer than two 32x128 tiles per CU (a handful of tokens): 32x64 tiles
+    // double the workgroups streaming the weights.
+    const long long nt128 = (long long)(rows / 32 + std::min(E, rows)) * ((a.routed.N + 127) / 128) +
+                            (long long)((a.shared_M + 31) / 32) * ((a.shared.N + 127) / 128);
+    if (nt128 < 2LL * kXcds * kSlots) return run_bf16<32, 64, 1, 2>(a, rows, E, s);
+    return run_bf16<32, 128, 1, 4>(a, rows, E, s);
+  }
   dim3 grid;
   GemmArgs b = a;
   grid_of<256, 256>(b, rows, E, grid);
