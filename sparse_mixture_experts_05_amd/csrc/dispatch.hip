@@ -8,7 +8,8 @@
 // is unpadded: expert e owns rows [offsets[e], offsets[e+1]), filled in
 // token order.
 //
-// Three launches, all deterministic (no order-dependent atomics):
+// Three launches (two when T <= 256: one block counts its own histogram),
+// all deterministic (no order-dependent atomics):
 //   hist    - one workgroup per 256-token block: LDS-privatised histogram,
 //             written expert-major as blk[e * nb + b].
 //   rank    - one workgroup per block: every workgroup reads the whole
@@ -64,19 +65,32 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int b = blockIdx.x;
 
-  // Totals over all blocks and this block's prefix over earlier blocks.
+  // Per-wave counts of this block (order-free integer adds).
+  for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
+  __syncthreads();
+  const int tw0 = b * kBlockTokens + wave * 64;  // first token of this wave
+  const int a0 = min(tw0, T) * k, a1 = min(tw0 + 64, T) * k;
+  for (int a = a0 + lane; a < a1; a += 64) atomicAdd(&wcnt[wave][expert_of(idx, a, E)], 1);
+  __syncthreads();
+
+  // Totals over all blocks and this block's prefix over earlier blocks. A
+  // single block (nb == 1, launched without the histogram pass) has them in
+  // its own wave counts.
   int total = 0, before = 0;
   if (tid < E) {
-    const int32_t* row = blk + (size_t)tid * nb;
-    for (int i = 0; i < nb; ++i) {
-      const int c = row[i];
-      total += c;
-      if (i < b) before += c;
+    if (nb == 1) {
+      total = wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
+    } else {
+      const int32_t* row = blk + (size_t)tid * nb;
+      for (int i = 0; i < nb; ++i) {
+        const int c = row[i];
+        total += c;
+        if (i < b) before += c;
+      }
     }
   }
   const int kept = cap < 0 ? total : min(total, cap);
   tot[tid] = tid < E ? kept : 0;
-  for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
   __syncthreads();
   // Exclusive scan of the kept totals over experts (Hillis-Steele on 256 entries).
   for (int d = 1; d < 256; d <<= 1) {
@@ -93,11 +107,6 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     if (tid == E - 1) offsets[E] = excl + kept;
   }
 
-  // Per-wave counts of this block (order-free integer adds).
-  const int tw0 = b * kBlockTokens + wave * 64;  // first token of this wave
-  const int a0 = min(tw0, T) * k, a1 = min(tw0 + 64, T) * k;
-  for (int a = a0 + lane; a < a1; a += 64) atomicAdd(&wcnt[wave][expert_of(idx, a, E)], 1);
-  __syncthreads();
   if (tid < E) {
     int base = before;  // rank of this block's first assignment within the expert
     for (int w = 0; w < 4; ++w) {
@@ -185,9 +194,12 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H,
                            int32_t* inv, void* xs, void* ws, hipStream_t s) {
   const int nb = dispatch_blocks(T);
   int32_t* blk = static_cast<int32_t*>(ws);
-  hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, blk);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err;
+  if (nb > 1) {  // one block (T <= 256) counts its own histogram in the rank kernel
+    hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, blk);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, cap,
                      blk, counts, offsets, perm, inv);
   err = hipGetLastError();
