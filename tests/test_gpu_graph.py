@@ -69,3 +69,28 @@ def test_graph_with_bias_feedback_matches_eager_loop():
         assert np.array_equal(to_host(b_graph), to_host(b_eager)), rep
         moved = max(moved, int((to_host(b_graph) != 0).sum()))
     assert moved > 0
+
+
+def test_graph_with_capacity_dropping_matches_eager():
+    """The captured layer with moe_dispatch_capped (capacity int(T*k/E*cf)): every
+    replay equals the eager capped layer bit for bit, dropped assignments included."""
+    cfg = get_config("decode@T64")
+    L = make_layer(cfg)
+    d = {k: to_dev(v) for k, v in L.items()}
+    cap = moe.moe_capacity(cfg.T, cfg.k, cfg.E, cfg.cf)
+    print(f"\n[gpu] graph with capacity decode@T64 cap={cap}", flush=True)
+    g = moe.MoELayerGraph(d["wg"], d["bias"], d["w1"], d["w2"], cfg.k, cfg.T, ws1=d["ws1"],
+                          ws2=d["ws2"], capacity_factor=cfg.cf, drop=True)
+    dropped = 0
+    for rep in range(3):
+        xr = to_dev(redraw_rows(cfg, np.arange(cfg.T), 300 + rep))
+        out_g = to_host(g.run(xr).clone())
+        inv_g = to_host(g.dsp["inv"].clone())
+        torch.cuda.synchronize()
+        r = moe.moe_layer_forward(xr, d["wg"], d["bias"], d["w1"], d["w2"], cfg.k, ws1=d["ws1"],
+                                  ws2=d["ws2"], capacity=cap)
+        torch.cuda.synchronize()
+        assert np.array_equal(inv_g, to_host(r["inv"])), rep
+        assert np.array_equal(out_g, to_host(r["out"])), rep
+        dropped = max(dropped, int((inv_g < 0).sum()))
+    assert dropped > 0
