@@ -70,19 +70,29 @@ def algorithmic_work(cfg, counts=None, kept=None):
                 ffn_weight_bytes=ffn_bytes, combine_bytes=combine)
 
 
+def code_sha256(path):
+    """SHA-256 of a source file's code: // comments, trailing blanks and empty
+    lines removed, so a comment edit does not count as a kernel change."""
+    lines = []
+    for line in open(path, encoding="utf-8").read().splitlines():
+        line = re.sub(r"//.*", "", line).rstrip()
+        if line:
+            lines.append(line)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
+
+
 def read_traffic():
     """HBM bytes per launch of the dominant kernel from the committed PMC summary,
-    or None if missing or if the kernel source changed since it was taken."""
+    or None if missing or if the kernel code changed since it was taken."""
     try:
         text = open(PMC_SUMMARY).read()
     except OSError:
         return None
-    m_src = re.search(r"source_sha256:\s*([0-9a-f]{64})", text)
+    m_src = re.search(r"code_sha256:\s*([0-9a-f]{64})", text)
     m_b = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
     if not (m_src and m_b):
         return None
-    cur = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
-    if cur != m_src.group(1):
+    if code_sha256(GEMM_SOURCE) != m_src.group(1):
         return None
     return float(m_b.group(1))
 

@@ -10,8 +10,8 @@
 // (a gather, so every output row is written exactly once: no atomics, and a
 // fixed summation order j = 0..k-1, then the shared row). An assignment that
 // a capacity dropped (inv < 0) is skipped; the other weights are kept as they
-// are (no renormalisation). 16-byte loads and
-// stores; fp32 accumulation in registers.
+// are (no renormalisation). 16-byte loads and stores; fp32 accumulation in
+// registers.
 #include "common.hpp"
 #include "kernels.hpp"
 

@@ -10,17 +10,22 @@
 //   down: ys[p, :] = h[p, :] . W2[e]^T           N = H,  K = F
 // Each launch also carries the shared expert as one more group (x -> hs -> ysh).
 //
-// Tiles: workgroup g covers rows [row0, row0+BM) of one expert segment and
+// Tiles: a workgroup covers rows [row0, row0+BM) of one expert segment and
 // columns [n0, n0+BN). The expert of a tile is looked up on the device from
 // offsets (per-expert tile counts, LDS scan), so the host never reads the
 // routing. The grid is sized for the worst case (sum over experts of
-// ceil(count/BM) <= rows/BM + E); surplus workgroups exit at once.
+// ceil(count/BM) <= rows/BM + min(E, rows)); surplus workgroups exit at once.
 //
-// bf16 path: v_mfma_f32_32x32x16_bf16, 4 waves in a WM x WN grid, operand
-// tiles of BK = 64 staged in LDS, double buffered (global loads of step k+1
-// in flight while step k runs on the matrix cores), 16-byte chunks XOR
-// swizzled by row so fragment reads are bank-conflict free. Rows past the
-// segment end are clamped on load and masked on store.
+// Three bf16 kernels, all v_mfma_f32_32x32x16_bf16 with fp32 accumulation and
+// operands copied global -> LDS by global_load_lds (8 rows of 128 contiguous
+// bytes per instruction), 16-byte chunks XOR-swizzled by row so fragment
+// reads are bank-conflict free; rows past the segment end are clamped on load
+// and masked on store:
+//   gemm_bf16_big_kernel   256x256 tiles, 8 waves, two LDS stages, blocked
+//                          XCD-aware tile order, split K in the last round of
+//                          long-K launches (gemm_tail_reduce_kernel sums it);
+//   gemm_bf16_kernel       32x128 or 32x64 tiles for few rows per expert
+//                          (decode): weight streaming through a 3-stage ring.
 // fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
 #include <algorithm>
 #include <type_traits>
@@ -514,18 +519,10 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
 }
 
 // ----------------------------------------------------------------- bf16 MFMA, large tiles
-//
-// BM x BN tile (128 or 256 each), 4 waves in 2 x 2, each wave a (BM/2) x (BN/2)
-// block of 32x32x16 MFMAs. Operand tiles go straight from global memory into
-// LDS (global_load_lds_dwordx4: lane i of an instruction fills the 16-byte
-// slot i after the wave-uniform LDS base), two stages: the loads of k-step
-// kt+1 are in flight while k-step kt runs. A row of a staged tile is 64 bf16
-// = 8 chunks of 16 bytes; chunk c of row r sits in slot c ^ (r & 7), so the
-// lane that fills slot p of row r loads chunk p ^ (r & 7), and fragment
-// reads (32 consecutive rows, one chunk column) hit distinct banks.
 
 // Large-tile kernel: BM x BN tile, NW waves in a 2 x (NW/2) grid, each wave a
-// (BM/2) x (BN/(NW/2)) block of 32x32x16 MFMAs. Two LDS stages of BK = 64.
+// (BM/2) x (BN/(NW/2)) block of 32x32x16 MFMAs. Two LDS stages of BK = 64; a
+// row of a staged tile is 64 bf16 = 8 chunks of 16 bytes.
 // Fragment registers are double buffered across the four 16-deep k slices of
 // a stage, and the one barrier per stage sits where every wave already holds
 // the old stage's last fragments in registers: after it the old stage is

@@ -13,10 +13,13 @@
 //   phase 1: scores [BT x E] into LDS. bf16: MFMA 16x16x32 tiles (tokens x
 //            experts, K = H), fp32 accumulation, operands staged in LDS by
 //            coalesced global -> LDS copies. fp32: plain dot products.
-//   phase 2: one wavefront per token; every lane holds up to 4 scores
-//            (E <= 256); k rounds of a wave-wide arg-max done in registers
-//            with DPP (quad_perm, row mirrors) and ds_swizzle, lanes 0/32
-//            merged with readlane. Ties go to the lower expert id.
+//   phase 2: the scores plus the bias go to an LDS tile; G = 256/BT lanes
+//            per token each keep a sorted top-k list of 64-bit (score, id)
+//            keys over a strided subset of the experts, merged across the G
+//            lanes by bitonic merges over DPP / ds_swizzle / bpermute
+//            exchanges. Ties go to the lower expert id.
+// Few tokens (bf16, T < 2048) take two launches: partial score tiles over K
+// slices into the workspace, then a sum in slice order and the top-k.
 #include "common.hpp"
 #include "kernels.hpp"
 
