@@ -15,7 +15,9 @@ seeded generator. Prints one JSON line:
   roofline     the dominant kernel, the bf16 MFMA grouped GEMM (launched twice
                per step: up and down projections, 2*rows*H*F flops each),
                against the dense bf16 MFMA peak of 2500 TFLOP/s
-  kernels      per-call average ms and the achieved fraction of its roofline
+  kernels      per-call average ms (p10 / median / p90 too) and the achieved
+               fraction of its roofline
+With --flush every step starts from cold caches (a 1 GiB write first).
   cpu_baseline the float64 CPU oracle on a bounded sample of the same workload
 """
 from __future__ import annotations
@@ -130,6 +132,9 @@ def main():
     ap.add_argument("--drop", action="store_true",
                     help="enforce the expert capacity int(T*k/E*cf): dispatch drops the "
                          "assignments past it (a variant, not the headline layer)")
+    ap.add_argument("--flush", action="store_true",
+                    help="cold caches: write a 1 GiB buffer before every step (outside the "
+                         "per-call events); value then comes from the event span of each step")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain 512 MiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
@@ -227,9 +232,12 @@ def main():
             graph.graph.replay()
         torch.cuda.synchronize()
     print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flush else None
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.fill_(s & 0xFF)  # a fill kernel (no memset): > MALL + all L2s
         if args.graph:
             graph.graph.replay()
         else:
@@ -240,13 +248,20 @@ def main():
         dsp = graph.dsp
 
     names = ["route", "dispatch", "expert_ffn", "combine", "load_stats"]
-    per = {n: float(np.mean([events[s][i].elapsed_time(events[s][i + 1])
-                             for s in range(args.steps)])) for i, n in enumerate(names)}
+    samples = {n: np.array([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)])
+               for i, n in enumerate(names)}
+    per = {n: float(v.mean()) for n, v in samples.items()}
+    layer_ms = np.array([events[s][0].elapsed_time(events[s][5]) for s in range(args.steps)])
     counts = dsp["counts"].cpu().numpy()
     kept = np.diff(dsp["offsets"].cpu().numpy()) if args.drop else None
     work = algorithmic_work(cfg, counts, kept)
-    ms_step = elapsed * 1e3 / args.steps
-    value = T * args.steps / elapsed
+    if args.flush and not args.graph:
+        # the flush sits outside the per-call events: time the layer itself
+        ms_step = float(layer_ms.mean())
+        value = T / (ms_step * 1e-3)
+    else:
+        ms_step = elapsed * 1e3 / args.steps
+        value = T * args.steps / elapsed
 
     ffn_ms = per["expert_ffn"]
     bf16 = cfg.dtype == "bf16"
@@ -267,6 +282,9 @@ def main():
     }
     for n in ["route", "dispatch", "combine"]:
         kernels[n]["hbm_frac"] = kernels[n]["GB/s"] / HBM_PEAK_GBS
+    for n in names:
+        p10, p50, p90 = np.percentile(samples[n], [10, 50, 90])
+        kernels[n].update(p10_ms=float(p10), median_ms=float(p50), p90_ms=float(p90))
     result = {
         "metric": "MoE layer tokens/sec at 1 GPU + MFMA util % (FFN) + HBM GB/s (route/dispatch)",
         "value": value,
@@ -284,7 +302,8 @@ def main():
                    "d_ff": F, "shared_d_ff": Fs, "routing_bias_amplitude": cfg.bias_amp,
                    "capacity_factor": cfg.cf, "parallelism": "single GPU",
                    "capacity_dropping": bool(args.drop),
-                   "launch": "hip graph replay" if args.graph else "eager"},
+                   "launch": "hip graph replay" if args.graph else "eager",
+                   "caches": "flushed before every step" if args.flush else "warm"},
         "roofline": {"bound": "mfma", "kernel": DOMINANT_KERNEL, "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic},
