@@ -34,7 +34,9 @@
  *     call directly. Calls keep no global state and are re-entrant.
  *   - Return value: MOE_OK (0) or a negative moe_status. Arguments are
  *     validated on the host before any HIP call; on error nothing is
- *     enqueued. A failed launch returns MOE_ERR_HIP.
+ *     enqueued. A failed launch returns MOE_ERR_HIP. A row or weight tensor
+ *     (x, wg, xs, w1, w2, ws1, ws2, ys, ysh, out) or workspace whose address
+ *     is not a multiple of 16 returns MOE_ERR_INVALID_ARG.
  *   - dtype: MOE_F32 (fp32 activations, weights, arithmetic) or MOE_BF16
  *     (bf16 activations and weights, fp32 accumulation, bf16 results rounded
  *     to nearest even).
@@ -59,7 +61,7 @@ typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
 
 typedef enum {
   MOE_OK = 0,
-  MOE_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, bad enum */
+  MOE_ERR_INVALID_ARG = -1, /* null or misaligned pointer, non-positive size, bad enum */
   MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported range */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query */
   MOE_ERR_HIP = -4          /* a HIP launch failed */

@@ -28,6 +28,9 @@ int check_tokens(int T, int H, int E, int k) {
 
 int from_hip(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Rows and weights are read and written with 16-byte vector accesses.
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
 
 }  // namespace
@@ -37,7 +40,7 @@ extern "C" {
 const char* moe_status_string(int status) {
   switch (status) {
     case MOE_OK: return "ok";
-    case MOE_ERR_INVALID_ARG: return "invalid argument (null pointer, non-positive size or bad dtype)";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (null or misaligned pointer, non-positive size or bad dtype)";
     case MOE_ERR_UNSUPPORTED: return "unsupported shape (needs 1<=E<=256, 1<=k<=min(E,8), H%64==0, F%64==0, T*k<2^31)";
     case MOE_ERR_WORKSPACE: return "workspace missing or smaller than the size query returned";
     case MOE_ERR_HIP: return "HIP launch failed";
@@ -54,6 +57,7 @@ int moe_route(const void* x, const void* wg, const float* bias, int T, int H, in
               int dtype, int32_t* topk_idx, float* topk_w, float* prob_mean, void* ws,
               size_t ws_bytes, void* stream) {
   if (!x || !wg || !topk_idx || !topk_w || !dtype_ok(dtype)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(wg) || (ws && !aligned16(ws))) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
   const size_t need = moe::route_ws_bytes(T, H, E, dtype == MOE_BF16, prob_mean != nullptr);
@@ -72,6 +76,7 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
                  void* ws, size_t ws_bytes, void* stream) {
   if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !xs || !dtype_ok(dtype))
     return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(xs)) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
   if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
@@ -83,7 +88,7 @@ int moe_dispatch_capped(const int32_t* topk_idx, const void* x, int T, int H, in
                         int capacity, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv, void* xs, void* ws, size_t ws_bytes, void* stream) {
   if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !xs || !dtype_ok(dtype) ||
-      capacity < 0)
+      capacity < 0 || !aligned16(x) || !aligned16(xs))
     return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
@@ -110,9 +115,13 @@ int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int 
                    const void* ws2, int T, int Fs, int dtype, void* ys, void* ysh, void* ws,
                    size_t ws_bytes, void* stream) {
   if (!xs || !offsets || !w1 || !w2 || !ys) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(xs) || !aligned16(w1) || !aligned16(w2) || !aligned16(ys)) return MOE_ERR_INVALID_ARG;
   const int st = check_ffn(rows, T, H, E, F, Fs, dtype);
   if (st != MOE_OK) return st;
   if (Fs > 0 && (!x || !ws1 || !ws2 || !ysh)) return MOE_ERR_INVALID_ARG;
+  if (Fs > 0 && (!aligned16(x) || !aligned16(ws1) || !aligned16(ws2) || !aligned16(ysh)))
+    return MOE_ERR_INVALID_ARG;
+  if (ws && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, E, F, Fs, dtype == MOE_BF16))
     return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_expert_ffn(xs, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T, Fs,
@@ -123,6 +132,7 @@ int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int 
 int moe_combine(const void* ys, const int32_t* inv, const float* topk_w, const void* ysh, int T,
                 int H, int k, int dtype, void* out, void* stream) {
   if (!ys || !inv || !topk_w || !out || !dtype_ok(dtype)) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(ys) || !aligned16(out) || (ysh && !aligned16(ysh))) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, kMaxTopK, k);
   if (st != MOE_OK) return st;
   return from_hip(moe::launch_combine(ys, inv, topk_w, ysh, T, H, k, dtype == MOE_BF16, out,

@@ -83,6 +83,23 @@ def test_route_workspace():
     assert L.moe_route_workspace_bytes(16, 4096, 300, 8, 1) == 0
 
 
+def test_misaligned_rows_are_rejected():
+    """Rows and weights are accessed 16 bytes at a time: an address that is not a
+    multiple of 16 is an invalid argument, caught before any launch."""
+    L = moe.lib()
+    ODD = ctypes.c_void_p(0x1004)
+    assert L.moe_route(ODD, FAKE, None, 4096, 4096, 8, 2, 1, FAKE, FAKE, None, None, 0, None) == -1
+    assert L.moe_route(FAKE, ODD, None, 4096, 4096, 8, 2, 1, FAKE, FAKE, None, None, 0, None) == -1
+    need = L.moe_dispatch_workspace_bytes(4096, 128, 8)
+    args = [FAKE, FAKE, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE, ODD]  # xs
+    assert L.moe_dispatch(*args, FAKE, need, None) == -1
+    rows, T, H, E, F, Fs = 8192, 4096, 4096, 8, 14336, 0
+    fneed = L.moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, 1)
+    base = [FAKE, FAKE, rows, E, H, F, ODD, FAKE, None, None, None, T, Fs, 1, FAKE, None]  # w1
+    assert L.moe_expert_ffn(*base, FAKE, fneed, None) == -1
+    assert L.moe_combine(FAKE, FAKE, FAKE, None, 16, 64, 2, 1, ODD, None) == -1
+
+
 def test_bias_update_validation():
     L = moe.lib()
     f = ctypes.c_float
