@@ -18,8 +18,9 @@
 //            keys over a strided subset of the experts, merged across the G
 //            lanes by bitonic merges over DPP / ds_swizzle / bpermute
 //            exchanges. Ties go to the lower expert id.
-// Few tokens (bf16, T < 2048) take two launches: partial score tiles over K
-// slices into the workspace, then a sum in slice order and the top-k.
+// Few tokens (bf16, T < 2048, or T < 3072 when E > 128) take two launches:
+// partial score tiles over K slices into the workspace, then a sum in slice
+// order and the top-k.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -509,7 +510,11 @@ int route_kslices(int T, int H, int E) {
   return ks;
 }
 
-bool route_two_phase(int T, bool bf16) { return bf16 && T < 2048; }
+// The two-launch path reads x once per K slice and expert tile and writes T x E
+// partial scores per slice, so its time grows faster with T than the one-launch
+// path's; measured crossover (graph replay, H = 4096, k = 8): T near 2048 up to
+// E = 128, near 3072 for E = 256 (each one-launch workgroup re-reads all of Wg).
+bool route_two_phase(int T, int E, bool bf16) { return bf16 && T < (E > 128 ? 3072 : 2048); }
 
 template <int BT, int EP>
 hipError_t launch_bf16(const void* x, const void* wg, const float* bias, int T, int H, int E,
@@ -536,8 +541,8 @@ hipError_t launch_bf16_bt(const void* x, const void* wg, const float* bias, int 
 int bf16_tokens_per_block(int T) { return T >= 64 * 256 ? 64 : T >= 32 * 256 ? 32 : 16; }
 
 // Workgroups of the launch that runs the top-k (one partial probability row each).
-int topk_blocks(int T, bool bf16) {
-  if (route_two_phase(T, bf16)) return (T + 3) / 4;
+int topk_blocks(int T, int E, bool bf16) {
+  if (route_two_phase(T, E, bf16)) return (T + 3) / 4;
   const int bt = bf16 ? bf16_tokens_per_block(T) : 16;
   return (T + bt - 1) / bt;
 }
@@ -545,7 +550,7 @@ int topk_blocks(int T, bool bf16) {
 size_t align256(size_t b) { return (b + 255) & ~size_t(255); }
 
 size_t scores_ws_bytes(int T, int H, int E, bool bf16) {
-  if (!route_two_phase(T, bf16)) return 0;
+  if (!route_two_phase(T, E, bf16)) return 0;
   return align256((size_t)route_kslices(T, H, E) * T * E * sizeof(float));
 }
 
@@ -553,7 +558,7 @@ size_t scores_ws_bytes(int T, int H, int E, bool bf16) {
 
 size_t route_ws_bytes(int T, int H, int E, bool bf16, bool prob) {
   size_t b = scores_ws_bytes(T, H, E, bf16);
-  if (prob) b += align256((size_t)topk_blocks(T, bf16) * E * sizeof(float));
+  if (prob) b += align256((size_t)topk_blocks(T, E, bf16) * E * sizeof(float));
   return b;
 }
 
@@ -565,7 +570,7 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
                   ? nullptr
                   : reinterpret_cast<float*>(static_cast<char*>(ws) + scores_ws_bytes(T, H, E, bf16));
   hipError_t err = hipSuccess;
-  if (route_two_phase(T, bf16)) {
+  if (route_two_phase(T, E, bf16)) {
     const int nks = route_kslices(T, H, E);
     const dim3 grid((T + kPartBT - 1) / kPartBT, (E + kPartEP - 1) / kPartEP, nks);
     hipLaunchKernelGGL(route_partial_kernel, grid, dim3(kThreads), 0, s,
@@ -590,7 +595,7 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
     }
   }
   if (err != hipSuccess || prob_mean == nullptr) return err;
-  hipLaunchKernelGGL(prob_mean_kernel, dim3(1), dim3(kThreads), 0, s, pp, topk_blocks(T, bf16), T,
+  hipLaunchKernelGGL(prob_mean_kernel, dim3(1), dim3(kThreads), 0, s, pp, topk_blocks(T, E, bf16), T,
                      E, prob_mean);
   return hipGetLastError();
 }

@@ -81,6 +81,12 @@ def test_route_workspace():
     assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE,
                        256 * 128 * 4 - 1, None) == -3
     assert L.moe_route_workspace_bytes(16, 4096, 300, 8, 1) == 0
+    # with E > 128 the two-launch path is kept up to T = 3071
+    # (partial scores on top of the probability rows, 16 tokens per row beyond it)
+    rows16 = lambda T, E: -(-(-(-T // 16) * E * 4) // 256) * 256
+    assert L.moe_route_workspace_bytes(2500, 4096, 256, 8, 1) > 2500 * 256 * 4
+    assert L.moe_route_workspace_bytes(2500, 4096, 128, 8, 1) == rows16(2500, 128)
+    assert L.moe_route_workspace_bytes(3072, 4096, 256, 8, 1) == rows16(3072, 256)
 
 
 def test_misaligned_rows_are_rejected():
