@@ -12,9 +12,11 @@
 //
 // Tiles: a workgroup covers rows [row0, row0+BM) of one expert segment and
 // columns [n0, n0+BN). The expert of a tile is looked up on the device from
-// offsets (per-expert tile counts, LDS scan), so the host never reads the
-// routing. The grid is sized for the worst case (sum over experts of
-// ceil(count/BM) <= rows/BM + min(E, rows)); surplus workgroups exit at once.
+// offsets, so the host never reads the routing: the small-tile kernels scan
+// per-expert tile counts in LDS; the big-tile launches read a tile table that
+// one planning launch (big_plan_kernel) writes for both GEMMs. The grid is
+// sized for the worst case (sum over experts of ceil(count/BM) <= rows/BM +
+// min(E, rows)); surplus workgroups exit at once.
 //
 // Three bf16 kernels, all v_mfma_f32_32x32x16_bf16 with fp32 accumulation and
 // operands copied global -> LDS by global_load_lds (8 rows of 128 contiguous
@@ -54,6 +56,8 @@ struct GemmArgs {
   int shared_M;      // 0 = no shared group
   int gelu;
   float* part;       // split-K partial tiles of the last round (big kernel), or null
+  const int4* table; // big kernel: tile descriptors, 2 per slot (launch slots, then reduce slots)
+  int slots;         // big kernel: workgroups of the launch (= reduce table start)
 };
 
 struct Tile {
@@ -171,7 +175,7 @@ constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
 struct SchedLds {
   int pf[257], pp[257];    // inclusive scans: full tiles by group, partial tiles by rank
   int prow[257], sgrp[257];  // partial-tile rows by group; group of each rank
-  int sel[4];              // the selected tile, broadcast
+  int goff[257], gcnt[257];  // first row and rows of each group
 };
 
 struct BigSched {
@@ -213,8 +217,16 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
     xfull = (a.shared_M / BM) * nts;
     xpart = (a.shared_M % BM) ? nts : 0;
   }
-  if (act) L.prow[tid] = tid < ng ? cnt % BM : 0;
-  if (tid == 255) L.prow[256] = ng == 257 ? a.shared_M % BM : 0;
+  if (act) {
+    L.prow[tid] = tid < ng ? cnt % BM : 0;
+    L.goff[tid] = off;
+    L.gcnt[tid] = cnt;
+  }
+  if (tid == 255) {
+    L.prow[256] = ng == 257 ? a.shared_M % BM : 0;
+    L.goff[256] = 0;
+    L.gcnt[256] = ng == 257 ? a.shared_M : 0;
+  }
   __syncthreads();
   // rank of each group with a partial tile: descending rows, ties by id
   auto rank_of = [&](int grp) {
@@ -243,7 +255,6 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
     L.sgrp[xrank] = 256;
   }
   if (act) L.pf[tid] = full;
-  if (tid == 0) L.sel[0] = -1;
   __syncthreads();
   if (tid == 255) xpart = L.pp[256];  // the scan below folds entry 256 in separately
   __syncthreads();
@@ -285,26 +296,16 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
   return S;
 }
 
-// Tile of logical slot `slot` on XCD x. mode 0: the tile (or K slice of a
-// split tail tile) to compute; mode 1: the split tail tile number `slot` to
-// reduce. Returns false if the slot holds none.
+// Tile of logical slot `slot` on XCD x, resolved by one thread from the
+// schedule tables. mode 0: the tile (or K slice of a split tail tile) to
+// compute; mode 1: the split tail tile number `slot` to reduce. Returns false
+// if the slot holds none.
 template <int BM, int BN, int GN>
-__device__ bool big_tile(const GemmArgs& a, const BigSched& S, SchedLds& L, int x, int slot,
-                         int mode, Tile& t) {
-  const int tid = threadIdx.x;
-  const bool act = tid < 256;
+__device__ bool resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLds& L, int x,
+                             int slot, int mode, Tile& t) {
   const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
   const int ntr = (a.routed.N + BN - 1) / BN;
   const int nts = (a.shared.N + BN - 1) / BN;
-  auto rows_of = [&](int grp, int& off, int& cnt) {
-    if (grp < a.E) {
-      off = min(max(a.offsets[grp], 0), a.rows);
-      cnt = min(max(a.offsets[grp + 1], off), a.rows) - off;
-    } else {
-      off = 0;
-      cnt = a.shared_M;
-    }
-  };
   const int F = S.F, P = S.P, CF = S.CF, CP = S.CP, R = S.R, tail = S.tail, spl = S.spl;
   int ks = 0, unit0 = -1;
   if (mode == 0) {
@@ -325,72 +326,88 @@ __device__ bool big_tile(const GemmArgs& a, const BigSched& S, SchedLds& L, int 
   const bool is_full = slot < CF;
   const int q = is_full ? x * CF + slot : (slot - CF) * kXcds + x;
   if (q >= (is_full ? F : P)) return false;
-  auto check_full = [&](int grp, int f_incl, int f_excl) {
-    int o, c;
-    rows_of(grp, o, c);
+  // the entry of the inclusive scan (by group for full tiles, by rank for
+  // partial ones) whose range holds q: the first one above q
+  const int* scan = is_full ? L.pf : L.pp;
+  int lo = 0, hi = ng - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (scan[mid] > q) hi = mid;
+    else lo = mid + 1;
+  }
+  const int excl = lo ? scan[lo - 1] : 0;
+  const int grp = is_full ? lo : L.sgrp[lo];
+  const int o = L.goff[grp], c = L.gcnt[grp];
+  const int mt_g = c / BM;  // full row tiles of the group
+  if (is_full) {
     const int nt_g = grp < a.E ? ntr : nts;
-    if (is_full && q >= f_excl && q < f_incl) {
-      const int mt_g = c / BM;  // full row tiles
-      const int local = q - f_excl;
-      const int blk = local / (mt_g * GN);
-      const int w = min(GN, nt_g - blk * GN);
-      const int li = local - blk * mt_g * GN;
-      const int mt = li / w, nt = blk * GN + li % w;
-      L.sel[0] = grp;
-      L.sel[1] = o + mt * BM;
-      L.sel[2] = BM;
-      L.sel[3] = nt * BN;
-    }
-  };
-  auto check_part = [&](int grp, int p_incl, int p_excl) {
-    if (!is_full && q >= p_excl && q < p_incl) {
-      int o, c;
-      rows_of(grp, o, c);
-      const int mt = c / BM;  // the partial row tile
-      L.sel[0] = grp;
-      L.sel[1] = o + mt * BM;
-      L.sel[2] = c - mt * BM;
-      L.sel[3] = (q - p_excl) * BN;
-    }
-  };
-  // full tiles by group id; partial tiles by rank (sgrp maps rank -> group)
-  __syncthreads();  // earlier readers of sel are done
-  if (tid == 0) L.sel[0] = -1;
-  __syncthreads();
-  if (act && tid < ng) {
-    int o_, c_;
-    rows_of(tid, o_, c_);
-    const int full = (c_ / BM) * (tid < a.E ? ntr : nts);
-    check_full(tid, L.pf[tid], L.pf[tid] - full);
-    const int pcount = L.pp[tid] - (tid ? L.pp[tid - 1] : 0);
-    check_part(L.sgrp[tid], L.pp[tid], L.pp[tid] - pcount);
+    const int local = q - excl;
+    const int blk = local / (mt_g * GN);
+    const int w = min(GN, nt_g - blk * GN);
+    const int li = local - blk * mt_g * GN;
+    t.row0 = o + (li / w) * BM;
+    t.M = BM;
+    t.n0 = (blk * GN + li % w) * BN;
+  } else {
+    t.row0 = o + mt_g * BM;  // the partial row tile
+    t.M = c - mt_g * BM;
+    t.n0 = (q - excl) * BN;
   }
-  if (tid == 255 && ng == 257) {
-    check_full(256, L.pf[256], L.pf[255]);
-    check_part(L.sgrp[256], L.pp[256], L.pp[255]);
-  }
-  __syncthreads();
-  const int grp = L.sel[0];
-  if (grp < 0) return false;
   t.group = grp < a.E ? 0 : 1;
   t.e = grp < a.E ? grp : 0;
-  t.row0 = L.sel[1];
-  t.M = L.sel[2];
-  t.n0 = L.sel[3];
   t.spl = unit0 >= 0 ? spl : 1;
   t.ks = ks;
   t.unit0 = unit0;
   return true;
 }
 
-// The tile workgroup gid (default blockIdx.x) runs: schedule, then slot
-// gid / 8 on XCD gid % 8.
+// Split tail tiles a reduce launch can hold: half a round of every XCD.
+constexpr int kReduceSlots = kXcds * kSlots / 2;
+
+// Writes the tile table of one big-tile launch: two int4 per workgroup slot
+// ({group or -1, expert, row0, M}, {n0, spl, ks, unit0}), slots [0, a.slots)
+// for the GEMM launch (workgroup g: slot g / 8 on XCD g % 8), then
+// kReduceSlots for its split-K reduce. Every workgroup computes the same
+// schedule (group ranks and scans, from offsets), then each thread resolves
+// one slot: the GEMM workgroups read one entry instead of each redoing the
+// schedule.
 template <int BM, int BN, int GN>
-__device__ bool find_tile_blocked(const GemmArgs& a, Tile& t, int mode = 0, int gid = -1) {
-  __shared__ SchedLds L;
+__device__ void plan_launch(const GemmArgs& a, int4* table, SchedLds& L) {
   const BigSched S = big_schedule<BM, BN>(a, L);
-  const int g = gid >= 0 ? gid : (int)blockIdx.x;
-  return big_tile<BM, BN, GN>(a, S, L, g % kXcds, g / kXcds, mode, t);
+  const int i = blockIdx.x * kThreads + threadIdx.x;
+  if (i >= a.slots + kReduceSlots) return;
+  const int mode = i < a.slots ? 0 : 1;
+  const int g = mode ? i - a.slots : i;
+  Tile t;
+  const bool ok = resolve_slot<BM, BN, GN>(a, S, L, g % kXcds, g / kXcds, mode, t);
+  table[2 * i] = ok ? make_int4(t.group, t.e, t.row0, t.M) : make_int4(-1, 0, 0, 0);
+  table[2 * i + 1] = ok ? make_int4(t.n0, t.spl, t.ks, t.unit0) : make_int4(0, 1, 0, -1);
+}
+
+// One launch plans both GEMMs of the FFN (blockIdx.y: 0 up, 1 down).
+template <int BM, int BN, int GN>
+__global__ __launch_bounds__(kThreads) void big_plan_kernel(GemmArgs up, GemmArgs down) {
+  __shared__ SchedLds L;
+  if (blockIdx.y == 0)
+    plan_launch<BM, BN, GN>(up, const_cast<int4*>(up.table), L);
+  else
+    plan_launch<BM, BN, GN>(down, const_cast<int4*>(down.table), L);
+}
+
+// The tile of table entry i (written by big_plan_kernel).
+__device__ __forceinline__ bool table_tile(const GemmArgs& a, int i, Tile& t) {
+  const int4 d0 = a.table[2 * i];
+  if (d0.x < 0) return false;
+  const int4 d1 = a.table[2 * i + 1];
+  t.group = d0.x;
+  t.e = d0.y;
+  t.row0 = d0.z;
+  t.M = d0.w;
+  t.n0 = d1.x;
+  t.spl = d1.y;
+  t.ks = d1.z;
+  t.unit0 = d1.w;
+  return true;
 }
 
 // ----------------------------------------------------------------- bf16 MFMA
@@ -543,7 +560,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
   Tile t;
-  if (!find_tile_blocked<BM, BN, 8>(args, t)) return;
+  if (!table_tile(args, blockIdx.x, t)) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N, K = G.K;
   const uint16_t* A = static_cast<const uint16_t*>(G.A) + (size_t)t.row0 * K;
@@ -718,7 +735,7 @@ constexpr int kReduceParts = 8;
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void gemm_tail_reduce_kernel(GemmArgs args) {
   Tile t;
-  if (!find_tile_blocked<BM, BN, 8>(args, t, 1, blockIdx.x / kReduceParts)) return;
+  if (!table_tile(args, args.slots + blockIdx.x / kReduceParts, t)) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N;
   uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
@@ -849,71 +866,111 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     if (nt128 < 2LL * kXcds * kSlots) return run_bf16<32, 64, 1, 2>(a, rows, E, s);
     return run_bf16<32, 128, 1, 4>(a, rows, E, s);
   }
-  dim3 grid;
-  GemmArgs b = a;
-  grid_of<256, 256>(b, rows, E, grid);
-  const bool long_k = b.routed.K >= kSplitMinK && (b.shared_M == 0 || b.shared.K >= kSplitMinK);
-  if (!long_k) b.part = nullptr;
-  // full and partial runs are each rounded up per XCD (at most 2*8 extra
-  // slots); a split last round adds at most one round of kSlots per XCD
-  grid.x = (grid.x + 2 * kXcds + kXcds - 1) / kXcds * kXcds + (b.part ? kXcds * kSlots : 0);
-  hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves>), grid, dim3(kBigWaves * 64), 0, s, b);
+  // big tiles: the table was written by big_plan_kernel
+  hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves>), dim3(a.slots),
+                     dim3(kBigWaves * 64), 0, s, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess || b.part == nullptr) return err;
-  hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>),
-                     dim3(kXcds * kSlots / 2 * kReduceParts), dim3(kThreads), 0, s, b);
+  if (err != hipSuccess || a.part == nullptr) return err;
+  hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>), dim3(kReduceSlots * kReduceParts),
+                     dim3(kThreads), 0, s, a);
   return hipGetLastError();
 }
 
 // The big-tile path (bf16, enough rows per expert) also needs the split-K
-// partial tiles.
+// partial tiles and the tile tables.
 bool big_tiles(int rows, int E, bool bf16) { return bf16 && (long long)rows >= 64LL * E; }
+
+// Workspace layout: h [rows, F] | hs [T, Fs] | big tiles only: split-K
+// partials [kPartTiles, 256, 256] fp32 | tile tables of the up and down launches.
+struct FfnLayout {
+  GemmArgs up, down;
+  size_t h, hs, part, table, bytes;  // byte offsets, total
+  bool big, small_segments;
+};
+
+// Arguments of both launches and the workspace layout; the same function
+// sizes the workspace and launches, so the two always agree.
+FfnLayout ffn_layout(const void* xs, const int32_t* offsets, int rows, int E, int H, int F,
+                     const void* w1, const void* w2, const void* x, const void* ws1,
+                     const void* ws2, int T, int Fs, bool bf16, void* ys, void* ysh, void* ws) {
+  FfnLayout Lo{};
+  const size_t es = bf16 ? 2 : 4;
+  Lo.big = big_tiles(rows, E, bf16);
+  // Few rows per expert on average: decode-like, weight-streaming bound.
+  Lo.small_segments = !Lo.big && bf16;
+  Lo.h = 0;
+  Lo.hs = Lo.h + align256((size_t)rows * F * es);
+  Lo.part = Lo.hs + align256((size_t)T * Fs * es);
+  Lo.table = Lo.part + (Lo.big ? kPartTiles * 256 * 256 * sizeof(float) : 0);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  auto at = [&](size_t off) { return base ? static_cast<void*>(base + off) : nullptr; };
+  const bool shared = Fs > 0;
+
+  GemmArgs& up = Lo.up;
+  up.routed = Group{xs, w1, at(Lo.h), F, H};
+  up.shared = Group{x, ws1, at(Lo.hs), Fs, H};
+  up.offsets = offsets;
+  up.E = E;
+  up.rows = rows;
+  up.shared_M = shared ? T : 0;
+  up.gelu = 1;
+
+  GemmArgs& down = Lo.down;
+  down.routed = Group{at(Lo.h), w2, ys, H, F};
+  down.shared = Group{at(Lo.hs), ws2, ysh, H, Fs};
+  down.offsets = offsets;
+  down.E = E;
+  down.rows = rows;
+  down.shared_M = shared ? T : 0;
+  down.gelu = 0;
+
+  size_t table_bytes = 0;
+  if (Lo.big) {
+    int4* tab = static_cast<int4*>(at(Lo.table));
+    for (GemmArgs* a : {&up, &down}) {
+      // split K only where every group's K is long (see kSplitMinK)
+      const bool long_k = a->routed.K >= kSplitMinK && (a->shared_M == 0 || a->shared.K >= kSplitMinK);
+      a->part = long_k ? static_cast<float*>(at(Lo.part)) : nullptr;
+      // worst-case tiles; full and partial runs are each rounded up per XCD
+      // (at most 2*8 extra slots); a split last round adds at most one round
+      // of kSlots per XCD
+      dim3 grid;
+      grid_of<256, 256>(*a, rows, E, grid);
+      a->slots = (int)((grid.x + 2 * kXcds + kXcds - 1) / kXcds * kXcds) +
+                 (a->part ? kXcds * kSlots : 0);
+      a->table = tab ? tab + table_bytes / sizeof(int4) : nullptr;
+      table_bytes += (size_t)(a->slots + kReduceSlots) * 2 * sizeof(int4);
+    }
+  }
+  Lo.bytes = Lo.table + align256(table_bytes);
+  return Lo;
+}
 
 }  // namespace
 
-size_t ffn_ws_bytes(int rows, int T, int E, int F, int Fs, bool bf16) {
-  const size_t es = bf16 ? 2 : 4;
-  size_t b = align256((size_t)rows * F * es) + align256((size_t)T * Fs * es);
-  if (big_tiles(rows, E, bf16)) b += kPartTiles * 256 * 256 * sizeof(float);
-  return b;
+size_t ffn_ws_bytes(int rows, int T, int E, int H, int F, int Fs, bool bf16) {
+  return ffn_layout(nullptr, nullptr, rows, E, H, F, nullptr, nullptr, nullptr, nullptr, nullptr,
+                    T, Fs, bf16, nullptr, nullptr, nullptr)
+      .bytes;
 }
 
 hipError_t launch_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H,
                              int F, const void* w1, const void* w2, const void* x,
                              const void* ws1, const void* ws2, int T, int Fs, bool bf16,
                              void* ys, void* ysh, void* ws, hipStream_t s) {
-  const size_t es = bf16 ? 2 : 4;
-  uint8_t* h = static_cast<uint8_t*>(ws);
-  uint8_t* hs = h + align256((size_t)rows * F * es);
-  float* part = big_tiles(rows, E, bf16)
-                    ? reinterpret_cast<float*>(hs + align256((size_t)T * Fs * es))
-                    : nullptr;
-  const bool shared = Fs > 0;
-  // Few rows per expert on average: decode-like, weight-streaming bound.
-  const bool small_segments = !big_tiles(rows, E, bf16) && bf16;
-
-  GemmArgs up{};
-  up.routed = Group{xs, w1, h, F, H};
-  up.shared = Group{x, ws1, hs, Fs, H};
-  up.offsets = offsets;
-  up.E = E;
-  up.rows = rows;
-  up.shared_M = shared ? T : 0;
-  up.gelu = 1;
-  up.part = part;
-  hipError_t err = run_gemm(up, rows, E, bf16, small_segments, s);
+  const FfnLayout Lo =
+      ffn_layout(xs, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T, Fs, bf16, ys, ysh, ws);
+  hipError_t err;
+  if (Lo.big) {
+    const int n = std::max(Lo.up.slots, Lo.down.slots) + kReduceSlots;
+    hipLaunchKernelGGL((big_plan_kernel<256, 256, 8>), dim3((n + kThreads - 1) / kThreads, 2),
+                       dim3(kThreads), 0, s, Lo.up, Lo.down);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  err = run_gemm(Lo.up, rows, E, bf16, Lo.small_segments, s);
   if (err != hipSuccess) return err;
-
-  GemmArgs down{};
-  down.routed = Group{h, w2, ys, H, F};
-  down.shared = Group{hs, ws2, ysh, H, Fs};
-  down.offsets = offsets;
-  down.E = E;
-  down.rows = rows;
-  down.shared_M = shared ? T : 0;
-  down.gelu = 0;
-  down.part = part;
-  return run_gemm(down, rows, E, bf16, small_segments, s);
+  return run_gemm(Lo.down, rows, E, bf16, Lo.small_segments, s);
 }
 
 }  // namespace moe

@@ -107,7 +107,7 @@ static int check_ffn(int rows, int T, int H, int E, int F, int Fs, int dtype) {
 
 size_t moe_expert_ffn_workspace_bytes(int rows, int T, int H, int E, int F, int Fs, int dtype) {
   if (check_ffn(rows, T, H, E, F, Fs, dtype) != MOE_OK) return 0;
-  return moe::ffn_ws_bytes(rows, T, E, F, Fs, dtype == MOE_BF16);
+  return moe::ffn_ws_bytes(rows, T, E, H, F, Fs, dtype == MOE_BF16);
 }
 
 int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H, int F,
@@ -122,7 +122,7 @@ int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int 
   if (Fs > 0 && (!aligned16(x) || !aligned16(ws1) || !aligned16(ws2) || !aligned16(ysh)))
     return MOE_ERR_INVALID_ARG;
   if (ws && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
-  if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, E, F, Fs, dtype == MOE_BF16))
+  if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, E, H, F, Fs, dtype == MOE_BF16))
     return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_expert_ffn(xs, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T, Fs,
                                          dtype == MOE_BF16, ys, Fs > 0 ? ysh : nullptr, ws,
