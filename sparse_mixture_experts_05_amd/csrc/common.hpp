@@ -31,6 +31,15 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return f32_to_bf16(a) | (f32_to_bf16(b) << 16);
 }
 
+// The same pair conversion in one instruction (v_cvt_pk_bf16_f32, round to
+// nearest even; NaN stays a quiet NaN of its own sign and payload bits).
+typedef __bf16 bf16x2_hw_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_hw_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t cvt_bf16x2(float a, float b) {
+  const f32x2_hw_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_hw_t));
+}
+
 // GeLU, erf form: 0.5 * a * (1 + erf(a / sqrt(2))). erff is the device library's.
 __device__ __forceinline__ float gelu_erf(float a) {
   return 0.5f * a * (1.0f + erff(a * 0.70710678118654752f));

@@ -544,7 +544,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
 // a stage, and the one barrier per stage sits where every wave already holds
 // the old stage's last fragments in registers: after it the old stage is
 // refilled (k-step kt+2) and the first fragments of the new stage are read.
-template <int BM, int BN, int NW>
+template <int BM, int BN, int NW, bool GELU>
 __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args) {
   constexpr int BK = 64;
   constexpr int ROWB = BK * 2;                  // 128 bytes = 8 chunks of 16
@@ -696,33 +696,57 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
     return;
   }
 
-  // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
-  // (v/4)*8 + (lane/32)*4 + v%4. Lanes 2m and 2m+1 (adjacent columns) swap
-  // one value per row pair with DPP, so each stores a bf16 pair (4 bytes):
-  // the even lane row r = R(v), the odd lane row r + 1. All lanes take part
-  // in the swap; only the stores are masked.
-  const bool gelu = args.gelu != 0;
-  const bool odd = lane & 1;
+  // Epilogue through LDS. 32x32 D layout: lane holds column lane%32 and rows
+  // (v/4)*8 + (lane/32)*4 + v%4. Each lane converts its rows (v, v+1) of its
+  // column to a bf16 pair in one instruction; lanes 2m and 2m+1 (adjacent
+  // columns) swap those words with DPP, and a byte permute leaves the even
+  // lane the pair (row R(v), its column and the next) and the odd lane the
+  // same for row R(v) + 1. The pairs go to a [BM x BN] bf16 tile in LDS (the
+  // operand stages are free by then), 512-byte rows whose 16-dword groups are
+  // XOR-swizzled by row bits 0 and 2: the four rows one write instruction
+  // touches (r, r+1, r+4, r+5) land in four different bank quarters. Those
+  // two row bits are the lane's parity and lane / 32 for every value, so the
+  // swizzled address is a per-lane base plus a constant. Then every wave
+  // stores whole rows, 16 bytes per lane (two 512-byte rows per instruction).
+  static_assert(BM * BN * 2 <= 2 * STAGE && BN == 256, "C tile in LDS: 512-byte rows");
+  constexpr int CROWB = BN * 2;
+  const int odd = lane & 1, hi = lane >> 5;
+  const int cg = odd | (hi << 1);  // == (row & 1) | ((row >> 2) & 1) << 1 for this lane's rows
+  const int rbase = wm * WTM + hi * 4 + odd;
+  int cbase[SN];
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+    cbase[j] = rbase * CROWB + (((wn * WTN + j * 32) / 32) ^ cg) * 64 + ((lane & 31) >> 1) * 4;
+  // even lane: low halves of (own, partner); odd lane: high halves of (partner, own)
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  lds_barrier();  // every wave has read the last stage
 #pragma unroll
   for (int i = 0; i < SM; ++i)
 #pragma unroll
-    for (int j = 0; j < SN; ++j) {
-      const int col = wn * WTN + j * 32 + (lane & 31);  // this lane's column
-      const int pcol = col & ~1;                        // first column of the stored pair
-      const bool cok = pcol < nvalid;                   // N % 64 == 0: pairs are all or nothing
-      float y[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) y[v] = gelu ? gelu_erf_fast(acc[i][j][v]) : acc[i][j][v];
+    for (int j = 0; j < SN; ++j)
 #pragma unroll
       for (int v = 0; v < 16; v += 2) {
-        const float send = odd ? y[v] : y[v + 1];
-        const float recv = __int_as_float(
-            __builtin_amdgcn_update_dpp(0, __float_as_int(send), 0xB1, 0xF, 0xF, false));
-        const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3) + (odd ? 1 : 0);
-        const uint32_t packed = odd ? pack_bf16x2(recv, y[v + 1]) : pack_bf16x2(y[v], recv);
-        if (cok && row < M) *reinterpret_cast<uint32_t*>(C + (size_t)row * N + pcol) = packed;
+        float y0 = acc[i][j][v], y1 = acc[i][j][v + 1];
+        if constexpr (GELU) {
+          y0 = gelu_erf_fast(y0);
+          y1 = gelu_erf_fast(y1);
+        }
+        const uint32_t own = cvt_bf16x2(y0, y1);  // (row R(v), row R(v) + 1) of this column
+        const uint32_t partner = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xF, 0xF, false);
+        const uint32_t pair = __builtin_amdgcn_perm(partner, own, sel);
+        const int roff = (i * 32 + (v >> 2) * 8 + (v & 3)) * CROWB;
+        *reinterpret_cast<uint32_t*>(smem + cbase[j] + roff) = pair;
       }
-    }
+  lds_barrier();
+  const int cl = lane & 31;
+  const bool cok = cl * 8 < nvalid;  // N % 64 == 0: 8-column chunks are all or nothing
+#pragma unroll 4
+  for (int it = 0; it < BM / NW / 2; ++it) {
+    const int row = wave * (BM / NW) + it * 2 + hi;
+    const int rg = (row & 1) | (((row >> 2) & 1) << 1);
+    const u32x4_t v = ld16(smem + row * CROWB + (((cl >> 2) ^ rg) << 6) + ((cl & 3) << 4));
+    if (cok && row < M) st16(C + (size_t)row * N + cl * 8, v);
+  }
 }
 
 
@@ -867,8 +891,12 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     return run_bf16<32, 128, 1, 4>(a, rows, E, s);
   }
   // big tiles: the table was written by big_plan_kernel
-  hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves>), dim3(a.slots),
-                     dim3(kBigWaves * 64), 0, s, a);
+  if (a.gelu)
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves, true>), dim3(a.slots),
+                       dim3(kBigWaves * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves, false>), dim3(a.slots),
+                       dim3(kBigWaves * 64), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.part == nullptr) return err;
   hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>), dim3(kReduceSlots * kReduceParts),
