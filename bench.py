@@ -45,12 +45,15 @@ PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_mixtral_8x7b_pmc.md")
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc", "ffn.hip")
 
 
-def algorithmic_work(cfg, counts=None, kept=None):
+def algorithmic_work(cfg, counts=None, kept=None, fused=True):
     """Bytes / flops each step must move or compute (per call).
 
     route:    x once + Wg + bias + ids/weights out
-    dispatch: ids in, x once, xs out, perm + inv out, counts + offsets out
-    ffn:      4*rows*H*F + 4*T*H*Fs flops (the up and down projections)
+    dispatch: ids in, perm + inv out, counts + offsets out; with the row copy
+              (fused=False) also x once in and xs out
+    ffn:      4*rows*H*F + 4*T*H*Fs flops (the up and down projections);
+              bytes: live expert weights, the rows in (x once when the gather
+              is fused, else xs) and ys out
     combine:  ys in, inv + weights in, shared rows in, out
     With capacity dropping, kept[e] is expert e's kept rows: rows = sum(kept)
     (xs, the FFN and ys) and an expert is live if it kept a row.
@@ -60,13 +63,16 @@ def algorithmic_work(cfg, counts=None, kept=None):
     assign = T * k
     rows = assign if kept is None else int(kept.sum())
     route = T * H * b + E * H * b + (4 * E if cfg.bias_amp else 0) + 8 * assign
-    dispatch = 4 * assign + T * H * b + rows * H * b + 8 * assign + 4 * (2 * E + 1)
+    dispatch = 4 * assign + 8 * assign + 4 * (2 * E + 1)
+    if not fused:
+        dispatch += T * H * b + rows * H * b
     ffn_flops = 4 * rows * H * F + 4 * T * H * Fs
     if kept is not None:
         live = int((kept > 0).sum())
     else:
         live = E if counts is None else int((counts > 0).sum())
-    ffn_bytes = 2 * H * F * b * live + 2 * H * Fs * b + 2 * rows * H * b
+    ffn_bytes = 2 * H * F * b * live + 2 * H * Fs * b + rows * H * b
+    ffn_bytes += T * H * b if fused else rows * H * b
     combine = rows * H * b + 8 * assign + (T * H * b if Fs else 0) + T * H * b
     return dict(route_bytes=route, dispatch_bytes=dispatch, ffn_flops=ffn_flops,
                 ffn_weight_bytes=ffn_bytes, combine_bytes=combine)
@@ -135,9 +141,14 @@ def main():
     ap.add_argument("--flush", action="store_true",
                     help="cold caches: write a 1 GiB buffer before every step (outside the "
                          "per-call events); value then comes from the event span of each step")
+    ap.add_argument("--copy-gather", action="store_true",
+                    help="dispatch copies the rows into xs and the FFN reads xs (the default "
+                         "FFN reads x through perm: moe_expert_ffn_gather)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="end with a plain 512 MiB device copy (scales the HBM byte counters)")
     args = ap.parse_args()
+    if args.graph and args.copy_gather:
+        ap.error("--graph captures the fused-gather layer; --copy-gather is eager only")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs the MoE layer on one GPU only (no expert parallelism "
@@ -177,7 +188,7 @@ def main():
                offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
                perm=torch.empty(rows, dtype=torch.int32, device="cuda"),
                inv=torch.empty(rows, dtype=torch.int32, device="cuda"),
-               xs=torch.empty((rows, H), dtype=dtype, device="cuda"))
+               xs=torch.empty((rows, H), dtype=dtype, device="cuda") if args.copy_gather else None)
     ws_r = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, k, dt_code)),
                        dtype=torch.uint8, device="cuda")
     ws_d = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, E, k)), dtype=torch.uint8,
@@ -203,8 +214,12 @@ def main():
         moe.moe_dispatch(idx, x, E, out=dsp, ws=ws_d, stream=stream, capacity=cap)
         if ev is not None:
             ev[2].record(stream)
-        moe.moe_expert_ffn(dsp["xs"], dsp["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2, T=T, ys=ys,
-                           ysh=ysh, ws=ws_f, stream=stream)
+        if args.copy_gather:
+            moe.moe_expert_ffn(dsp["xs"], dsp["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2, T=T,
+                               ys=ys, ysh=ysh, ws=ws_f, stream=stream)
+        else:
+            moe.moe_expert_ffn_gather(x, dsp["perm"], k, dsp["offsets"], w1, w2, ws1=ws1,
+                                      ws2=ws2, ys=ys, ysh=ysh, ws=ws_f, stream=stream)
         if ev is not None:
             ev[3].record(stream)
         moe.moe_combine(ys, dsp["inv"], wts, ysh, out=out, stream=stream)
@@ -254,7 +269,7 @@ def main():
     layer_ms = np.array([events[s][0].elapsed_time(events[s][5]) for s in range(args.steps)])
     counts = dsp["counts"].cpu().numpy()
     kept = np.diff(dsp["offsets"].cpu().numpy()) if args.drop else None
-    work = algorithmic_work(cfg, counts, kept)
+    work = algorithmic_work(cfg, counts, kept, fused=not args.copy_gather)
     if args.flush and not args.graph:
         # the flush sits outside the per-call events: time the layer itself
         ms_step = float(layer_ms.mean())
@@ -302,6 +317,8 @@ def main():
                    "d_ff": F, "shared_d_ff": Fs, "routing_bias_amplitude": cfg.bias_amp,
                    "capacity_factor": cfg.cf, "parallelism": "single GPU",
                    "capacity_dropping": bool(args.drop),
+                   "gather": "dispatch copy (xs)" if args.copy_gather else
+                             "fused into the FFN (x read through perm)",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "caches": "flushed before every step" if args.flush else "warm"},
         "roofline": {"bound": "mfma", "kernel": DOMINANT_KERNEL, "achieved": achieved,

@@ -7,7 +7,8 @@
  *   moe_dispatch   expert histogram, offsets, stable permutation, row gather
  *                  (moe_dispatch_capped: the same with each expert's capacity enforced)
  *   moe_expert_ffn grouped Linear -> erf-GeLU -> Linear over ragged segments
- *                  (plus the optional always-on shared expert)
+ *                  (plus the optional always-on shared expert; moe_expert_ffn_gather:
+ *                  the same reading the token rows through perm, no xs copy)
  *   moe_combine    weighted sum of each token's k expert rows (+ shared row)
  *   moe_load_stats capacity, overflow / drops, skew, Gini, stragglers
  * and, after the layer, the routing-bias feedback of the next step:
@@ -134,6 +135,8 @@ size_t moe_dispatch_workspace_bytes(int T, int E, int k);
  * topk_idx [T,k] int32 in [0,E)  device, read (ids of one token are distinct)
  * x        [T,H] dtype           device, read
  * counts [E], offsets [E+1], perm [T*k], inv [T*k] int32; xs [T*k,H] dtype: device, written
+ * xs may be NULL: then no rows are copied (x is not read and may be NULL too),
+ * for moe_expert_ffn_gather, which reads x through perm itself.
  * ws / ws_bytes: device workspace of at least moe_dispatch_workspace_bytes(T,E,k)
  */
 int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k, int dtype,
@@ -187,6 +190,25 @@ int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int 
                    const void* w1, const void* w2, const void* x, const void* ws1,
                    const void* ws2, int T, int Fs, int dtype, void* ys, void* ysh, void* ws,
                    size_t ws_bytes, void* stream);
+
+/*
+ * moe_expert_ffn_gather - moe_expert_ffn with the dispatch gather fused into
+ * the first Linear: buffer row p of the routed experts is read from the token
+ * rows directly, xs[p,:] = x[perm[p] / k, :] ([BLOG] section 3.1 groups token
+ * indices by expert; the copy into a shared buffer is not materialised).
+ * Results are bit-identical to moe_dispatch (with xs) followed by moe_expert_ffn.
+ * x [T,H] dtype, perm [rows] int32 (device, from moe_dispatch or
+ *   moe_dispatch_capped, which may run with xs = NULL), 1 <= k <= 8 the
+ *   experts per token of that dispatch; a perm entry outside [0, T*k) is
+ *   clamped into it (never read out of bounds).
+ * All other arguments, the workspace (moe_expert_ffn_workspace_bytes) and the
+ * errors as moe_expert_ffn; x is required (it is the routed input as well as
+ * the shared expert's).
+ */
+int moe_expert_ffn_gather(const void* x, const int32_t* perm, int k, const int32_t* offsets,
+                          int rows, int E, int H, int F, const void* w1, const void* w2,
+                          const void* ws1, const void* ws2, int T, int Fs, int dtype, void* ys,
+                          void* ysh, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * moe_combine - weighted combine back to token order ([K3] combine phase;

@@ -30,6 +30,8 @@ SIGNATURES = {
     "moe_expert_ffn_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i, _i]),
     "moe_expert_ffn": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _vp,
                             _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_gather": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i,
+                                   _i, _i, _vp, _vp, _vp, _sz, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "moe_load_stats": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
     "moe_bias_update": (_i, [_vp, _i, ctypes.c_float, _vp, _vp, _vp]),
@@ -170,9 +172,12 @@ def moe_capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
     return int(((T * k) / E) * float(capacity_factor))
 
 
-def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=None):
+def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=None,
+                 gather: bool = True):
     """Returns dict(counts, offsets, perm, inv, xs). With ``capacity`` (int >= 0)
-    each expert keeps its first ``capacity`` assignments (moe_dispatch_capped)."""
+    each expert keeps its first ``capacity`` assignments (moe_dispatch_capped).
+    With ``gather=False`` no rows are copied and xs is None (for
+    moe_expert_ffn_gather); a given ``out`` without "xs" (or xs None) does the same."""
     T, H = x.shape
     k = topk_idx.shape[1]
     dev = x.device
@@ -181,13 +186,14 @@ def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=N
                    offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                    perm=torch.empty(T * k, dtype=torch.int32, device=dev),
                    inv=torch.empty(T * k, dtype=torch.int32, device=dev),
-                   xs=torch.empty((T * k, H), dtype=x.dtype, device=dev))
+                   xs=torch.empty((T * k, H), dtype=x.dtype, device=dev) if gather else None)
+    xs = out.get("xs")
     nbytes = moe_dispatch_workspace_bytes(T, E, k)
     ws = _workspace(nbytes, dev, ws)
     tail = (_dtype_code(x),
             _dev(out["counts"], "counts", torch.int32), _dev(out["offsets"], "offsets", torch.int32),
             _dev(out["perm"], "perm", torch.int32), _dev(out["inv"], "inv", torch.int32),
-            _dev(out["xs"], "xs", x.dtype), _dev(ws, "ws"), ws.numel(), _stream(stream))
+            _dev(xs, "xs", x.dtype), _dev(ws, "ws"), ws.numel(), _stream(stream))
     if capacity is None:
         _check("moe_dispatch", lib().moe_dispatch(
             _dev(topk_idx, "topk_idx", torch.int32), _dev(x, "x"), T, H, E, k, *tail))
@@ -219,6 +225,31 @@ def moe_expert_ffn(xs, offsets, w1, w2, x=None, ws1=None, ws2=None, T=None, ys=N
         _dev(w1, "w1", xs.dtype), _dev(w2, "w2", xs.dtype), _dev(x, "x", xs.dtype),
         _dev(ws1, "ws1", xs.dtype), _dev(ws2, "ws2", xs.dtype), T, Fs, dt, _dev(ys, "ys", xs.dtype),
         _dev(ysh, "ysh", xs.dtype) if Fs > 0 else None, _dev(ws, "ws"), ws.numel(),
+        _stream(stream)))
+    return ys, (ysh if Fs > 0 else None)
+
+
+def moe_expert_ffn_gather(x, perm, k: int, offsets, w1, w2, ws1=None, ws2=None, rows=None,
+                          ys=None, ysh=None, ws=None, stream=None):
+    """moe_expert_ffn reading routed row p from x[perm[p] // k] (no xs copy).
+    Returns (ys [rows,H], ysh [T,H] or None); rows defaults to T*k."""
+    T, H = x.shape
+    E, F, _ = w1.shape
+    Fs = 0 if ws1 is None else ws1.shape[0]
+    rows = T * k if rows is None else rows
+    dt = _dtype_code(x)
+    dev = x.device
+    if ys is None:
+        ys = torch.empty((rows, H), dtype=x.dtype, device=dev)
+    if Fs > 0 and ysh is None:
+        ysh = torch.empty((T, H), dtype=x.dtype, device=dev)
+    nbytes = moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dt)
+    ws = _workspace(nbytes, dev, ws)
+    _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
+        _dev(x, "x"), _dev(perm, "perm", torch.int32), k, _dev(offsets, "offsets", torch.int32),
+        rows, E, H, F, _dev(w1, "w1", x.dtype), _dev(w2, "w2", x.dtype),
+        _dev(ws1, "ws1", x.dtype), _dev(ws2, "ws2", x.dtype), T, Fs, dt, _dev(ys, "ys", x.dtype),
+        _dev(ysh, "ysh", x.dtype) if Fs > 0 else None, _dev(ws, "ws"), ws.numel(),
         _stream(stream)))
     return ys, (ysh if Fs > 0 else None)
 
@@ -263,15 +294,22 @@ def moe_load_stats(counts, T: int, k: int, capacity_factor: float, stats=None, o
 
 
 def moe_layer_forward(x, wg, bias, w1, w2, k: int, ws1=None, ws2=None, stream=None,
-                      prob_mean=None, capacity=None):
+                      prob_mean=None, capacity=None, fused_gather: bool = True):
     """All five steps on one stream (no host synchronisation). Returns a dict.
     prob_mean (optional fp32 [E]) receives the mean router probabilities;
-    capacity (optional int) drops each expert's assignments past it."""
+    capacity (optional int) drops each expert's assignments past it.
+    fused_gather (default): dispatch copies no rows and the FFN reads x through
+    perm (moe_expert_ffn_gather; xs is None); otherwise dispatch writes xs and
+    moe_expert_ffn reads it. Both give bit-identical outputs."""
     E = wg.shape[0]
     idx, w = moe_route(x, wg, bias, k, stream=stream, prob_mean=prob_mean)
-    d = moe_dispatch(idx, x, E, stream=stream, capacity=capacity)
-    ys, ysh = moe_expert_ffn(d["xs"], d["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2,
-                             T=x.shape[0], stream=stream)
+    d = moe_dispatch(idx, x, E, stream=stream, capacity=capacity, gather=not fused_gather)
+    if fused_gather:
+        ys, ysh = moe_expert_ffn_gather(x, d["perm"], k, d["offsets"], w1, w2, ws1=ws1, ws2=ws2,
+                                        stream=stream)
+    else:
+        ys, ysh = moe_expert_ffn(d["xs"], d["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2,
+                                 T=x.shape[0], stream=stream)
     out = moe_combine(ys, d["inv"], w, ysh, stream=stream)
     return dict(topk_idx=idx, topk_w=w, ys=ys, ysh=ysh, out=out, **d)
 
@@ -312,7 +350,7 @@ class MoELayerGraph:
                         offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
                         perm=torch.empty(T * k, dtype=torch.int32, device=dev),
                         inv=torch.empty(T * k, dtype=torch.int32, device=dev),
-                        xs=torch.empty((T * k, H), dtype=dtype, device=dev))
+                        xs=None)  # the FFN reads x through perm
         self.ws_r = torch.empty(max(1, moe_route_workspace_bytes(T, H, E, k, dt)),
                                 dtype=torch.uint8, device=dev)
         self.ws_d = torch.empty(max(1, moe_dispatch_workspace_bytes(T, E, k)), dtype=torch.uint8,
@@ -350,9 +388,9 @@ class MoELayerGraph:
                   ws=self.ws_r, prob_mean=self.prob_mean)
         moe_dispatch(self.idx, self.x, self.wg.shape[0], out=self.dsp, ws=self.ws_d,
                      capacity=self.cap)
-        moe_expert_ffn(self.dsp["xs"], self.dsp["offsets"], self.w1, self.w2, x=self.x,
-                       ws1=self.ws1, ws2=self.ws2, T=self.T, ys=self.ys, ysh=self.ysh,
-                       ws=self.ws_f)
+        moe_expert_ffn_gather(self.x, self.dsp["perm"], self.k, self.dsp["offsets"], self.w1,
+                              self.w2, ws1=self.ws1, ws2=self.ws2, ys=self.ys, ysh=self.ysh,
+                              ws=self.ws_f)
         moe_combine(self.ys, self.dsp["inv"], self.w, self.ysh, out=self.out)
         moe_load_stats(self.dsp["counts"], self.T, self.k, self.cf, stats=self.stats,
                        overflow=self.overflow, straggler_ids=self.stragglers, read_back=False)

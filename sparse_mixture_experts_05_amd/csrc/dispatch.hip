@@ -203,7 +203,7 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H,
   hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, cap,
                      blk, counts, offsets, perm, inv);
   err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || xs == nullptr) return err;  // no xs: ranks only (gather fused downstream)
   const int row_bytes = H * (bf16 ? 2 : 4);
   const int grid = (T + 3) / 4;
   hipLaunchKernelGGL(scatter_kernel<uint4>, dim3(grid), dim3(kThreads), 0, s,

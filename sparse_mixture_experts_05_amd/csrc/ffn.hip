@@ -58,7 +58,20 @@ struct GemmArgs {
   float* part;       // split-K partial tiles of the last round (big kernel), or null
   const int4* table; // big kernel: tile descriptors, 2 per slot (launch slots, then reduce slots)
   int slots;         // big kernel: workgroups of the launch (= reduce table start)
+  const int32_t* gather;  // routed rows read through perm: A row p = token perm[p] / gk, or null
+  int gk, gT;             // experts per token and tokens of that gather
 };
+
+// Row of the A operand that buffer row p of a group reads: p itself, or for
+// the routed group of a gathering launch the token perm[p] / k (perm clamped
+// into [0, T*k), so no read leaves x).
+__device__ __forceinline__ size_t a_row(const GemmArgs& a, int group, int p) {
+  if (group == 0 && a.gather != nullptr) {
+    const int v = min(max(a.gather[p], 0), a.gT * a.gk - 1);
+    return (size_t)(v / a.gk);
+  }
+  return (size_t)p;
+}
 
 struct Tile {
   int group;  // 0 routed, 1 shared
@@ -438,7 +451,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
   if (!find_tile<BM, BN>(args, t)) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N, K = G.K;
-  const uint16_t* A = static_cast<const uint16_t*>(G.A) + (size_t)t.row0 * K;
+  const uint16_t* A = static_cast<const uint16_t*>(G.A);
   const uint16_t* B = static_cast<const uint16_t*>(G.B) + (size_t)t.e * N * K + (size_t)t.n0 * K;
   uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
   const int M = t.M;
@@ -457,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
     const int g = wave * NI + q;
     const int r = 8 * g + (lane >> 3);
     const int chunk = (lane & 7) ^ ((r >> 1) & 7);
-    const uint16_t* row = r < BM ? A + (size_t)min(r, M - 1) * K
+    const uint16_t* row = r < BM ? A + a_row(args, t.group, t.row0 + min(r, M - 1)) * K
                                  : B + (size_t)min(r - BM, N - t.n0 - 1) * K;
     src[q] = row + chunk * 8;
     dst[q] = g * 8 * ROWB;
@@ -563,7 +576,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
   if (!table_tile(args, blockIdx.x, t)) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N, K = G.K;
-  const uint16_t* A = static_cast<const uint16_t*>(G.A) + (size_t)t.row0 * K;
+  const uint16_t* A = static_cast<const uint16_t*>(G.A);
   const uint16_t* B = static_cast<const uint16_t*>(G.B) + (size_t)t.e * N * K + (size_t)t.n0 * K;
   uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
   const int M = t.M;
@@ -584,7 +597,7 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
   for (int j = 0; j < A_INST; ++j) {
     const int r = (wave * A_INST + j) * ROWS_PER_INST + lrow;
     const int c = (lane & 7) ^ ((r >> 1) & 7);
-    ga[j] = A + (size_t)min(r, M - 1) * K + c * 8;
+    ga[j] = A + a_row(args, t.group, t.row0 + min(r, M - 1)) * K + c * 8;
   }
 #pragma unroll
   for (int j = 0; j < B_INST; ++j) {
@@ -801,13 +814,13 @@ __global__ __launch_bounds__(kThreads) void gemm_f32_kernel(GemmArgs args) {
   if (!find_tile<BM, BN>(args, t)) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N, K = G.K;
-  const float* A = static_cast<const float*>(G.A) + (size_t)t.row0 * K;
+  const float* A = static_cast<const float*>(G.A);
   const float* B = static_cast<const float*>(G.B) + (size_t)t.e * N * K + (size_t)t.n0 * K;
   float* C = static_cast<float*>(G.C) + (size_t)t.row0 * N + t.n0;
   const int M = t.M;
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int lr = tid >> 2, lk = (tid & 3) * 4;  // loader: row, first k of a float4
-  const float* ga = A + (size_t)min(lr, M - 1) * K + lk;
+  const float* ga = A + a_row(args, t.group, t.row0 + min(lr, M - 1)) * K + lk;
   const float* gb = B + (size_t)min(lr, N - t.n0 - 1) * K + lk;
   float acc[4][4] = {};
   for (int k0 = 0; k0 < K; k0 += BK) {
@@ -918,9 +931,10 @@ struct FfnLayout {
 
 // Arguments of both launches and the workspace layout; the same function
 // sizes the workspace and launches, so the two always agree.
-FfnLayout ffn_layout(const void* xs, const int32_t* offsets, int rows, int E, int H, int F,
-                     const void* w1, const void* w2, const void* x, const void* ws1,
-                     const void* ws2, int T, int Fs, bool bf16, void* ys, void* ysh, void* ws) {
+FfnLayout ffn_layout(const void* xs, const int32_t* gather, int gk, const int32_t* offsets,
+                     int rows, int E, int H, int F, const void* w1, const void* w2, const void* x,
+                     const void* ws1, const void* ws2, int T, int Fs, bool bf16, void* ys,
+                     void* ysh, void* ws) {
   FfnLayout Lo{};
   const size_t es = bf16 ? 2 : 4;
   Lo.big = big_tiles(rows, E, bf16);
@@ -942,6 +956,9 @@ FfnLayout ffn_layout(const void* xs, const int32_t* offsets, int rows, int E, in
   up.rows = rows;
   up.shared_M = shared ? T : 0;
   up.gelu = 1;
+  up.gather = gather;  // routed A = x read through perm (xs is then x)
+  up.gk = gk;
+  up.gT = T;
 
   GemmArgs& down = Lo.down;
   down.routed = Group{at(Lo.h), w2, ys, H, F};
@@ -977,17 +994,18 @@ FfnLayout ffn_layout(const void* xs, const int32_t* offsets, int rows, int E, in
 }  // namespace
 
 size_t ffn_ws_bytes(int rows, int T, int E, int H, int F, int Fs, bool bf16) {
-  return ffn_layout(nullptr, nullptr, rows, E, H, F, nullptr, nullptr, nullptr, nullptr, nullptr,
-                    T, Fs, bf16, nullptr, nullptr, nullptr)
+  return ffn_layout(nullptr, nullptr, 0, nullptr, rows, E, H, F, nullptr, nullptr, nullptr,
+                    nullptr, nullptr, T, Fs, bf16, nullptr, nullptr, nullptr)
       .bytes;
 }
 
-hipError_t launch_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int H,
-                             int F, const void* w1, const void* w2, const void* x,
-                             const void* ws1, const void* ws2, int T, int Fs, bool bf16,
-                             void* ys, void* ysh, void* ws, hipStream_t s) {
-  const FfnLayout Lo =
-      ffn_layout(xs, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T, Fs, bf16, ys, ysh, ws);
+hipError_t launch_expert_ffn(const void* xs, const int32_t* gather, int gk,
+                             const int32_t* offsets, int rows, int E, int H, int F, const void* w1,
+                             const void* w2, const void* x, const void* ws1, const void* ws2,
+                             int T, int Fs, bool bf16, void* ys, void* ysh, void* ws,
+                             hipStream_t s) {
+  const FfnLayout Lo = ffn_layout(xs, gather, gk, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T,
+                                  Fs, bf16, ys, ysh, ws);
   hipError_t err;
   if (Lo.big) {
     const int n = std::max(Lo.up.slots, Lo.down.slots) + kReduceSlots;

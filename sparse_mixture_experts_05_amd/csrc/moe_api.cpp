@@ -74,9 +74,9 @@ size_t moe_dispatch_workspace_bytes(int T, int E, int k) {
 int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k, int dtype,
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* xs,
                  void* ws, size_t ws_bytes, void* stream) {
-  if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !xs || !dtype_ok(dtype))
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !dtype_ok(dtype))
     return MOE_ERR_INVALID_ARG;
-  if (!aligned16(x) || !aligned16(xs)) return MOE_ERR_INVALID_ARG;
+  if (xs && (!x || !aligned16(x) || !aligned16(xs))) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
   if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
@@ -87,9 +87,9 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
 int moe_dispatch_capped(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
                         int capacity, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv, void* xs, void* ws, size_t ws_bytes, void* stream) {
-  if (!topk_idx || !x || !counts || !offsets || !perm || !inv || !xs || !dtype_ok(dtype) ||
-      capacity < 0 || !aligned16(x) || !aligned16(xs))
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !dtype_ok(dtype) || capacity < 0)
     return MOE_ERR_INVALID_ARG;
+  if (xs && (!x || !aligned16(x) || !aligned16(xs))) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
   if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
@@ -124,8 +124,29 @@ int moe_expert_ffn(const void* xs, const int32_t* offsets, int rows, int E, int 
   if (ws && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
   if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, E, H, F, Fs, dtype == MOE_BF16))
     return MOE_ERR_WORKSPACE;
-  return from_hip(moe::launch_expert_ffn(xs, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T, Fs,
-                                         dtype == MOE_BF16, ys, Fs > 0 ? ysh : nullptr, ws,
+  return from_hip(moe::launch_expert_ffn(xs, nullptr, 0, offsets, rows, E, H, F, w1, w2, x, ws1,
+                                         ws2, T, Fs, dtype == MOE_BF16, ys,
+                                         Fs > 0 ? ysh : nullptr, ws, as_stream(stream)));
+}
+
+int moe_expert_ffn_gather(const void* x, const int32_t* perm, int k, const int32_t* offsets,
+                          int rows, int E, int H, int F, const void* w1, const void* w2,
+                          const void* ws1, const void* ws2, int T, int Fs, int dtype, void* ys,
+                          void* ysh, void* ws, size_t ws_bytes, void* stream) {
+  if (!x || !perm || !offsets || !w1 || !w2 || !ys) return MOE_ERR_INVALID_ARG;
+  if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(ys)) return MOE_ERR_INVALID_ARG;
+  if (k < 1) return MOE_ERR_INVALID_ARG;
+  if (k > kMaxTopK || (long long)T * k >= (1LL << 31)) return MOE_ERR_UNSUPPORTED;
+  const int st = check_ffn(rows, T, H, E, F, Fs, dtype);
+  if (st != MOE_OK) return st;
+  if ((long long)rows > (long long)T * k) return MOE_ERR_UNSUPPORTED;
+  if (Fs > 0 && (!ws1 || !ws2 || !ysh)) return MOE_ERR_INVALID_ARG;
+  if (Fs > 0 && (!aligned16(ws1) || !aligned16(ws2) || !aligned16(ysh))) return MOE_ERR_INVALID_ARG;
+  if (ws && !aligned16(ws)) return MOE_ERR_INVALID_ARG;
+  if (!ws || ws_bytes < moe::ffn_ws_bytes(rows, T, E, H, F, Fs, dtype == MOE_BF16))
+    return MOE_ERR_WORKSPACE;
+  return from_hip(moe::launch_expert_ffn(x, perm, k, offsets, rows, E, H, F, w1, w2, x, ws1, ws2,
+                                         T, Fs, dtype == MOE_BF16, ys, Fs > 0 ? ysh : nullptr, ws,
                                          as_stream(stream)));
 }
 

@@ -22,7 +22,8 @@ import numpy as np
 import torch
 
 import oracle
-from sparse_mixture_experts_05_amd import moe_bias_update, moe_layer_forward, moe_load_stats
+from sparse_mixture_experts_05_amd import (moe_bias_update, moe_dispatch, moe_layer_forward,
+                                           moe_load_stats)
 
 TOL_W = 1e-4
 TOL_F32_ABS = 1e-4
@@ -58,8 +59,15 @@ def run_layer(cfg, L, sample=None):
                                                                      device="cuda")
     frac = torch.empty(cfg.E, dtype=torch.float32, device="cuda")
     moe_bias_update(r["counts"], b, GAMMA, load_frac=frac)
+    # the layer reads x through perm (no xs); the dispatch gather is checked on
+    # its own: moe_dispatch with xs on the same routing must agree bit for bit
+    dx = moe_dispatch(r["topk_idx"], d["x"], cfg.E)
     torch.cuda.synchronize()
-    got = {k: to_host(r[k]) for k in ["topk_idx", "topk_w", "counts", "offsets", "perm", "inv", "xs"]}
+    got = {k: to_host(r[k]) for k in ["topk_idx", "topk_w", "counts", "offsets", "perm", "inv"]}
+    for k in ["counts", "offsets", "perm", "inv"]:
+        assert np.array_equal(to_host(dx[k]), got[k]), f"dispatch with xs: {k} differs"
+    got["xs"] = to_host(dx["xs"])
+    del dx
     got["prob_mean"], got["bias_next"], got["load_frac"] = to_host(pm), to_host(b), to_host(frac)
     if sample is None:
         got["ys"], got["out"] = to_host(r["ys"]), to_host(r["out"])

@@ -27,7 +27,7 @@ def test_header_declares_the_five_steps():
     names = declared_functions()
     for n in ["moe_route", "moe_dispatch", "moe_expert_ffn", "moe_combine", "moe_load_stats",
               "moe_dispatch_capped", "moe_bias_update", "moe_status_string", "moe_route_workspace_bytes", "moe_dispatch_workspace_bytes",
-              "moe_expert_ffn_workspace_bytes"]:
+              "moe_expert_ffn_workspace_bytes", "moe_expert_ffn_gather"]:
         assert n in names
 
 
@@ -193,3 +193,47 @@ def test_binding_rejects_cpu_tensors():
         moe.moe_route(x, torch.zeros(8, 64, dtype=torch.bfloat16), None, 2,
                       topk_idx=torch.zeros(4, 2, dtype=torch.int32),
                       topk_w=torch.zeros(4, 2), stream=type("S", (), {"cuda_stream": 0})())
+
+
+def test_dispatch_without_row_copy_validation():
+    """xs = NULL asks for the ranks only (x is then not read and may be NULL);
+    a given xs still needs a 16-byte aligned x."""
+    L = moe.lib()
+    need = L.moe_dispatch_workspace_bytes(4096, 128, 8)
+    ODD = ctypes.c_void_p(0x1004)
+    # with xs: x is required and aligned
+    assert L.moe_dispatch(FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE,
+                          FAKE, need, None) == -1
+    assert L.moe_dispatch_capped(FAKE, ODD, 4096, 4096, 128, 8, 10, 1, FAKE, FAKE, FAKE, FAKE,
+                                 FAKE, FAKE, need, None) == -1
+    # without xs the other checks still apply (workspace, sizes, capacity)
+    assert L.moe_dispatch(FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE, None,
+                          None, need, None) == -3
+    assert L.moe_dispatch(FAKE, None, 4096, 4096, 300, 8, 1, FAKE, FAKE, FAKE, FAKE, None,
+                          FAKE, need, None) == -2
+    assert L.moe_dispatch_capped(FAKE, None, 4096, 4096, 128, 8, -1, 1, FAKE, FAKE, FAKE, FAKE,
+                                 None, FAKE, need, None) == -1
+
+
+def test_expert_ffn_gather_validation():
+    L = moe.lib()
+    rows, T, H, E, F, Fs, k = 8192, 4096, 4096, 8, 14336, 0, 2
+    need = L.moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, 1)
+    ODD = ctypes.c_void_p(0x1004)
+
+    def call(x=FAKE, perm=FAKE, k_=k, rows_=rows, w1=FAKE, ws=FAKE, nbytes=need, Fs_=Fs,
+             ws1=None, ysh=None):
+        return L.moe_expert_ffn_gather(x, perm, k_, FAKE, rows_, E, H, F, w1, FAKE, ws1, ws1, T,
+                                       Fs_, 1, FAKE, ysh, ws, nbytes, None)
+
+    assert call(x=None) == -1
+    assert call(perm=None) == -1
+    assert call(x=ODD) == -1
+    assert call(w1=ODD) == -1
+    assert call(k_=0) == -1
+    assert call(k_=9) == -2
+    assert call(rows_=T * k + 1) == -2      # more rows than assignments
+    assert call(ws=None) == -3
+    assert call(nbytes=need - 1) == -3
+    assert call(Fs_=64) == -1                # shared expert without its weights / output
+    assert call(Fs_=64, ws1=FAKE, ysh=ODD) == -1

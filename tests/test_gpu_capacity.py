@@ -1,4 +1,5 @@
-"""GPU parity of the capacity-enforced layer (moe_dispatch_capped + FFN + combine).
+"""GPU parity of the capacity-enforced layer (moe_dispatch_capped + FFN + combine;
+the FFN reads the kept rows through perm, the row copy is checked on its own).
 
 Against the oracle's dispatch_capped and layer_rows(keep=...):
   bit-exact: raw counts, kept offsets, the kept part of perm, inv (-1 for a
@@ -66,8 +67,14 @@ def test_capped_layer_parity(case):
     n = int(offsets[-1])
     assert np.array_equal(to_host(r["perm"])[:n], perm)
     assert np.array_equal(to_host(r["inv"]), inv)
-    xs = to_host(r["xs"][:n])
+    # the layer read x through perm; the capped dispatch's own row copy on the
+    # same routing must hold exactly the kept rows
+    dx = moe.moe_dispatch(r["topk_idx"], d["x"], E, capacity=cap)
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(dx["perm"])[:n], perm)
+    xs = to_host(dx["xs"][:n])
     assert np.array_equal(xs, L["x"][perm // k])
+    del dx
 
     tokens = np.arange(T) if sample is None else sample
     out_ref, _, _ = oracle.layer_rows(L, idx, w, tokens, keep=keep)
