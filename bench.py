@@ -40,7 +40,6 @@ BF16_PEAK_TFLOPS = 2500.0
 FP32_PEAK_TFLOPS = 157.3
 CPU_TARGET_S = 15.0
 CALIB_BYTES = 512 << 20
-DOMINANT_KERNEL = "gemm_bf16_kernel"
 PMC_SUMMARY = os.path.join(ROOT, "profiles", "gemm_bf16_mixtral_8x7b_pmc.md")
 GEMM_SOURCE = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc", "ffn.hip")
 
@@ -76,6 +75,14 @@ def algorithmic_work(cfg, counts=None, kept=None, fused=True):
     combine = rows * H * b + 8 * assign + (T * H * b if Fs else 0) + T * H * b
     return dict(route_bytes=route, dispatch_bytes=dispatch, ffn_flops=ffn_flops,
                 ffn_weight_bytes=ffn_bytes, combine_bytes=combine)
+
+
+def gemm_kernel_name(cfg):
+    """The grouped-GEMM kernel the FFN launches run (the rule of the library's
+    launcher: 256x256 tiles once there are 64 rows per expert on average)."""
+    if cfg.dtype != "bf16":
+        return "gemm_f32_kernel"
+    return "gemm_bf16_big_kernel" if cfg.T * cfg.k >= 64 * cfg.E else "gemm_bf16_kernel"
 
 
 def code_sha256(path):
@@ -321,7 +328,7 @@ def main():
                              "fused into the FFN (x read through perm)",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "caches": "flushed before every step" if args.flush else "warm"},
-        "roofline": {"bound": "mfma", "kernel": DOMINANT_KERNEL, "achieved": achieved,
+        "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(cfg), "achieved": achieved,
                      "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
                      "traffic": traffic},
         "kernels": kernels,
