@@ -6,12 +6,15 @@
 // scattered back to the original positions); the always-on shared expert's
 // row is added with weight 1.
 //
-// One wavefront per token. The token's k buffer rows are found through inv
+// One wavefront per token (per column segment of the token's row when there
+// are few tokens). The token's k buffer rows are found through inv
 // (a gather, so every output row is written exactly once: no atomics, and a
 // fixed summation order j = 0..k-1, then the shared row). An assignment that
 // a capacity dropped (inv < 0) is skipped; the other weights are kept as they
 // are (no renormalisation). 16-byte loads and stores; fp32 accumulation in
 // registers.
+#include <algorithm>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -44,11 +47,13 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], uint4 v) {
 template <int KM>
 __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     const uint4* __restrict__ ys, const int32_t* __restrict__ inv, const float* __restrict__ w,
-    const uint4* __restrict__ ysh, int T, int vpr, int k, uint4* __restrict__ out) {
+    const uint4* __restrict__ ysh, int T, int vpr, int k, int seg, uint4* __restrict__ out) {
   constexpr int U = 8 / KM;
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
+  // this wave's columns: segment blockIdx.y of the row (one segment when T is large)
+  const int cbeg = blockIdx.y * seg, cend = min(vpr, cbeg + seg);
   int row[KM];
   float wt[KM];
   bool keep[KM];
@@ -59,12 +64,12 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     row[j] = min(max(r, 0), T * k - 1);
     wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
-  for (int c0 = lane; c0 < vpr; c0 += U * kWave) {
+  for (int c0 = cbeg + lane; c0 < cend; c0 += U * kWave) {
     uint4 v[U][KM], sh[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kWave;
-      if (c < vpr) {
+      if (c < cend) {
 #pragma unroll
         for (int j = 0; j < KM; ++j)
           if (keep[j]) v[u][j] = ys[(size_t)row[j] * vpr + c];
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = c0 + u * kWave;
-      if (c < vpr) {
+      if (c < cend) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < KM; ++j)
@@ -94,10 +99,11 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
 // fp32: each 16-byte vector holds 4 values.
 __global__ __launch_bounds__(kThreads) void combine_f32_kernel(
     const float4* __restrict__ ys, const int32_t* __restrict__ inv, const float* __restrict__ w,
-    const float4* __restrict__ ysh, int T, int vpr, int k, float4* __restrict__ out) {
+    const float4* __restrict__ ysh, int T, int vpr, int k, int seg, float4* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
+  const int cbeg = blockIdx.y * seg, cend = min(vpr, cbeg + seg);
   int row[8];
   float wt[8];
   bool keep[8];
@@ -108,7 +114,7 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(
     row[j] = min(max(r, 0), T * k - 1);
     wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
-  for (int c = lane; c < vpr; c += kWave) {
+  for (int c = cbeg + lane; c < cend; c += kWave) {
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
@@ -136,19 +142,28 @@ __global__ __launch_bounds__(kThreads) void combine_f32_kernel(
 hipError_t launch_combine(const void* ys, const int32_t* inv, const float* topk_w,
                           const void* ysh, int T, int H, int k, bool bf16, void* out,
                           hipStream_t s) {
+  // Few tokens: split each row into column segments (grid.y) so that about
+  // 1024 wavefronts stream the rows, each segment one pass of the wave.
   const int grid = (T + 3) / 4;
+  const int vpr = H / (bf16 ? 8 : 4);
+  const int km = k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : 8;
+  const int step = bf16 ? (8 / km) * kWave : kWave;  // vectors one pass of a wave covers
+  int nseg = std::max(1, std::min((vpr + step - 1) / step, (1024 + T - 1) / T));
+  const int seg = ((vpr + nseg - 1) / nseg + step - 1) / step * step;
+  nseg = (vpr + seg - 1) / seg;
   if (bf16) {
-    auto kern = k <= 1   ? combine_bf16_kernel<1>
-                : k <= 2 ? combine_bf16_kernel<2>
-                : k <= 4 ? combine_bf16_kernel<4>
-                         : combine_bf16_kernel<8>;
-    hipLaunchKernelGGL(kern, dim3(grid), dim3(kThreads), 0, s, static_cast<const uint4*>(ys), inv,
-                       topk_w, static_cast<const uint4*>(ysh), T, H / 8, k,
-                       static_cast<uint4*>(out));
+    auto kern = km == 1   ? combine_bf16_kernel<1>
+                : km == 2 ? combine_bf16_kernel<2>
+                : km == 4 ? combine_bf16_kernel<4>
+                          : combine_bf16_kernel<8>;
+    hipLaunchKernelGGL(kern, dim3(grid, nseg), dim3(kThreads), 0, s,
+                       static_cast<const uint4*>(ys), inv, topk_w,
+                       static_cast<const uint4*>(ysh), T, vpr, k, seg, static_cast<uint4*>(out));
   } else {
-    hipLaunchKernelGGL(combine_f32_kernel, dim3(grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(combine_f32_kernel, dim3(grid, nseg), dim3(kThreads), 0, s,
                        static_cast<const float4*>(ys), inv, topk_w,
-                       static_cast<const float4*>(ysh), T, H / 4, k, static_cast<float4*>(out));
+                       static_cast<const float4*>(ysh), T, vpr, k, seg,
+                       static_cast<float4*>(out));
   }
   return hipGetLastError();
 }
