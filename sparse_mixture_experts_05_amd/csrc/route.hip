@@ -18,9 +18,9 @@
 //            keys over a strided subset of the experts, merged across the G
 //            lanes by bitonic merges over DPP / ds_swizzle / bpermute
 //            exchanges. Ties go to the lower expert id.
-// Few tokens (bf16, T < 2048, or T < 3072 when E > 128) take two launches:
-// partial score tiles over K slices into the workspace, then a sum in slice
-// order and the top-k.
+// Few tokens (bf16, T < 2048, or T < 3072 when E > 128), and mid-size
+// batches (T < 6144) with E > 64, take two launches: partial score tiles over
+// K slices into the workspace, then a sum in slice order and the top-k.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -445,30 +445,42 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
 }
 
 
-// Few tokens (bf16, T < 2048): one workgroup per 16 tokens would stream all
-// of Wg through a single CU, so the scores are computed in two launches.
-// Phase 1: workgroup (token block, 64-expert block, K slice) computes its
-// partial score tile and stores it in the workspace ws[ks][t][e]. Phase 2:
-// one wavefront per token sums its K slices in a fixed order (ks ascending),
-// adds the bias and runs the top-k.
+// Two launches (bf16). Phase 1: workgroup (token block, expert block, K slice)
+// computes its BT x EP partial score tile and stores it in the workspace
+// ws[ks][t][e]. Phase 2: one wavefront per token sums its K slices in a fixed
+// order (ks ascending), adds the bias and runs the top-k.
+//   Few tokens: 16 x 64 tiles, so that a few tokens still spread Wg over
+//   about 256 workgroups (one workgroup per 16 tokens would stream all of Wg
+//   through a single CU).
+//   Mid-size batches and E > 64: 64 x 128 (E <= 128) or 128 x 256 tiles, so
+//   that Wg is read once per 64 or 128 tokens instead of once per 16-64, the
+//   L2 -> LDS traffic that bounds the one-launch kernel at large E.
 constexpr int kPartBT = 16, kPartEP = 64, kMaxSlices = 16;
 
+template <int BT, int EP>
 __global__ __launch_bounds__(kThreads) void route_partial_kernel(const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ wg,
                                                                  int T, int H, int E, int kps,
                                                                  float* __restrict__ ws) {
-  using C = RouteTile<kPartBT, kPartEP>;
+  using C = RouteTile<BT, EP>;
+  static_assert(!C::KSPLIT, "each wave owns EP / 4 experts");
   __shared__ __align__(16) uint8_t smem[C::NS * C::SB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t0 = blockIdx.x * kPartBT, e0 = blockIdx.y * kPartEP, ks = blockIdx.z;
+  const int t0 = blockIdx.x * BT, e0 = blockIdx.y * EP, ks = blockIdx.z;
   f32x4_t acc[C::MC][C::NC];
-  score_tile<kPartBT, kPartEP>(smem, x, wg, t0, T, e0, E, H, ks * kps, (ks + 1) * kps, acc);
-  const int e = e0 + wave * (kPartEP / 4) + (lane & 15);
+  score_tile<BT, EP>(smem, x, wg, t0, T, e0, E, H, ks * kps, (ks + 1) * kps, acc);
+  // D layout of 16x16: lane holds column lane%16, rows (lane/16)*4 + v
 #pragma unroll
-  for (int v = 0; v < 4; ++v) {
-    const int t = t0 + (lane >> 4) * 4 + v;
-    if (t < T && e < E) ws[((size_t)ks * T + t) * E + e] = acc[0][0][v];
-  }
+  for (int m = 0; m < C::MC; ++m)
+#pragma unroll
+    for (int n = 0; n < C::NC; ++n) {
+      const int e = e0 + wave * (EP / 4) + n * 16 + (lane & 15);
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int t = t0 + m * 16 + (lane >> 4) * 4 + v;
+        if (t < T && e < E) ws[((size_t)ks * T + t) * E + e] = acc[m][n][v];
+      }
+    }
 }
 
 template <int NKS>
@@ -501,20 +513,35 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __r
                  ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
-// K slices for the two-phase path: about 256 workgroups in phase 1, a power of
+// Path of a route call. Both two-launch paths write and re-read T x E partial
+// scores per K slice, so their time grows faster with T than the one-launch
+// path's. Measured crossovers (graph replay, H = 4096, k = 8): small tiles
+// against one launch near T = 2048 up to E = 128 and near 3072 for E = 256;
+// big tiles against one launch between T = 4096 and 8192 (E = 128: 27.2
+// against 29.3 us at 4096, 42.4 against 33.8 at 8192; E = 256: 35.6 against
+// 39.4, 52.0 against 45.6).
+enum RouteMode { kOneLaunch, kTwoSmall, kTwoBig };
+RouteMode route_mode(int T, int E, bool bf16) {
+  if (!bf16) return kOneLaunch;
+  if (T < (E > 128 ? 3072 : 2048)) return kTwoSmall;
+  return E > 64 && T < 6144 ? kTwoBig : kOneLaunch;
+}
+bool route_two_phase(int T, int E, bool bf16) { return route_mode(T, E, bf16) != kOneLaunch; }
+
+// Tile of the big-tile path.
+int big_bt(int E) { return E > 128 ? 128 : 64; }
+int big_ep(int E) { return E > 128 ? 256 : 128; }
+
+// K slices of a two-launch path: about 256 workgroups in phase 1, a power of
 // two (at most kMaxSlices) that divides the H/64 panels.
 int route_kslices(int T, int H, int E) {
-  const int tiles = ((T + kPartBT - 1) / kPartBT) * ((E + kPartEP - 1) / kPartEP);
+  const bool big = route_mode(T, E, true) == kTwoBig;
+  const int bt = big ? big_bt(E) : kPartBT, ep = big ? big_ep(E) : kPartEP;
+  const int tiles = ((T + bt - 1) / bt) * ((E + ep - 1) / ep);
   int ks = 1;
   while (ks * 2 * tiles <= 256 && (H / 64) % (ks * 2) == 0 && ks * 2 <= kMaxSlices) ks *= 2;
   return ks;
 }
-
-// The two-launch path reads x once per K slice and expert tile and writes T x E
-// partial scores per slice, so its time grows faster with T than the one-launch
-// path's; measured crossover (graph replay, H = 4096, k = 8): T near 2048 up to
-// E = 128, near 3072 for E = 256 (each one-launch workgroup re-reads all of Wg).
-bool route_two_phase(int T, int E, bool bf16) { return bf16 && T < (E > 128 ? 3072 : 2048); }
 
 template <int BT, int EP>
 hipError_t launch_bf16(const void* x, const void* wg, const float* bias, int T, int H, int E,
@@ -570,12 +597,26 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
                   ? nullptr
                   : reinterpret_cast<float*>(static_cast<char*>(ws) + scores_ws_bytes(T, H, E, bf16));
   hipError_t err = hipSuccess;
-  if (route_two_phase(T, E, bf16)) {
+  const RouteMode mode = route_mode(T, E, bf16);
+  if (mode != kOneLaunch) {
     const int nks = route_kslices(T, H, E);
-    const dim3 grid((T + kPartBT - 1) / kPartBT, (E + kPartEP - 1) / kPartEP, nks);
-    hipLaunchKernelGGL(route_partial_kernel, grid, dim3(kThreads), 0, s,
-                       static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), T, H, E,
-                       (H / 64) / nks, static_cast<float*>(ws));
+    const int kps = (H / 64) / nks;
+    const uint16_t* xp = static_cast<const uint16_t*>(x);
+    const uint16_t* wp = static_cast<const uint16_t*>(wg);
+    float* sp = static_cast<float*>(ws);
+    if (mode == kTwoSmall) {
+      const dim3 grid((T + kPartBT - 1) / kPartBT, (E + kPartEP - 1) / kPartEP, nks);
+      hipLaunchKernelGGL((route_partial_kernel<kPartBT, kPartEP>), grid, dim3(kThreads), 0, s, xp,
+                         wp, T, H, E, kps, sp);
+    } else if (E > 128) {
+      const dim3 grid((T + 127) / 128, (E + 255) / 256, nks);
+      hipLaunchKernelGGL((route_partial_kernel<128, 256>), grid, dim3(kThreads), 0, s, xp, wp, T,
+                         H, E, kps, sp);
+    } else {
+      const dim3 grid((T + 63) / 64, (E + 127) / 128, nks);
+      hipLaunchKernelGGL((route_partial_kernel<64, 128>), grid, dim3(kThreads), 0, s, xp, wp, T, H,
+                         E, kps, sp);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
     hipLaunchKernelGGL(route_select_kernel<kMaxSlices>, dim3((T + 3) / 4), dim3(kThreads), 0, s,

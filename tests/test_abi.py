@@ -73,20 +73,31 @@ def test_route_workspace():
     assert need >= 16 * 128 * 4 + 4 * 128 * 4 and need % 256 == 0
     assert L.moe_route(FAKE, FAKE, None, 16, 4096, 128, 8, 1, FAKE, FAKE, None, None, 0, None) == -3
     assert L.moe_route(FAKE, FAKE, None, 16, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE, need - 1, None) == -3
-    # large batches only need it for the mean probabilities: one row of E
-    # floats per workgroup of 16 tokens (T = 4096, bf16) or 16 tokens (fp32)
-    assert L.moe_route_workspace_bytes(4096, 4096, 128, 8, 1) == 256 * 128 * 4
-    assert L.moe_route_workspace_bytes(64, 256, 8, 2, 0) == 256
-    assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, None, 0, None) == -3
-    assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE,
-                       256 * 128 * 4 - 1, None) == -3
-    assert L.moe_route_workspace_bytes(16, 4096, 300, 8, 1) == 0
-    # with E > 128 the two-launch path is kept up to T = 3071
-    # (partial scores on top of the probability rows, 16 tokens per row beyond it)
+    # the one-launch path (large batches, E <= 64) only needs it for the mean
+    # probabilities: one row of E floats per workgroup of 16 tokens
     rows16 = lambda T, E: -(-(-(-T // 16) * E * 4) // 256) * 256
+    assert L.moe_route_workspace_bytes(4096, 4096, 64, 8, 1) == 256 * 64 * 4
+    assert L.moe_route_workspace_bytes(64, 256, 8, 2, 0) == 256
+    assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 64, 8, 1, FAKE, FAKE, FAKE, None, 0, None) == -3
+    assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 64, 8, 1, FAKE, FAKE, FAKE, FAKE,
+                       256 * 64 * 4 - 1, None) == -3
+    assert L.moe_route_workspace_bytes(16, 4096, 300, 8, 1) == 0
+    assert L.moe_route_workspace_bytes(2500, 4096, 64, 8, 1) == rows16(2500, 64)
+    # two launches: partial scores [slices][T][E] fp32, then (with the mean
+    # probabilities) one row of E floats per 4 tokens. Few tokens, or E > 64 and
+    # T < 6144 (big tiles: 64 x 128 for E <= 128, 128 x 256 above, ~256 workgroups)
+    al = lambda b: -(-b // 256) * 256
     assert L.moe_route_workspace_bytes(2500, 4096, 256, 8, 1) > 2500 * 256 * 4
-    assert L.moe_route_workspace_bytes(2500, 4096, 128, 8, 1) == rows16(2500, 128)
-    assert L.moe_route_workspace_bytes(3072, 4096, 256, 8, 1) == rows16(3072, 256)
+    assert L.moe_route_workspace_bytes(4096, 4096, 128, 8, 1) == (al(4 * 4096 * 128 * 4)
+                                                                  + al(1024 * 128 * 4))
+    assert L.moe_route_workspace_bytes(5000, 4096, 256, 8, 1) > 5000 * 256 * 4
+    # large batches go back to one launch (64 tokens per workgroup at T = 16384)
+    assert L.moe_route_workspace_bytes(16384, 4096, 256, 8, 1) == 256 * 256 * 4
+    # the partial scores are needed even without the mean probabilities
+    assert L.moe_route(FAKE, FAKE, None, 4096, 4096, 128, 8, 1, FAKE, FAKE, None, FAKE,
+                       al(4 * 4096 * 128 * 4) - 1, None) == -3
+    # fp32 keeps one launch: only the probability rows (16 tokens per row)
+    assert L.moe_route_workspace_bytes(4096, 4096, 128, 8, 0) == 256 * 128 * 4
 
 
 def test_misaligned_rows_are_rejected():

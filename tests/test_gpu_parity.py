@@ -30,6 +30,9 @@ SMALL = [
     MoEConfig("route_bt64_E12_H192", T=16400, H=192, E=12, k=3, F=64, bias_amp=1.0),
     # two-launch route above T = 2048 (E > 128), ragged expert and token tiles
     MoEConfig("route_two_launch_E200", T=2500, H=256, E=200, k=8, F=64, bias_amp=1.0),
+    # big-tile two-launch route: 64 x 128 tiles (E <= 128), 128 x 256 tiles (E > 128)
+    MoEConfig("route_big_E128", T=2100, H=512, E=128, k=8, F=64, bias_amp=1.5),
+    MoEConfig("route_big_E136", T=3100, H=256, E=136, k=4, F=64, bias_amp=1.0),
     # down projection with K = 8192 (routed and shared): the last round is split over K
     MoEConfig("split_k_tail", T=600, H=256, E=4, k=1, F=8192, Fs=8192, bias_amp=0.5),
 ]
