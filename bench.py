@@ -349,7 +349,11 @@ def main():
         print(f"[bench] cpu baseline on {n} tokens", file=sys.stderr, flush=True)
         cb = cpu_baseline(cfg, L, n)
         if cb["seconds"] < CPU_TARGET_S / 2 and n < T:
-            n2 = min(T, int(n * CPU_TARGET_S / max(cb["seconds"], 1e-3)))
+            # the whole layer when it fits in about twice the target, else a
+            # sample sized to the target (the first sample's rate includes
+            # fixed costs, so this errs on the short side)
+            est_all = cb["seconds"] * T / n
+            n2 = T if est_all <= 2 * CPU_TARGET_S else min(T, int(n * CPU_TARGET_S / max(cb["seconds"], 1e-3)))
             print(f"[bench] cpu baseline on {n2} tokens", file=sys.stderr, flush=True)
             cb = cpu_baseline(cfg, L, n2)
         cb.pop("seconds")
