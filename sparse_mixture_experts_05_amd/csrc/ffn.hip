@@ -35,6 +35,7 @@
 #include "common.hpp"
 #include "kernels.hpp"
 
+
 namespace moe {
 namespace {
 
@@ -150,23 +151,21 @@ __device__ bool find_tile(const GemmArgs& a, Tile& t) {
 }
 
 // Blocked, XCD-aware tile order (large tiles). Groups are the E experts and
-// then the shared expert. A group with c rows has floor(c/BM) full row tiles
-// and, if BM does not divide c, one partial row tile.
+// then the shared expert. A group with c rows has ceil(c/BM) row tiles; if BM
+// does not divide c the last one is partial (it skips the 32-row sub-tiles
+// past the segment end).
 //
-// Full tiles come first. Inside a group they are visited in n-blocks of GN
-// column tiles, row tile by row tile inside an n-block (consecutive tiles
-// share A rows and cycle through GN weight panels). Workgroups are handed to
-// the 8 XCDs round robin (workgroup g runs on XCD g % 8); XCD x takes the
-// contiguous run [x*CF, (x+1)*CF) of the full-tile order (CF = ceil(F/8)),
-// so the ~32 tiles an XCD runs at once form a compact block whose operand
-// panels its L2 shares.
+// Inside a group tiles are visited in n-blocks of GN column tiles, row tile by
+// row tile inside an n-block (consecutive tiles share A rows and cycle
+// through GN weight panels). A partial row tile sits in the n-blocks with the
+// full ones, so it reads each weight panel while the others of its n-block
+// do, not again after every panel has left the caches. Workgroups are handed
+// to the 8 XCDs round robin (workgroup g runs on XCD g % 8); XCD x takes the
+// contiguous run [x*C, (x+1)*C) of this order (C = ceil(tiles/8)), so the ~32
+// tiles an XCD runs at once form a compact block whose operand panels its L2
+// shares.
 //
-// Partial tiles come last on every XCD (partial tile p on XCD p % 8), in
-// groups ordered by descending partial-tile rows (ties: lower group first).
-// They skip the 32-row sub-tiles past the segment end, so they are the short
-// tiles; running them last, longest first, packs the final round.
-//
-// Split K in the last round: an XCD runs S = CF + CP tiles, kSlots at a time.
+// Split K in the last round: an XCD runs S = C tiles, kSlots at a time.
 // When the last round holds tail = S mod kSlots tiles and that is at most half
 // a round, each of those tiles is cut into spl K slices (one workgroup each,
 // spl = kSlots / tail, at most kMaxSplit, and every slice keeps at least
@@ -186,13 +185,12 @@ constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
 
 // Tables of the big-tile schedule (per workgroup, in LDS).
 struct SchedLds {
-  int pf[257], pp[257];    // inclusive scans: full tiles by group, partial tiles by rank
-  int prow[257], sgrp[257];  // partial-tile rows by group; group of each rank
+  int pf[257];               // inclusive scan of the tiles by group
   int goff[257], gcnt[257];  // first row and rows of each group
 };
 
 struct BigSched {
-  int F, P, CF, CP;  // full / partial tiles in all; per XCD
+  int F, CF;         // tiles in all; per XCD
   int R, tail, spl;  // whole rounds per XCD, tiles of the last round, K slices of those
 };
 
@@ -218,80 +216,34 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
       cnt = a.shared_M;
     }
   };
-  int off = 0, cnt = 0, full = 0, part = 0;
+  int off = 0, cnt = 0, tiles = 0;
   if (act && tid < ng) {
     rows_of(tid, off, cnt);
-    const int nt = tid < a.E ? ntr : nts;
-    full = (cnt / BM) * nt;
-    part = (cnt % BM) ? nt : 0;
+    tiles = ((cnt + BM - 1) / BM) * (tid < a.E ? ntr : nts);
   }
-  int xfull = 0, xpart = 0;
-  if (tid == 255 && ng == 257) {
-    xfull = (a.shared_M / BM) * nts;
-    xpart = (a.shared_M % BM) ? nts : 0;
-  }
+  const int xtiles = (tid == 255 && ng == 257) ? ((a.shared_M + BM - 1) / BM) * nts : 0;
   if (act) {
-    L.prow[tid] = tid < ng ? cnt % BM : 0;
     L.goff[tid] = off;
     L.gcnt[tid] = cnt;
+    L.pf[tid] = tiles;
   }
   if (tid == 255) {
-    L.prow[256] = ng == 257 ? a.shared_M % BM : 0;
     L.goff[256] = 0;
     L.gcnt[256] = ng == 257 ? a.shared_M : 0;
   }
   __syncthreads();
-  // rank of each group with a partial tile: descending rows, ties by id
-  auto rank_of = [&](int grp) {
-    const int r = L.prow[grp];
-    int k = 0;
-    for (int o = 0; o < ng; ++o) {
-      const int ro = L.prow[o];
-      k += (ro > r) || (ro == r && o < grp);
-    }
-    return k;
-  };
-  int myrank = -1, xrank = -1;
-  if (act && tid < ng) myrank = rank_of(tid);
-  if (tid == 255 && ng == 257) xrank = rank_of(256);
-  __syncthreads();
-  // pp is indexed by rank: partial tile counts in longest-first order
-  if (act) L.pp[tid] = 0;
-  if (tid == 255) L.pp[256] = 0;
-  __syncthreads();
-  if (myrank >= 0) {
-    L.pp[myrank] = part;
-    L.sgrp[myrank] = tid;
-  }
-  if (xrank >= 0) {
-    L.pp[xrank] = xpart;
-    L.sgrp[xrank] = 256;
-  }
-  if (act) L.pf[tid] = full;
-  __syncthreads();
-  if (tid == 255) xpart = L.pp[256];  // the scan below folds entry 256 in separately
-  __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {
-    const int vf = (act && tid >= d) ? L.pf[tid - d] : 0;
-    const int vp = (act && tid >= d) ? L.pp[tid - d] : 0;
+    const int v = (act && tid >= d) ? L.pf[tid - d] : 0;
     __syncthreads();
-    if (act) {
-      L.pf[tid] += vf;
-      L.pp[tid] += vp;
-    }
+    if (act) L.pf[tid] += v;
     __syncthreads();
   }
-  if (tid == 255) {
-    L.pf[256] = L.pf[255] + xfull;
-    L.pp[256] = L.pp[255] + xpart;
-  }
+  if (tid == 255) L.pf[256] = L.pf[255] + xtiles;
   __syncthreads();
   const int last = ng <= 256 ? ng - 1 : 256;
-  const int F = L.pf[last], P = L.pp[last];
+  const int F = L.pf[last];
   const int CF = (F + kXcds - 1) / kXcds;
-  const int CP = (P + kXcds - 1) / kXcds;
-  const int slots = CF + CP;
-  const int R = slots / kSlots, tail = slots - R * kSlots;
+  const int R = CF / kSlots, tail = CF - R * kSlots;
   int spl = 1;
   if (a.part != nullptr && tail > 0 && 2 * tail <= kSlots) {  // a.part: K long enough
     int ktmin = a.routed.K / 64;
@@ -300,9 +252,7 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
   }
   BigSched S;
   S.F = F;
-  S.P = P;
   S.CF = CF;
-  S.CP = CP;
   S.R = R;
   S.tail = tail;
   S.spl = spl;
@@ -319,7 +269,7 @@ __device__ bool resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLd
   const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
   const int ntr = (a.routed.N + BN - 1) / BN;
   const int nts = (a.shared.N + BN - 1) / BN;
-  const int F = S.F, P = S.P, CF = S.CF, CP = S.CP, R = S.R, tail = S.tail, spl = S.spl;
+  const int F = S.F, CF = S.CF, R = S.R, tail = S.tail, spl = S.spl;
   int ks = 0, unit0 = -1;
   if (mode == 0) {
     if (spl > 1 && slot >= R * kSlots) {
@@ -335,37 +285,29 @@ __device__ bool resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLd
     unit0 = x * kSlots + slot * spl;
     slot = R * kSlots + slot;
   }
-  if (slot >= CF + CP) return false;
-  const bool is_full = slot < CF;
-  const int q = is_full ? x * CF + slot : (slot - CF) * kXcds + x;
-  if (q >= (is_full ? F : P)) return false;
-  // the entry of the inclusive scan (by group for full tiles, by rank for
-  // partial ones) whose range holds q: the first one above q
-  const int* scan = is_full ? L.pf : L.pp;
+  if (slot >= CF) return false;
+  const int q = x * CF + slot;
+  if (q >= F) return false;
+  // the entry of the inclusive scan by group whose range holds q: the first
+  // one above q
   int lo = 0, hi = ng - 1;
   while (lo < hi) {
     const int mid = (lo + hi) >> 1;
-    if (scan[mid] > q) hi = mid;
+    if (L.pf[mid] > q) hi = mid;
     else lo = mid + 1;
   }
-  const int excl = lo ? scan[lo - 1] : 0;
-  const int grp = is_full ? lo : L.sgrp[lo];
+  const int excl = lo ? L.pf[lo - 1] : 0;
+  const int grp = lo;
   const int o = L.goff[grp], c = L.gcnt[grp];
-  const int mt_g = c / BM;  // full row tiles of the group
-  if (is_full) {
-    const int nt_g = grp < a.E ? ntr : nts;
-    const int local = q - excl;
-    const int blk = local / (mt_g * GN);
-    const int w = min(GN, nt_g - blk * GN);
-    const int li = local - blk * mt_g * GN;
-    t.row0 = o + (li / w) * BM;
-    t.M = BM;
-    t.n0 = (blk * GN + li % w) * BN;
-  } else {
-    t.row0 = o + mt_g * BM;  // the partial row tile
-    t.M = c - mt_g * BM;
-    t.n0 = (q - excl) * BN;
-  }
+  const int mt_g = (c + BM - 1) / BM;  // row tiles of the group, the last one maybe partial
+  const int nt_g = grp < a.E ? ntr : nts;
+  const int local = q - excl;
+  const int blk = local / (mt_g * GN);
+  const int w = min(GN, nt_g - blk * GN);
+  const int li = local - blk * mt_g * GN;
+  t.row0 = o + (li / w) * BM;
+  t.M = min(BM, c - (li / w) * BM);
+  t.n0 = (blk * GN + li % w) * BN;
   t.group = grp < a.E ? 0 : 1;
   t.e = grp < a.E ? grp : 0;
   t.spl = unit0 >= 0 ? spl : 1;
@@ -976,12 +918,11 @@ FfnLayout ffn_layout(const void* xs, const int32_t* gather, int gk, const int32_
       // split K only where every group's K is long (see kSplitMinK)
       const bool long_k = a->routed.K >= kSplitMinK && (a->shared_M == 0 || a->shared.K >= kSplitMinK);
       a->part = long_k ? static_cast<float*>(at(Lo.part)) : nullptr;
-      // worst-case tiles; full and partial runs are each rounded up per XCD
-      // (at most 2*8 extra slots); a split last round adds at most one round
-      // of kSlots per XCD
+      // worst-case tiles rounded up to whole slots of every XCD; a split last
+      // round adds at most one round of kSlots per XCD
       dim3 grid;
       grid_of<256, 256>(*a, rows, E, grid);
-      a->slots = (int)((grid.x + 2 * kXcds + kXcds - 1) / kXcds * kXcds) +
+      a->slots = (int)((grid.x + kXcds - 1) / kXcds * kXcds) +
                  (a->part ? kXcds * kSlots : 0);
       a->table = tab ? tab + table_bytes / sizeof(int4) : nullptr;
       table_bytes += (size_t)(a->slots + kReduceSlots) * 2 * sizeof(int4);
