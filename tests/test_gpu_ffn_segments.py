@@ -1,0 +1,92 @@
+"""Grouped expert FFN on hand-picked segment layouts, through the C ABI
+(moe_expert_ffn), against the oracle's expert FFN segment by segment.
+
+The tile schedule of the 256x256 kernel is built on the device from the
+offsets alone, so these layouts aim at its corners: empty experts, segments of
+1, 255, 256 and 257 rows, rows in several n-blocks of column tiles, every row
+in one expert, the largest expert count, the split-K last round (K >= 8192),
+and the small-segment kernel. ys is filled with NaN first, so a tile that is
+never computed (or computed twice into the wrong rows) cannot pass. Every
+segment must meet the bf16 bar on its own (relative L2 <= 2e-2 against the
+float64 oracle), and so must the shared expert.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_mixture_experts_05_amd as moe
+from synth.workloads import bf16_bits_to_f32, f32_to_bf16_bits
+from tests.parity import TOL_BF16_REL_L2, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+# name, H, F, Fs, counts per expert (or ("zipf", E, rows, seed))
+CASES = [
+    ("ragged_nblocks", 256, 2560, 0, [0, 1, 255, 256, 257, 0, 511, 769]),
+    ("multiples_of_256", 384, 512, 256, [256, 512, 0, 768, 256, 0, 0, 1024]),
+    ("one_hot_expert", 256, 320, 192, [0] * 11 + [1100] + [0] * 4),
+    ("e256_skewed_small_tiles", 128, 192, 0, ("zipf", 256, 22000, 7)),
+    ("e256_skewed_big_tiles", 128, 192, 64, ("zipf", 256, 60000, 7)),
+    ("split_k_tail", 256, 8192, 8192, [300, 0, 129, 40]),
+    ("small_segments", 512, 448, 128, [1, 0, 2, 0, 0, 3, 0, 1, 0, 0, 0, 5, 0, 0, 2, 0]),
+]
+
+
+def _counts(spec):
+    if isinstance(spec, tuple):
+        _, E, rows, seed = spec
+        rng = np.random.default_rng([seed, 1])
+        p = 1.0 / np.arange(1, E + 1) ** 1.1
+        p = p[rng.permutation(E)]
+        p /= p.sum()
+        c = rng.multinomial(rows, p)
+        c[rng.choice(E, size=E // 4, replace=False)] = 0  # some idle experts
+        return c
+    return np.asarray(spec, dtype=np.int64)
+
+
+def _bf16(rng, shape, std):
+    return f32_to_bf16_bits(rng.standard_normal(shape, dtype=np.float32) * np.float32(std))
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_ffn_segments(case):
+    name, H, F, Fs, spec = case
+    counts = _counts(spec)
+    E = len(counts)
+    rows = int(counts.sum())
+    T = max(rows, 1)  # shared-expert rows (the buffer rows themselves serve as x)
+    rng = np.random.default_rng([11, len(name), rows])
+    xs = _bf16(rng, (rows, H), 1.0)
+    w1 = _bf16(rng, (E, F, H), H ** -0.5)
+    w2 = _bf16(rng, (E, H, F), F ** -0.5)
+    ws1 = _bf16(rng, (Fs, H), H ** -0.5) if Fs else None
+    ws2 = _bf16(rng, (H, Fs), Fs ** -0.5) if Fs else None
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    big = rows >= 64 * E
+    print(f"\n[gpu] ffn segments {name}: E={E} rows={rows} H={H} F={F} Fs={Fs} "
+          f"{'256x256 tiles' if big else 'small tiles'} max={counts.max()}", flush=True)
+
+    d_xs = to_dev(xs)
+    ys = torch.full((rows, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    ysh = torch.full((T, H), float("nan"), dtype=torch.bfloat16, device="cuda") if Fs else None
+    moe.moe_expert_ffn(d_xs, to_dev(offsets), to_dev(w1), to_dev(w2),
+                       x=d_xs if Fs else None, ws1=to_dev(ws1), ws2=to_dev(ws2), T=T,
+                       ys=ys, ysh=ysh)
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(to_host(ys)).astype(np.float64)
+    assert np.isfinite(got).all(), "rows left unwritten"
+    for e in range(E):
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        if hi == lo:
+            continue
+        ref = oracle.expert_ffn(xs[lo:hi], w1[e], w2[e])
+        err = np.linalg.norm(got[lo:hi] - ref) / np.linalg.norm(ref)
+        assert err <= TOL_BF16_REL_L2, (e, lo, hi, err)
+    if Fs:
+        gsh = bf16_bits_to_f32(to_host(ysh)).astype(np.float64)
+        ref = oracle.shared_outputs(xs, ws1, ws2)
+        assert np.isfinite(gsh).all()
+        err = np.linalg.norm(gsh - ref) / np.linalg.norm(ref)
+        assert err <= TOL_BF16_REL_L2, err
