@@ -183,14 +183,32 @@ constexpr int kSplitMinK = 8192;
 constexpr int kBigWaves = 8;
 constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
 
+// Small segments inside a big-tile launch. A routed segment of at most 32
+// rows would fill one of the 8 sub-tile rows of a 256x256 tile while the tile
+// streams the whole weight panel and copies 256 (clamped) A rows. Such
+// segments run as 32 x 128 tiles (kSBM x kSBN) instead, two per workgroup (one
+// per half of the 8 waves, each with its own LDS ring), and their slots are
+// spread evenly through each XCD's sequence among the big tiles. Measured on
+// the fine-grained and heavy-skew layers: 1-2% off the FFN; a 128-row limit
+// (up to 4 strips re-reading the same weights) was 3% slower than none. Not in
+// split-K launches, and not for the shared group (the two tiles of a
+// workgroup must have the same K: they meet the same barriers). If the
+// launch's slots cannot hold the pairs, every segment takes big tiles.
+constexpr int kSmallRows = 33;
+constexpr int kSBM = 32, kSBN = 128;
+
 // Tables of the big-tile schedule (per workgroup, in LDS).
 struct SchedLds {
-  int pf[257];               // inclusive scan of the tiles by group
+  int pf[257];               // inclusive scan of the big tiles by group (small mode)
+  int pa[257];               // the same when every segment takes big tiles
+  int ps[257];               // inclusive scan of the small tiles by group
   int goff[257], gcnt[257];  // first row and rows of each group
 };
 
 struct BigSched {
-  int F, CF;         // tiles in all; per XCD
+  const int* pf;     // big-tile scan in use
+  int F, CF;         // big tiles in all; per XCD
+  int P, CP;         // small-tile pairs in all; per XCD
   int R, tail, spl;  // whole rounds per XCD, tiles of the last round, K slices of those
 };
 
@@ -205,6 +223,8 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
   const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
   const int ntr = (a.routed.N + BN - 1) / BN;
   const int nts = (a.shared.N + BN - 1) / BN;
+  const int nsr = (a.routed.N + kSBN - 1) / kSBN;
+  const bool small_ok = a.part == nullptr;
   // thread e: expert e; thread E: the shared group; thread 255 also carries
   // the shared group as group 256 when E == 256
   auto rows_of = [&](int grp, int& off, int& cnt) {
@@ -216,16 +236,21 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
       cnt = a.shared_M;
     }
   };
-  int off = 0, cnt = 0, tiles = 0;
+  int off = 0, cnt = 0, all = 0, big = 0, sml = 0;
   if (act && tid < ng) {
     rows_of(tid, off, cnt);
-    tiles = ((cnt + BM - 1) / BM) * (tid < a.E ? ntr : nts);
+    all = ((cnt + BM - 1) / BM) * (tid < a.E ? ntr : nts);
+    const bool small = small_ok && tid < a.E && cnt > 0 && cnt < kSmallRows;
+    big = small ? 0 : all;
+    sml = small ? ((cnt + kSBM - 1) / kSBM) * nsr : 0;
   }
   const int xtiles = (tid == 255 && ng == 257) ? ((a.shared_M + BM - 1) / BM) * nts : 0;
   if (act) {
     L.goff[tid] = off;
     L.gcnt[tid] = cnt;
-    L.pf[tid] = tiles;
+    L.pa[tid] = all;
+    L.pf[tid] = big;
+    L.ps[tid] = sml;
   }
   if (tid == 255) {
     L.goff[256] = 0;
@@ -233,71 +258,128 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
   }
   __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {
-    const int v = (act && tid >= d) ? L.pf[tid - d] : 0;
+    const int va = (act && tid >= d) ? L.pa[tid - d] : 0;
+    const int vf = (act && tid >= d) ? L.pf[tid - d] : 0;
+    const int vs = (act && tid >= d) ? L.ps[tid - d] : 0;
     __syncthreads();
-    if (act) L.pf[tid] += v;
+    if (act) {
+      L.pa[tid] += va;
+      L.pf[tid] += vf;
+      L.ps[tid] += vs;
+    }
     __syncthreads();
   }
-  if (tid == 255) L.pf[256] = L.pf[255] + xtiles;
+  if (tid == 255) {
+    L.pa[256] = L.pa[255] + xtiles;
+    L.pf[256] = L.pf[255] + xtiles;
+    L.ps[256] = L.ps[255];
+  }
   __syncthreads();
   const int last = ng <= 256 ? ng - 1 : 256;
-  const int F = L.pf[last];
-  const int CF = (F + kXcds - 1) / kXcds;
-  const int R = CF / kSlots, tail = CF - R * kSlots;
-  int spl = 1;
-  if (a.part != nullptr && tail > 0 && 2 * tail <= kSlots) {  // a.part: K long enough
+  BigSched S;
+  const int Fs = L.pf[last], Ps = (L.ps[last] + 1) / 2;
+  const int CFs = (Fs + kXcds - 1) / kXcds, CPs = (Ps + kXcds - 1) / kXcds;
+  if (Ps > 0 && kXcds * (CFs + CPs) <= a.slots) {
+    S.pf = L.pf;
+    S.F = Fs;
+    S.P = Ps;
+  } else {
+    S.pf = L.pa;
+    S.F = L.pa[last];
+    S.P = 0;
+  }
+  S.CF = (S.F + kXcds - 1) / kXcds;
+  S.CP = (S.P + kXcds - 1) / kXcds;
+  S.R = S.CF / kSlots;
+  S.tail = S.CF - S.R * kSlots;
+  S.spl = 1;
+  if (a.part != nullptr && S.tail > 0 && 2 * S.tail <= kSlots) {  // a.part: K long enough
     int ktmin = a.routed.K / 64;
     if (a.shared_M > 0) ktmin = min(ktmin, a.shared.K / 64);
-    spl = max(1, min(min(kSlots / tail, kMaxSplit), ktmin / kMinSliceStages));
+    S.spl = max(1, min(min(kSlots / S.tail, kMaxSplit), ktmin / kMinSliceStages));
   }
-  BigSched S;
-  S.F = F;
-  S.CF = CF;
-  S.R = R;
-  S.tail = tail;
-  S.spl = spl;
   return S;
 }
 
-// Tile of logical slot `slot` on XCD x, resolved by one thread from the
-// schedule tables. mode 0: the tile (or K slice of a split tail tile) to
-// compute; mode 1: the split tail tile number `slot` to reduce. Returns false
-// if the slot holds none.
+// The first entry of an inclusive scan over groups [0, ng) above q.
+__device__ __forceinline__ int scan_find(const int* scan, int ng, int q) {
+  int lo = 0, hi = ng - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi) >> 1;
+    if (scan[mid] > q) hi = mid;
+    else lo = mid + 1;
+  }
+  return lo;
+}
+
+// Small tile u of the launch (u < number of small tiles).
+__device__ __forceinline__ void small_tile_of(const GemmArgs& a, const SchedLds& L, int u,
+                                              Tile& t) {
+  const int grp = scan_find(L.ps, a.E, u);
+  const int li = u - (grp ? L.ps[grp - 1] : 0);
+  const int c = L.gcnt[grp];
+  const int nrs = (c + kSBM - 1) / kSBM;  // row strips of the segment
+  const int r = li % nrs;
+  t.group = 0;
+  t.e = grp;
+  t.row0 = L.goff[grp] + r * kSBM;
+  t.M = min(kSBM, c - r * kSBM);
+  t.n0 = (li / nrs) * kSBN;
+  t.spl = 1;
+  t.ks = 0;
+  t.unit0 = -1;
+}
+
+// Slot `slot` on XCD x, resolved by one thread from the schedule tables.
+// mode 0: the launch's work, kind 0 = one big tile (or K slice of a split
+// tail tile) in ta, kind 1 = a pair of small tiles (ta, and tb unless
+// tb.M == 0); mode 1: the split tail tile number `slot` to reduce (kind 0).
+// Returns -1 if the slot holds nothing.
+// An XCD runs CF big-tile slots and CP pair slots; pair slots sit at the
+// positions s where floor((s + 1) * CP / n) steps (n = CF + CP), evenly
+// spread.
 template <int BM, int BN, int GN>
-__device__ bool resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLds& L, int x,
-                             int slot, int mode, Tile& t) {
+__device__ int resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLds& L, int x,
+                            int slot, int mode, Tile& ta, Tile& tb) {
   const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
   const int ntr = (a.routed.N + BN - 1) / BN;
   const int nts = (a.shared.N + BN - 1) / BN;
   const int F = S.F, CF = S.CF, R = S.R, tail = S.tail, spl = S.spl;
   int ks = 0, unit0 = -1;
   if (mode == 0) {
+    if (S.CP > 0) {  // pairs (never with split K, whose slices sit past CF)
+      const int n = CF + S.CP;
+      if (slot >= n) return -1;
+      const int pb = (int)((long long)slot * S.CP / n);
+      if ((int)((long long)(slot + 1) * S.CP / n) > pb) {  // a pair slot
+        const int p = pb * kXcds + x;
+        if (p >= S.P) return -1;
+        const int nsm = L.ps[a.E - 1];
+        small_tile_of(a, L, 2 * p, ta);
+        if (2 * p + 1 < nsm) small_tile_of(a, L, 2 * p + 1, tb);
+        else tb.M = 0;
+        return 1;
+      }
+      slot -= pb;  // big-tile slots before this one
+    }
     if (spl > 1 && slot >= R * kSlots) {
       const int u = slot - R * kSlots;
-      if (u >= tail * spl) return false;
+      if (u >= tail * spl) return -1;
       const int tt = u / spl;
       ks = u - tt * spl;
       slot = R * kSlots + tt;
       unit0 = x * kSlots + tt * spl;
     }
   } else {
-    if (spl <= 1 || slot >= tail) return false;
+    if (spl <= 1 || slot >= tail) return -1;
     unit0 = x * kSlots + slot * spl;
     slot = R * kSlots + slot;
   }
-  if (slot >= CF) return false;
+  if (slot >= CF) return -1;
   const int q = x * CF + slot;
-  if (q >= F) return false;
-  // the entry of the inclusive scan by group whose range holds q: the first
-  // one above q
-  int lo = 0, hi = ng - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (L.pf[mid] > q) hi = mid;
-    else lo = mid + 1;
-  }
-  const int excl = lo ? L.pf[lo - 1] : 0;
-  const int grp = lo;
+  if (q >= F) return -1;
+  const int grp = scan_find(S.pf, ng, q);
+  const int excl = grp ? S.pf[grp - 1] : 0;
   const int o = L.goff[grp], c = L.gcnt[grp];
   const int mt_g = (c + BM - 1) / BM;  // row tiles of the group, the last one maybe partial
   const int nt_g = grp < a.E ? ntr : nts;
@@ -305,27 +387,29 @@ __device__ bool resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLd
   const int blk = local / (mt_g * GN);
   const int w = min(GN, nt_g - blk * GN);
   const int li = local - blk * mt_g * GN;
-  t.row0 = o + (li / w) * BM;
-  t.M = min(BM, c - (li / w) * BM);
-  t.n0 = (blk * GN + li % w) * BN;
-  t.group = grp < a.E ? 0 : 1;
-  t.e = grp < a.E ? grp : 0;
-  t.spl = unit0 >= 0 ? spl : 1;
-  t.ks = ks;
-  t.unit0 = unit0;
-  return true;
+  ta.row0 = o + (li / w) * BM;
+  ta.M = min(BM, c - (li / w) * BM);
+  ta.n0 = (blk * GN + li % w) * BN;
+  ta.group = grp < a.E ? 0 : 1;
+  ta.e = grp < a.E ? grp : 0;
+  ta.spl = unit0 >= 0 ? spl : 1;
+  ta.ks = ks;
+  ta.unit0 = unit0;
+  return 0;
 }
 
 // Split tail tiles a reduce launch can hold: half a round of every XCD.
 constexpr int kReduceSlots = kXcds * kSlots / 2;
+constexpr int kTableInt4 = 4;  // int4 per table entry
 
-// Writes the tile table of one big-tile launch: two int4 per workgroup slot
-// ({group or -1, expert, row0, M}, {n0, spl, ks, unit0}), slots [0, a.slots)
-// for the GEMM launch (workgroup g: slot g / 8 on XCD g % 8), then
+// Writes the tile table of one big-tile launch, four int4 per workgroup slot:
+// {kind, group a, expert a, row0 a}, {M a, n0 a, spl, ks},
+// {unit0, group b, expert b, row0 b}, {M b, n0 b, 0, 0} (kind -1: nothing,
+// 0: a big tile in a, 1: small tiles a and b, b absent if M b = 0); slots
+// [0, a.slots) for the GEMM launch (workgroup g: slot g / 8 on XCD g % 8), then
 // kReduceSlots for its split-K reduce. Every workgroup computes the same
-// schedule (group ranks and scans, from offsets), then each thread resolves
-// one slot: the GEMM workgroups read one entry instead of each redoing the
-// schedule.
+// schedule (group scans, from offsets), then each thread resolves one slot:
+// the GEMM workgroups read one entry instead of each redoing the schedule.
 template <int BM, int BN, int GN>
 __device__ void plan_launch(const GemmArgs& a, int4* table, SchedLds& L) {
   const BigSched S = big_schedule<BM, BN>(a, L);
@@ -333,10 +417,13 @@ __device__ void plan_launch(const GemmArgs& a, int4* table, SchedLds& L) {
   if (i >= a.slots + kReduceSlots) return;
   const int mode = i < a.slots ? 0 : 1;
   const int g = mode ? i - a.slots : i;
-  Tile t;
-  const bool ok = resolve_slot<BM, BN, GN>(a, S, L, g % kXcds, g / kXcds, mode, t);
-  table[2 * i] = ok ? make_int4(t.group, t.e, t.row0, t.M) : make_int4(-1, 0, 0, 0);
-  table[2 * i + 1] = ok ? make_int4(t.n0, t.spl, t.ks, t.unit0) : make_int4(0, 1, 0, -1);
+  Tile ta{}, tb{};
+  const int kind = resolve_slot<BM, BN, GN>(a, S, L, g % kXcds, g / kXcds, mode, ta, tb);
+  int4* e = table + kTableInt4 * i;
+  e[0] = make_int4(kind, ta.group, ta.e, ta.row0);
+  e[1] = make_int4(ta.M, ta.n0, ta.spl, ta.ks);
+  e[2] = make_int4(ta.unit0, tb.group, tb.e, tb.row0);
+  e[3] = make_int4(kind == 1 ? tb.M : 0, tb.n0, 0, 0);
 }
 
 // One launch plans both GEMMs of the FFN (blockIdx.y: 0 up, 1 down).
@@ -349,20 +436,29 @@ __global__ __launch_bounds__(kThreads) void big_plan_kernel(GemmArgs up, GemmArg
     plan_launch<BM, BN, GN>(down, const_cast<int4*>(down.table), L);
 }
 
-// The tile of table entry i (written by big_plan_kernel).
-__device__ __forceinline__ bool table_tile(const GemmArgs& a, int i, Tile& t) {
-  const int4 d0 = a.table[2 * i];
-  if (d0.x < 0) return false;
-  const int4 d1 = a.table[2 * i + 1];
-  t.group = d0.x;
-  t.e = d0.y;
-  t.row0 = d0.z;
-  t.M = d0.w;
-  t.n0 = d1.x;
-  t.spl = d1.y;
-  t.ks = d1.z;
-  t.unit0 = d1.w;
-  return true;
+// The work of table entry i (written by big_plan_kernel): returns its kind.
+__device__ __forceinline__ int table_entry(const GemmArgs& a, int i, Tile& ta, Tile& tb) {
+  const int4* e = a.table + kTableInt4 * i;
+  const int4 d0 = e[0];
+  if (d0.x < 0) return -1;
+  const int4 d1 = e[1], d2 = e[2], d3 = e[3];
+  ta.group = d0.y;
+  ta.e = d0.z;
+  ta.row0 = d0.w;
+  ta.M = d1.x;
+  ta.n0 = d1.y;
+  ta.spl = d1.z;
+  ta.ks = d1.w;
+  ta.unit0 = d2.x;
+  tb.group = d2.y;
+  tb.e = d2.z;
+  tb.row0 = d2.w;
+  tb.M = d3.x;
+  tb.n0 = d3.y;
+  tb.spl = 1;
+  tb.ks = 0;
+  tb.unit0 = -1;
+  return d0.x;
 }
 
 // ----------------------------------------------------------------- bf16 MFMA
@@ -375,22 +471,31 @@ __device__ __forceinline__ bool table_tile(const GemmArgs& a, int i, Tile& t) {
 // CU). Chunk c of row r sits at slot c ^ ((r >> 1) & 7): the 16 lanes served
 // together by a 128-bit read (16 consecutive rows, one chunk) hit 16
 // distinct 4-bank groups.
+template <int BM, int BN>
+struct SmallTileShape {
+  static constexpr int BK = 64;                           // bf16 elements per K step
+  static constexpr int ROWB = BK * 2;                     // bytes per staged row (128)
+  static constexpr int STAGE = (BM + BN) * ROWB;
+  static constexpr int NS = 3;                            // stages (2 workgroups per CU)
+  static constexpr int LDS = NS * STAGE;
+};
+
+// One small tile computed by 4 waves (wave = 0..3 inside them) with the
+// operand ring at smem. Every LDS hand-off is a workgroup barrier, so all the
+// waves of the workgroup must run the same number of K stages (the paired
+// tiles of the large-tile kernel share their K). store = false runs the tile
+// without writing C (the idle half of an unpaired slot).
 template <int BM, int BN, int WM, int WN>
-__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
-  constexpr int BK = 64;                      // bf16 elements per K step
-  constexpr int ROWB = BK * 2;                // bytes per staged row (128)
+__device__ __forceinline__ void small_tile(const GemmArgs& args, const Tile& t, uint8_t* smem,
+                                           int wave, bool store) {
+  using Sh = SmallTileShape<BM, BN>;
+  constexpr int BK = Sh::BK, ROWB = Sh::ROWB, STAGE = Sh::STAGE, NS = Sh::NS;
   constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
   constexpr int SM = WTM / 32, SN = WTN / 32; // 32x32 sub-tiles per wave
-  constexpr int STAGE = (BM + BN) * ROWB;
-  constexpr int NS = 3;                                   // stages (2 workgroups per CU)
-  constexpr int NI = (BM + BN) / 8 / (kThreads / kWave);  // DMA instructions per wave per stage
+  constexpr int NI = (BM + BN) / 8 / 4;       // DMA instructions per wave per stage
   static_assert(WM * WN <= 4, "at most 4 computing waves");
   static_assert(SM >= 1 && SN >= 1, "tile shape");
   static_assert((BM + BN) % 32 == 0 && NI >= 1 && NI * (NS - 2) < 64, "whole DMA instructions");
-  __shared__ __attribute__((aligned(16))) uint8_t smem[NS * STAGE];
-
-  Tile t;
-  if (!find_tile<BM, BN>(args, t)) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N, K = G.K;
   const uint16_t* A = static_cast<const uint16_t*>(G.A);
@@ -398,7 +503,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
   uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
   const int M = t.M;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63;
   // waves WM*WN .. 3 only take part in the copies (narrow tiles for few rows)
   const bool computes = wave < WM * WN;
   const int wm = computes ? wave / WN : 0, wn = computes ? wave % WN : 0;
@@ -470,7 +575,7 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
 
   // Epilogue. 32x32 D layout: lane holds column lane%32 and rows
   // (v/4)*8 + (lane/32)*4 + v%4 of each sub-tile.
-  if (!computes) return;
+  if (!computes || !store) return;
   const bool gelu = args.gelu != 0;
 #pragma unroll
   for (int i = 0; i < SM; ++i)
@@ -488,6 +593,14 @@ __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
         }
       }
     }
+}
+
+template <int BM, int BN, int WM, int WN>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[SmallTileShape<BM, BN>::LDS];
+  Tile t;
+  if (!find_tile<BM, BN>(args, t)) return;
+  small_tile<BM, BN, WM, WN>(args, t, smem, threadIdx.x >> 6, true);
 }
 
 // ----------------------------------------------------------------- bf16 MFMA, large tiles
@@ -514,8 +627,21 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
   static_assert(A_INST >= 1 && B_INST >= 1 && SM >= 1 && SN >= 1, "tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
 
-  Tile t;
-  if (!table_tile(args, blockIdx.x, t)) return;
+  Tile t, tb;
+  const int kind = table_entry(args, blockIdx.x, t, tb);
+  if (kind < 0) return;
+  if (kind == 1) {
+    // two small tiles of short segments, one per half of the waves, each with
+    // its own LDS ring (the same K, so both halves meet the same barriers); a
+    // slot without a second tile runs the first one twice and stores it once
+    static_assert(NW == 8 && 2 * SmallTileShape<kSBM, kSBN>::LDS <= 2 * STAGE, "two small rings");
+    const int half = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 8));
+    const bool has_b = tb.M > 0;
+    small_tile<kSBM, kSBN, 1, 4>(args, half && has_b ? tb : t,
+                                 smem + half * SmallTileShape<kSBM, kSBN>::LDS,
+                                 (threadIdx.x >> 6) & 3, half == 0 || has_b);
+    return;
+  }
   const Group G = pick_group(args, t.group);
   const int N = G.N, K = G.K;
   const uint16_t* A = static_cast<const uint16_t*>(G.A);
@@ -713,8 +839,8 @@ constexpr int kReduceParts = 8;
 
 template <int BM, int BN>
 __global__ __launch_bounds__(kThreads) void gemm_tail_reduce_kernel(GemmArgs args) {
-  Tile t;
-  if (!table_tile(args, args.slots + blockIdx.x / kReduceParts, t)) return;
+  Tile t, tb;
+  if (table_entry(args, args.slots + blockIdx.x / kReduceParts, t, tb) != 0) return;
   const Group G = pick_group(args, t.group);
   const int N = G.N;
   uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
@@ -925,7 +1051,7 @@ FfnLayout ffn_layout(const void* xs, const int32_t* gather, int gk, const int32_
       a->slots = (int)((grid.x + kXcds - 1) / kXcds * kXcds) +
                  (a->part ? kXcds * kSlots : 0);
       a->table = tab ? tab + table_bytes / sizeof(int4) : nullptr;
-      table_bytes += (size_t)(a->slots + kReduceSlots) * 2 * sizeof(int4);
+      table_bytes += (size_t)(a->slots + kReduceSlots) * kTableInt4 * sizeof(int4);
     }
   }
   Lo.bytes = Lo.table + align256(table_bytes);
