@@ -33,6 +33,11 @@ SMALL = [
     # big-tile two-launch route: 64 x 128 tiles (E <= 128), 128 x 256 tiles (E > 128)
     MoEConfig("route_big_E128", T=2100, H=512, E=128, k=8, F=64, bias_amp=1.5),
     MoEConfig("route_big_E136", T=3100, H=256, E=136, k=4, F=64, bias_amp=1.0),
+    # one-launch route, 16 tokens per workgroup, few experts (panels split over the waves):
+    # ragged token tail, a single stage of K panels (H = 512), one expert
+    MoEConfig("route_bt16_E16_H2048", T=2500, H=2048, E=16, k=4, F=64, bias_amp=1.0),
+    MoEConfig("route_bt16_E4_H512", T=2100, H=512, E=4, k=2, F=64),
+    MoEConfig("route_bt16_E1", T=2048, H=2048, E=1, k=1, F=64),
     # down projection with K = 8192 (routed and shared): the last round is split over K
     MoEConfig("split_k_tail", T=600, H=256, E=4, k=1, F=8192, Fs=8192, bias_amp=0.5),
 ]
