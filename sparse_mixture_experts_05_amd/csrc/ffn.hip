@@ -26,7 +26,7 @@
 //   gemm_bf16_big_kernel   256x256 tiles, 8 waves, two LDS stages, blocked
 //                          XCD-aware tile order, split K in the last round of
 //                          long-K launches (gemm_tail_reduce_kernel sums it);
-//   gemm_bf16_kernel       32x128 or 32x64 tiles for few rows per expert
+//   gemm_bf16_kernel       32x64 tiles for few rows per expert
 //                          (decode): weight streaming through a 3-stage ring.
 // fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
 #include <algorithm>
@@ -964,12 +964,11 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     return hipGetLastError();
   }
   if (small_segments) {
-    // Fewer than two 32x128 tiles per CU (a handful of tokens): 32x64 tiles
-    // double the workgroups streaming the weights.
-    const long long nt128 = (long long)(rows / 32 + std::min(E, rows)) * ((a.routed.N + 127) / 128) +
-                            (long long)((a.shared_M + 31) / 32) * ((a.shared.N + 127) / 128);
-    if (nt128 < 2LL * kXcds * kSlots) return run_bf16<32, 64, 1, 2>(a, rows, E, s);
-    return run_bf16<32, 128, 1, 4>(a, rows, E, s);
+    // 32x64 tiles: 36 KiB rings, so more workgroups per CU keep weight copies
+    // in flight than with 32x128 tiles (measured, graph-replayed decode layer,
+    // H = 4096, E = 128, k = 8: FFN at T = 128 640 -> 603 us, T = 16 426 ->
+    // 412 us, T = 1 unchanged; a four- or five-stage ring gains nothing more)
+    return run_bf16<32, 64, 1, 2>(a, rows, E, s);
   }
   // big tiles: the table was written by big_plan_kernel
   if (a.gelu)
