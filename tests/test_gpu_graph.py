@@ -9,15 +9,22 @@ import pytest
 import torch
 
 import sparse_mixture_experts_05_amd as moe
-from synth import get_config, make_layer, redraw_rows
+from synth import MoEConfig, get_config, make_layer, redraw_rows
 from tests.parity import to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("name", ["decode@T1", "decode@T16"])
-def test_graph_replays_match_eager(name):
-    cfg = get_config(name)
+# decode shapes (small-segment GEMM) and a skewed mid-size layer on the 256x256
+# kernel with its planning launch, split over short segments in tile pairs
+GRAPH_CASES = ["decode@T1", "decode@T16",
+               MoEConfig("graph_big_pairs", T=1024, H=512, E=16, k=4, F=512, Fs=256, bias_amp=2.0)]
+
+
+@pytest.mark.parametrize("case", GRAPH_CASES, ids=lambda c: c if isinstance(c, str) else c.name)
+def test_graph_replays_match_eager(case):
+    cfg = get_config(case) if isinstance(case, str) else case
+    name = cfg.name
     L = make_layer(cfg)
     d = {k: to_dev(v) for k, v in L.items()}
     print(f"\n[gpu] graph {name}", flush=True)
