@@ -484,10 +484,13 @@ struct SmallTileShape {
 // operand ring at smem. Every LDS hand-off is a workgroup barrier, so all the
 // waves of the workgroup must run the same number of K stages (the paired
 // tiles of the large-tile kernel share their K). store = false runs the tile
-// without writing C (the idle half of an unpaired slot).
+// without writing C (the idle half of an unpaired slot). With part, the
+// workgroup computes K slice ks of nks and writes its fp32 partial tile
+// ([BM][BN], rows past M and columns past N left unwritten) there instead of C.
 template <int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void small_tile(const GemmArgs& args, const Tile& t, uint8_t* smem,
-                                           int wave, bool store) {
+                                           int wave, bool store, int ks = 0, int nks = 1,
+                                           float* part = nullptr) {
   using Sh = SmallTileShape<BM, BN>;
   constexpr int BK = Sh::BK, ROWB = Sh::ROWB, STAGE = Sh::STAGE, NS = Sh::NS;
   constexpr int WTM = BM / WM, WTN = BN / WN; // wave tile
@@ -522,11 +525,13 @@ __device__ __forceinline__ void small_tile(const GemmArgs& args, const Tile& t, 
     src[q] = row + chunk * 8;
     dst[q] = g * 8 * ROWB;
   }
-  const int KT = K / BK;
+  const int KT0 = K / BK;
+  const int kbase = ks * KT0 / nks;
+  const int KT = (ks + 1) * KT0 / nks - kbase;
   auto issue = [&](int kt) {
     uint8_t* base = smem + (kt % NS) * STAGE;
 #pragma unroll
-    for (int q = 0; q < NI; ++q) lds_dma16(src[q] + kt * BK, base + dst[q]);
+    for (int q = 0; q < NI; ++q) lds_dma16(src[q] + (kbase + kt) * BK, base + dst[q]);
   };
 
   f32x16_t acc[SM][SN];
@@ -587,6 +592,10 @@ __device__ __forceinline__ void small_tile(const GemmArgs& args, const Tile& t, 
       for (int v = 0; v < 16; ++v) {
         const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
         if (row < M) {
+          if (part != nullptr) {
+            part[row * BN + col] = acc[i][j][v];
+            continue;
+          }
           float y = acc[i][j][v];
           if (gelu) y = gelu_erf(y);
           C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
@@ -595,12 +604,46 @@ __device__ __forceinline__ void small_tile(const GemmArgs& args, const Tile& t, 
     }
 }
 
+// blockIdx.y: K slice of gridDim.y (split K writes fp32 partial tiles to
+// args.part, [workgroup][slice][BM][BN]; gemm_small_reduce_kernel finishes them).
 template <int BM, int BN, int WM, int WN>
 __global__ __launch_bounds__(kThreads) void gemm_bf16_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[SmallTileShape<BM, BN>::LDS];
   Tile t;
   if (!find_tile<BM, BN>(args, t)) return;
-  small_tile<BM, BN, WM, WN>(args, t, smem, threadIdx.x >> 6, true);
+  const int nks = gridDim.y;
+  float* part = nks > 1 ? args.part + ((size_t)blockIdx.x * nks + blockIdx.y) * BM * BN : nullptr;
+  small_tile<BM, BN, WM, WN>(args, t, smem, threadIdx.x >> 6, true, blockIdx.y, nks, part);
+}
+
+// Sums the nks K slices of each split small tile in slice order, then the
+// epilogue of small_tile (erf-GeLU if requested, bf16 rounding, rows past the
+// segment end and columns past N masked). Same grid as the GEMM launch.
+constexpr int kMaxSmallSplit = 8;
+
+template <int BM, int BN>
+__global__ __launch_bounds__(kThreads) void gemm_small_reduce_kernel(GemmArgs args, int nks) {
+  Tile t;
+  if (!find_tile<BM, BN>(args, t)) return;
+  const Group G = pick_group(args, t.group);
+  const int N = G.N;
+  uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
+  const float* P = args.part + (size_t)blockIdx.x * nks * BM * BN;
+  const bool gelu = args.gelu != 0;
+  for (int q = threadIdx.x; q < t.M * BN; q += kThreads) {
+    const int row = q / BN, col = q % BN;
+    if (t.n0 + col >= N) continue;
+    float v[kMaxSmallSplit];
+#pragma unroll
+    for (int s = 0; s < kMaxSmallSplit; ++s)  // all loads first, then the sum in slice order
+      if (s < nks) v[s] = P[(size_t)s * BM * BN + row * BN + col];
+    float y = 0.0f;
+#pragma unroll
+    for (int s = 0; s < kMaxSmallSplit; ++s)
+      if (s < nks) y += v[s];
+    if (gelu) y = gelu_erf(y);
+    C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
+  }
 }
 
 // ----------------------------------------------------------------- bf16 MFMA, large tiles
@@ -946,11 +989,35 @@ void grid_of(GemmArgs& a, int rows, int E, dim3& grid) {
   grid = dim3(a.routed_tiles + shared_tiles);
 }
 
+// K slices of a small-tile launch. With fewer tiles than CUs (a single token:
+// every workgroup would walk all of K alone on a CU of its own) K is split so
+// that about 1024 workgroups stream the weights, each slice at least 8 stages
+// of the routed K; gemm_small_reduce_kernel sums the slices. Measured on the
+// graph-replayed decode layer (H = 4096, E = 128, k = 8, F = 1536 + shared):
+// T = 1 FFN 55.1 -> 48.7 us (216 up-projection tiles, 4 slices); at T = 2
+// (408 tiles) a 2-way split cost 3 us more than it saved, hence the limit.
+constexpr int kSmallBM = 32, kSmallBN = 64;
+
+int small_splits(const GemmArgs& a, int rows, int E) {
+  GemmArgs b = a;
+  dim3 grid;
+  grid_of<kSmallBM, kSmallBN>(b, rows, E, grid);
+  if (grid.x >= (unsigned)(kXcds * kSlots)) return 1;
+  const int by_tiles = (int)(1024 / std::max(1u, grid.x));
+  const int by_k = a.routed.K / 64 / 8;
+  return std::max(1, std::min(std::min(by_tiles, by_k), kMaxSmallSplit));
+}
+
 template <int BM, int BN, int WM, int WN>
-hipError_t run_bf16(GemmArgs a, int rows, int E, hipStream_t s) {
+hipError_t run_bf16(GemmArgs a, int rows, int E, int nks, hipStream_t s) {
   dim3 grid;
   grid_of<BM, BN>(a, rows, E, grid);
+  const unsigned nt = grid.x;
+  grid.y = nks;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nks <= 1) return err;
+  hipLaunchKernelGGL((gemm_small_reduce_kernel<BM, BN>), dim3(nt), dim3(kThreads), 0, s, a, nks);
   return hipGetLastError();
 }
 
@@ -968,7 +1035,8 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     // in flight than with 32x128 tiles (measured, graph-replayed decode layer,
     // H = 4096, E = 128, k = 8: FFN at T = 128 640 -> 603 us, T = 16 426 ->
     // 412 us, T = 1 unchanged; a four- or five-stage ring gains nothing more)
-    return run_bf16<32, 64, 1, 2>(a, rows, E, s);
+    const int nks = a.part != nullptr ? small_splits(a, rows, E) : 1;
+    return run_bf16<kSmallBM, kSmallBN, 1, 2>(a, rows, E, nks, s);
   }
   // big tiles: the table was written by big_plan_kernel
   if (a.gelu)
@@ -1037,6 +1105,21 @@ FfnLayout ffn_layout(const void* xs, const int32_t* gather, int gk, const int32_
   down.gelu = 0;
 
   size_t table_bytes = 0;
+  if (Lo.small_segments) {
+    // split-K partial tiles of launches with few small tiles (part stays null
+    // for a launch that does not split)
+    size_t need = 0;
+    for (GemmArgs* a : {&up, &down}) {
+      const int nks = small_splits(*a, rows, E);
+      if (nks <= 1) continue;
+      dim3 grid;
+      grid_of<kSmallBM, kSmallBN>(*a, rows, E, grid);
+      need = std::max(need, (size_t)grid.x * nks * kSmallBM * kSmallBN * sizeof(float));
+    }
+    for (GemmArgs* a : {&up, &down})
+      a->part = small_splits(*a, rows, E) > 1 ? static_cast<float*>(at(Lo.part)) : nullptr;
+    Lo.table = Lo.part + align256(need);
+  }
   if (Lo.big) {
     int4* tab = static_cast<int4*>(at(Lo.table));
     for (GemmArgs* a : {&up, &down}) {

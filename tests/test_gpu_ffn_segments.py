@@ -5,7 +5,7 @@ The tile schedule of the 256x256 kernel is built on the device from the
 offsets alone, so these layouts aim at its corners: empty experts, segments of
 1, 255, 256 and 257 rows, rows in several n-blocks of column tiles, every row
 in one expert, the largest expert count, the split-K last round (K >= 8192),
-and the small-segment kernel. ys is filled with NaN first, so a tile that is
+and the small-segment kernel, whole-K and split over K. ys is filled with NaN first, so a tile that is
 never computed (or computed twice into the wrong rows) cannot pass. Every
 segment must meet the bf16 bar on its own (relative L2 <= 2e-2 against the
 float64 oracle), and so must the shared expert.
@@ -30,6 +30,8 @@ CASES = [
     ("e256_skewed_big_tiles", 128, 192, 64, ("zipf", 256, 60000, 7)),
     ("split_k_tail", 256, 8192, 8192, [300, 0, 129, 40]),
     ("small_segments", 512, 448, 128, [1, 0, 2, 0, 0, 3, 0, 1, 0, 0, 0, 5, 0, 0, 2, 0]),
+    # a few rows and long K: the small-tile up projection splits K over 8 slices
+    ("small_split_k", 4096, 512, 256, [1, 0, 2, 0, 0, 0, 1, 0]),
 ]
 
 
