@@ -84,12 +84,17 @@ def test_route_workspace():
     assert L.moe_route_workspace_bytes(16, 4096, 300, 8, 1) == 0
     assert L.moe_route_workspace_bytes(2500, 4096, 64, 8, 1) == rows16(2500, 64)
     # two launches: partial scores [slices][T][E] fp32, then (with the mean
-    # probabilities) one row of E floats per 4 tokens. Few tokens, or E > 64 and
-    # T < 6144 (big tiles: 64 x 128 for E <= 128, 128 x 256 above, ~256 workgroups)
+    # probabilities) one row of E floats per select workgroup: 16 tokens from
+    # T = 1024 up, else 4. Few tokens, or E > 64 and T < 6144 (big tiles:
+    # 64 x 128 for E <= 128, 128 x 256 above, ~256 workgroups)
     al = lambda b: -(-b // 256) * 256
     assert L.moe_route_workspace_bytes(2500, 4096, 256, 8, 1) > 2500 * 256 * 4
     assert L.moe_route_workspace_bytes(4096, 4096, 128, 8, 1) == (al(4 * 4096 * 128 * 4)
-                                                                  + al(1024 * 128 * 4))
+                                                                  + al(256 * 128 * 4))
+    # below T = 1024 the select keeps 4 tokens per workgroup (2 K slices of the
+    # 16 x 64 partial tiles at T = 1000, E = 128)
+    assert L.moe_route_workspace_bytes(1000, 4096, 128, 8, 1) == (al(2 * 1000 * 128 * 4)
+                                                                  + al(250 * 128 * 4))
     assert L.moe_route_workspace_bytes(5000, 4096, 256, 8, 1) > 5000 * 256 * 4
     # large batches go back to one launch (64 tokens per workgroup at T = 16384)
     assert L.moe_route_workspace_bytes(16384, 4096, 256, 8, 1) == 256 * 256 * 4
