@@ -279,7 +279,7 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
   BigSched S;
   const int Fs = L.pf[last], Ps = (L.ps[last] + 1) / 2;
   const int CFs = (Fs + kXcds - 1) / kXcds, CPs = (Ps + kXcds - 1) / kXcds;
-  if (Ps > 0 && kXcds * (CFs + CPs) <= a.slots) {
+  if (Ps > 0 && kXcds * (CFs + CPs) <= a.slots && CFs + CPs < (1 << 15)) {
     S.pf = L.pf;
     S.F = Fs;
     S.P = Ps;
@@ -350,8 +350,9 @@ __device__ int resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLds
     if (S.CP > 0) {  // pairs (never with split K, whose slices sit past CF)
       const int n = CF + S.CP;
       if (slot >= n) return -1;
-      const int pb = (int)((long long)slot * S.CP / n);
-      if ((int)((long long)(slot + 1) * S.CP / n) > pb) {  // a pair slot
+      // slot < n < 2^15 and CP < 2^15 (pairs only then): the products fit 32 bits
+      const int pb = (int)((unsigned)(slot * S.CP) / (unsigned)n);
+      if ((int)((unsigned)((slot + 1) * S.CP) / (unsigned)n) > pb) {  // a pair slot
         const int p = pb * kXcds + x;
         if (p >= S.P) return -1;
         const int nsm = L.ps[a.E - 1];

@@ -27,7 +27,7 @@ def sched(counts, Nr, Kr, shared_M, Ns, Ks, part, slots):
         pa.append(allt); pf.append(0 if sm else allt); ps.append(cdiv(c, kSBM) * nsr if sm else 0)
     pa, pf, ps = np.cumsum(pa), np.cumsum(pf), np.cumsum(ps)
     Fs, Ps = pf[-1], (ps[E - 1] + 1) // 2
-    if Ps > 0 and kX * (cdiv(Fs, kX) + cdiv(Ps, kX)) <= slots: use, F, P = pf, Fs, Ps
+    if Ps > 0 and kX * (cdiv(Fs, kX) + cdiv(Ps, kX)) <= slots and cdiv(Fs, kX) + cdiv(Ps, kX) < (1 << 15): use, F, P = pf, Fs, Ps
     else: use, F, P = pa, pa[-1], 0
     CF, CP = cdiv(F, kX), cdiv(P, kX)
     R, tail = CF // kSlots, CF - (CF // kSlots) * kSlots
