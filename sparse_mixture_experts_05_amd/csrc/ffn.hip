@@ -18,7 +18,7 @@
 // sized for the worst case (sum over experts of ceil(count/BM) <= rows/BM +
 // min(E, rows)); surplus workgroups exit at once.
 //
-// Three bf16 kernels, all v_mfma_f32_32x32x16_bf16 with fp32 accumulation and
+// Two bf16 kernels, both v_mfma_f32_32x32x16_bf16 with fp32 accumulation and
 // operands copied global -> LDS by global_load_lds (8 rows of 128 contiguous
 // bytes per instruction), 16-byte chunks XOR-swizzled by row so fragment
 // reads are bank-conflict free; rows past the segment end are clamped on load
@@ -26,8 +26,12 @@
 //   gemm_bf16_big_kernel   256x256 tiles, 8 waves, two LDS stages, blocked
 //                          XCD-aware tile order, split K in the last round of
 //                          long-K launches (gemm_tail_reduce_kernel sums it);
-//   gemm_bf16_kernel       32x64 tiles for few rows per expert
-//                          (decode): weight streaming through a 3-stage ring.
+//                          segments of at most 32 rows as pairs of 32x128
+//                          tiles, one per half of the waves;
+//   gemm_bf16_kernel       32x64 tiles for launches with few rows per expert
+//                          (decode): weight streaming through a 3-stage ring,
+//                          split over K when there are fewer tiles than CUs
+//                          (gemm_small_reduce_kernel sums the slices).
 // fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
 #include <algorithm>
 #include <type_traits>
