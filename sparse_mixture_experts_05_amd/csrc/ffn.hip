@@ -185,6 +185,11 @@ constexpr int kMaxSplit = 8;
 constexpr int kMinSliceStages = 32;  // a slice writes a 256 KB partial: keep it worth it
 constexpr int kSplitMinK = 8192;
 constexpr int kBigWaves = 8;
+// GN of the tile order: column tiles per n-block. Measured against 8 (FFN,
+// same box, two alternating runs): Mixtral-shaped 2162-2166 -> 2133 us,
+// fine-grained 1227-1231 -> 1216 us, heavy-skew unchanged; 16 was 3% slower
+// on the Mixtral-shaped layer, 2 1-2% slower on the heavy-skew one.
+constexpr int kBlockCols = 4;
 constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
 
 // Small segments inside a big-tile launch. A routed segment of at most 32
@@ -1163,7 +1168,7 @@ hipError_t launch_expert_ffn(const void* xs, const int32_t* gather, int gk,
   hipError_t err;
   if (Lo.big) {
     const int n = std::max(Lo.up.slots, Lo.down.slots) + kReduceSlots;
-    hipLaunchKernelGGL((big_plan_kernel<256, 256, 8>), dim3((n + kThreads - 1) / kThreads, 2),
+    hipLaunchKernelGGL((big_plan_kernel<256, 256, kBlockCols>), dim3((n + kThreads - 1) / kThreads, 2),
                        dim3(kThreads), 0, s, Lo.up, Lo.down);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

@@ -11,7 +11,7 @@ device code when that changes; the GPU tests check the device code itself.
 """
 import numpy as np
 # constants of ffn.hip: XCDs, CUs per XCD, split limits, small-segment rows, tile shapes, n-block
-kX, kSlots, kMaxSplit, kMinSlice, kSmallRows, kSBM, kSBN, BM, BN, GN = 8, 32, 8, 32, 33, 32, 128, 256, 256, 8
+kX, kSlots, kMaxSplit, kMinSlice, kSmallRows, kSBM, kSBN, BM, BN, GN = 8, 32, 8, 32, 33, 32, 128, 256, 256, 4
 kReduce = kX * kSlots // 2
 def cdiv(a, b): return (a + b - 1) // b
 def sched(counts, Nr, Kr, shared_M, Ns, Ks, part, slots):
