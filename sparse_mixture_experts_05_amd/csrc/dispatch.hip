@@ -81,8 +81,20 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
     if (nb == 1) {
       total = wcnt[0][tid] + wcnt[1][tid] + wcnt[2][tid] + wcnt[3][tid];
     } else {
+      // 16 loads of the row in flight at a time (exact integer sums)
       const int32_t* row = blk + (size_t)tid * nb;
-      for (int i = 0; i < nb; ++i) {
+      int i = 0;
+      for (; i + 16 <= nb; i += 16) {
+        int c[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) c[u] = row[i + u];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+          total += c[u];
+          if (i + u < b) before += c[u];
+        }
+      }
+      for (; i < nb; ++i) {
         const int c = row[i];
         total += c;
         if (i < b) before += c;
