@@ -233,7 +233,15 @@ __global__ __launch_bounds__(kThreads) void prob_mean_kernel(const float* __rest
                                                              float* __restrict__ prob_mean) {
   for (int e = threadIdx.x; e < E; e += kThreads) {
     double s = 0.0;
-    for (int b = 0; b < nb; ++b) s += (double)part[(size_t)b * E + e];
+    int b = 0;
+    for (; b + 16 <= nb; b += 16) {  // 16 loads in flight, then the sum in order
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = part[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += (double)v[u];
+    }
+    for (; b < nb; ++b) s += (double)part[(size_t)b * E + e];
     prob_mean[e] = (float)(s / (double)T);
   }
 }
