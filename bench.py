@@ -16,7 +16,9 @@ seeded generator. Prints one JSON line:
                per step: up and down projections, 2*rows*H*F flops each),
                against the dense bf16 MFMA peak of 2500 TFLOP/s
   kernels      per-call average ms (p10 / median / p90 too) and the achieved
-               fraction of its roofline
+               fraction of its roofline; route, dispatch and combine also as a
+               fraction of a plain device copy timed in the same run
+               (measured_copy_GB/s)
 With --flush every step starts from cold caches (a 1 GiB write first).
   cpu_baseline the float64 CPU oracle on a bounded sample of the same workload
 """
@@ -334,6 +336,24 @@ def main():
         "kernels": kernels,
         "mfma_util_pct_ffn": 100.0 * achieved / peak,
     }
+    # Context for the datasheet fractions of the HBM-bound steps: a plain
+    # 512 MiB device copy (1 GiB of reads and writes, beyond the last-level
+    # cache) timed with events on the same stream; copy_frac = a step's GB/s
+    # over it.
+    src = torch.empty(CALIB_BYTES, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(5):
+        dst.copy_(src)
+    ev1.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * CALIB_BYTES * 5 / (ev0.elapsed_time(ev1) * 1e-3) / 1e9
+    del src, dst
+    result["measured_copy_GB/s"] = copy_gbs
+    for n in ["route", "dispatch", "combine"]:
+        kernels[n]["copy_frac"] = kernels[n]["GB/s"] / copy_gbs
     if args.copy_calibration:
         # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
         # readings convert those counters to bytes for the kernels above
