@@ -63,3 +63,14 @@ def test_more_than_one_gpu_is_refused():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2
     assert "one GPU" in r.stderr
+
+
+def test_cpu_baseline_repeats_short_samples():
+    from synth.workloads import make_layer
+    cfg = get_config("tiny_fp32")
+    L = make_layer(cfg)
+    cb = bench.cpu_baseline(cfg, L, cfg.T, min_seconds=0.3)
+    assert cb["seconds"] >= 0.3 and cb["kind"] == "oracle" and cb["cores"] >= 1
+    passes = int(cb["sample"].split(" passes")[0])
+    assert passes > 1
+    assert abs(cb["value"] - passes * cfg.T / cb["seconds"]) <= 1e-9 * cb["value"]
