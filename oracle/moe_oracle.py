@@ -27,7 +27,7 @@ Sources (the three web pages this layer is built from):
         layers with GeLU; the dispatcher groups tokens by expert id, runs each
         expert on its group and scatters results back to the original order.
 
-Readings where the pages are silent or garbled (each listed in the design doc):
+Readings where the pages are silent or garbled:
   * the routing bias sits inside the softmax, so it moves both the selection
     and the weights ([DIAG] 4.2);
   * top-k ids are in descending score order; ties go to the lower expert id;
