@@ -314,6 +314,9 @@ def main():
     }
     for n in ["route", "dispatch", "combine"]:
         kernels[n]["hbm_frac"] = kernels[n]["GB/s"] / HBM_PEAK_GBS
+    if not args.copy_gather:
+        kernels["dispatch"]["moves"] = ("ids and indices only (the FFN gathers the token rows "
+                                        "through perm), so launch latency bounds it")
     for n in names:
         p10, p50, p90 = np.percentile(samples[n], [10, 50, 90])
         kernels[n].update(p10_ms=float(p10), median_ms=float(p50), p90_ms=float(p90))

@@ -580,7 +580,9 @@ int bf16_tokens_per_block(int T) { return T >= 64 * 256 ? 64 : T >= 32 * 256 ? 3
 // Tokens per workgroup of the two-launch select: 16 from T = 1024 up (at
 // least 64 workgroups), else 4. Measured on the whole route of the
 // fine-grained layer (T = 4096, H = 4096, E = 128, k = 8): 34.5 -> 33.2 us.
-int select_tokens_per_block(int T) { return T >= 1024 ? 16 : 4; }
+// Up to 4 tokens there is one workgroup either way, and 16 lanes per token
+// merge over fewer levels than 64.
+int select_tokens_per_block(int T) { return T >= 1024 || T <= 4 ? 16 : 4; }
 
 // Workgroups of the launch that runs the top-k (one partial probability row each).
 int topk_blocks(int T, int E, bool bf16) {
