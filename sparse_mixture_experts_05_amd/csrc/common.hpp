@@ -103,4 +103,23 @@ __device__ __forceinline__ void lds_dma16(const void* g, void* lds_uniform) {
       : "memory");
 }
 
+// Value of the partner lane of butterfly level L: xor 1, xor 2, the mirror
+// lane within 8, within 16 (DPP), xor 16 (ds_swizzle), xor 32 (bpermute).
+// Each level pairs two groups that the earlier levels already merged.
+template <int L>
+__device__ __forceinline__ uint32_t partner(uint32_t v) {
+  if constexpr (L == 0) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false);
+  if constexpr (L == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false);
+  if constexpr (L == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false);
+  if constexpr (L == 3) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false);
+  if constexpr (L == 4) return (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x401F);
+  if constexpr (L == 5)
+    return (uint32_t)__builtin_amdgcn_ds_bpermute((int)(((threadIdx.x & 63) ^ 32) * 4), (int)v);
+  return v;
+}
+template <int L>
+__device__ __forceinline__ uint64_t partner64(uint64_t v) {
+  return ((uint64_t)partner<L>((uint32_t)(v >> 32)) << 32) | partner<L>((uint32_t)v);
+}
+
 }  // namespace moe

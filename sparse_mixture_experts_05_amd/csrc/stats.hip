@@ -24,70 +24,126 @@ struct Stats {
   double load_skew_ratio, gini, drop_rate;
 };
 
+// Sum, max and min over the 64 lanes of a wavefront through the partner<L>
+// butterfly (DPP within 16 lanes, then a swizzle and a permute); exact
+// integer arithmetic, so the pairing order does not matter.
+template <int L = 0>
+__device__ __forceinline__ long long wave_sum(long long v) {
+  if constexpr (L < 6) return wave_sum<L + 1>(v + (long long)partner64<L>((uint64_t)v));
+  return v;
+}
+template <int L = 0>
+__device__ __forceinline__ int wave_max(int v) {
+  if constexpr (L < 6) return wave_max<L + 1>(max(v, (int)partner<L>((uint32_t)v)));
+  return v;
+}
+template <int L = 0>
+__device__ __forceinline__ int wave_min(int v) {
+  if constexpr (L < 6) return wave_min<L + 1>(min(v, (int)partner<L>((uint32_t)v)));
+  return v;
+}
+
 __global__ __launch_bounds__(256) void stats_kernel(const int32_t* __restrict__ counts, int T,
                                                     int E, int k, double cf,
                                                     Stats* __restrict__ out,
                                                     int32_t* __restrict__ overflow,
                                                     int32_t* __restrict__ stragglers) {
-  __shared__ int c[256];
-  __shared__ long long red_sum[256], red_isum[256], red_drop[256];
-  __shared__ int red_max[256], red_min[256], red_str[256];
-  const int e = threadIdx.x;
+  __shared__ __align__(16) int c[256];
+  __shared__ __align__(16) uint32_t key[256];
+  __shared__ long long w_sum[4], w_isum[4], w_drop[4];
+  __shared__ int w_max[4], w_min[4], w_str[4];
+  const int e = threadIdx.x, lane = e & 63, wave = e >> 6;
   const long long assignments = (long long)T * k;
   const long long capacity = (long long)(((double)assignments / (double)E) * cf);
   const int ce = e < E ? counts[e] : 0;
+  // With every count in [0, 2^24), (count << 8 | id) is a unique key whose
+  // unsigned order is (count, id): one compare per pair. Padding keys are
+  // never below a real one. Other counts take the plain comparisons.
   c[e] = ce;
-  __syncthreads();
+  key[e] = e < E ? ((uint32_t)ce << 8) | (uint32_t)e : 0xFFFFFFFFu;
+  const bool packed = !__syncthreads_or(e < E && (uint32_t)ce >= (1u << 24));
   long long rank = 0;  // 1-based ascending rank of c[e]
   int strag = 0;
   long long over = 0;
   if (e < E) {
+    // 32 counts per round, all LDS reads issued before the comparisons
     int less = 0;
-    for (int q = 0; q < E; ++q) less += (c[q] < ce) || (c[q] == ce && q < e);
+    if (packed) {
+      const uint32_t mine = ((uint32_t)ce << 8) | (uint32_t)e;
+      const uint4* k4 = reinterpret_cast<const uint4*>(key);
+      for (int q0 = 0; q0 < E; q0 += 32) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = k4[q0 / 4 + u];
+#pragma unroll
+        for (int u = 0; u < 8; ++u)
+          less += (int)(v[u].x < mine) + (int)(v[u].y < mine) + (int)(v[u].z < mine) +
+                  (int)(v[u].w < mine);
+      }
+    }
+    const int4* c4 = reinterpret_cast<const int4*>(c);
+    for (int q0 = 0; !packed && q0 < E; q0 += 32) {
+      int4 v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = c4[q0 / 4 + u];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int q = q0 + 4 * u;
+        less += (q + 0 < E) & ((v[u].x < ce) | ((v[u].x == ce) & (q + 0 < e)));
+        less += (q + 1 < E) & ((v[u].y < ce) | ((v[u].y == ce) & (q + 1 < e)));
+        less += (q + 2 < E) & ((v[u].z < ce) | ((v[u].z == ce) & (q + 2 < e)));
+        less += (q + 3 < E) & ((v[u].w < ce) | ((v[u].w == ce) & (q + 3 < e)));
+      }
+    }
     rank = less + 1;
     over = ce > capacity ? ce - capacity : 0;
     strag = ce > capacity;
     if (overflow != nullptr) overflow[e] = (int32_t)over;
   }
-  red_sum[e] = ce;
-  red_isum[e] = rank * ce;
-  red_drop[e] = over;
-  red_max[e] = e < E ? ce : INT_MIN;
-  red_min[e] = e < E ? ce : INT_MAX;
-  red_str[e] = strag;
+  // per-wavefront totals, then the four wavefronts in LDS; the straggler
+  // flags become positions in the ascending id list through a ballot
+  const long long s_sum = wave_sum(ce);
+  const long long s_isum = wave_sum(rank * ce);
+  const long long s_drop = wave_sum(over);
+  const int s_max = wave_max(e < E ? ce : INT_MIN);
+  const int s_min = wave_min(e < E ? ce : INT_MAX);
+  const unsigned long long smask = __ballot(strag);
+  if (lane == 0) {
+    w_sum[wave] = s_sum;
+    w_isum[wave] = s_isum;
+    w_drop[wave] = s_drop;
+    w_max[wave] = s_max;
+    w_min[wave] = s_min;
+    w_str[wave] = __popcll(smask);
+  }
   __syncthreads();
-  // Inclusive scan of the straggler flags (for the ascending id list) and
-  // tree reductions of the rest, 8 steps over 256 entries.
-  for (int d = 1; d < 256; d <<= 1) {
-    const int v = e >= d ? red_str[e - d] : 0;
-    __syncthreads();
-    red_str[e] += v;
-    __syncthreads();
+  int before = 0, nstrag = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    if (w < wave) before += w_str[w];
+    nstrag += w_str[w];
   }
-  for (int d = 128; d > 0; d >>= 1) {
-    if (e < d) {
-      red_sum[e] += red_sum[e + d];
-      red_isum[e] += red_isum[e + d];
-      red_drop[e] += red_drop[e + d];
-      red_max[e] = max(red_max[e], red_max[e + d]);
-      red_min[e] = min(red_min[e], red_min[e + d]);
-    }
-    __syncthreads();
-  }
-  const int nstrag = red_str[255];
   if (e < E) {
-    if (strag) stragglers[red_str[e] - 1] = e;
+    if (strag) stragglers[before + __popcll(smask & ((1ull << lane) - 1))] = e;
     if (e >= nstrag) stragglers[e] = -1;
   }
   if (e == 0) {
-    const long long total = red_sum[0];
-    const long long dropped = red_drop[0];
+    long long total = 0, isum = 0, dropped = 0;
+    int mx = INT_MIN, mn = INT_MAX;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      total += w_sum[w];
+      isum += w_isum[w];
+      dropped += w_drop[w];
+      mx = max(mx, w_max[w]);
+      mn = min(mn, w_min[w]);
+    }
     Stats s;
     s.num_tokens = T;
     s.assignments = assignments;
     s.capacity = capacity;
-    s.max_load = red_max[0];
-    s.min_load = red_min[0];
+    s.max_load = mx;
+    s.min_load = mn;
     s.dropped = dropped;
     s.num_stragglers = nstrag;
     if (total == 0) {
@@ -95,7 +151,7 @@ __global__ __launch_bounds__(256) void stats_kernel(const int32_t* __restrict__ 
       s.gini_den = 1;
       s.gini = 0.0;
     } else {
-      s.gini_num = 2 * red_isum[0] - (long long)(E + 1) * total;
+      s.gini_num = 2 * isum - (long long)(E + 1) * total;
       s.gini_den = (long long)E * total;
       s.gini = (double)s.gini_num / (double)s.gini_den;
     }
