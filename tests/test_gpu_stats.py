@@ -33,7 +33,7 @@ def _cases():
     yield "at_2^24_E64", np.concatenate([[2 ** 24], rng.integers(0, 100, size=63)]), 1 << 20, 8, 1.25
     yield "near_int32_E256", rng.integers(2 ** 31 - 1000, 2 ** 31 - 1, size=256), 1 << 24, 8, 1.25
     yield "near_int32_ties_E33", np.repeat([2 ** 31 - 2, 2 ** 31 - 5, 3], 11), 1 << 24, 2, 1.0
-    yield "E1_big", np.array([2 ** 30]), 1 << 27, 8, 1.25
+    yield "E1_big", np.array([2 ** 30]), 1 << 28, 1, 1.25
 
 
 CASES = list(_cases())
