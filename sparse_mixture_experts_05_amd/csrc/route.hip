@@ -478,30 +478,59 @@ __global__ __launch_bounds__(kThreads) void route_partial_kernel(const uint16_t*
 template <int NKS, int BT>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __restrict__ ws,
                                                                 const float* __restrict__ bias,
-                                                                int T, int E, int k, int nks,
+                                                                int T, int E, int k,
                                                                 int32_t* __restrict__ topk_idx,
                                                                 float* __restrict__ topk_w,
                                                                 float* __restrict__ ppart) {
   constexpr int S = tile_stride<BT>();
   __shared__ float sc[BT * S];
   const int t0 = blockIdx.x * BT;
-  for (int p = threadIdx.x; p < BT * E; p += kThreads) {
-    const int t = p / E, e = p % E;
-    if (t0 + t < T) {
-      float v[NKS];
+  // PER entries per thread at a time (about 32 loads in flight): all their
+  // slice loads are issued first, from addresses clamped into the buffer, then
+  // each entry is summed in slice order
+  constexpr int PER = NKS >= 8 ? 32 / NKS : 8;
+  const int nval = min(BT, T - t0) * E;  // entries of the tile's real tokens (t-major)
+  for (int p0 = threadIdx.x; p0 < nval; p0 += PER * kThreads) {
+    float v[PER][NKS], bv[PER];
 #pragma unroll
-      for (int q = 0; q < NKS; ++q)  // all loads first, then the sum in slice order
-        v[q] = q < nks ? ws[((size_t)q * T + t0 + t) * E + e] : 0.0f;
-      float s = 0.0f;
+    for (int i = 0; i < PER; ++i) {
+      const int p = p0 + i * kThreads;
+      const int tt = min(t0 + p / E, T - 1), e = p % E;
 #pragma unroll
-      for (int q = 0; q < NKS; ++q)
-        if (q < nks) s += v[q];
-      sc[t * S + e] = bias != nullptr ? s + bias[e] : s;
+      for (int q = 0; q < NKS; ++q) v[i][q] = ws[((size_t)q * T + tt) * E + e];
+      bv[i] = bias != nullptr ? bias[e] : 0.0f;
+    }
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+      const int p = p0 + i * kThreads;
+      const int t = p / E, e = p % E;
+      if (p < nval) {
+        float s = 0.0f;
+#pragma unroll
+        for (int q = 0; q < NKS; ++q) s += v[i][q];
+        sc[t * S + e] = bias != nullptr ? s + bv[i] : s;
+      }
     }
   }
   __syncthreads();
   topk_phase<BT>(sc, t0, T, E, k, topk_idx, topk_w,
                  ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+}
+
+// The select for exactly nks K slices (a power of two up to kMaxSlices).
+template <int BT>
+hipError_t launch_select(int nks, const float* ws, const float* bias, int T, int E, int k,
+                         int32_t* idx, float* w, float* pp, hipStream_t s) {
+  const dim3 grid((T + BT - 1) / BT), block(kThreads);
+  switch (nks) {
+    case 1: hipLaunchKernelGGL((route_select_kernel<1, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 2: hipLaunchKernelGGL((route_select_kernel<2, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 4: hipLaunchKernelGGL((route_select_kernel<4, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 8: hipLaunchKernelGGL((route_select_kernel<8, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 16: hipLaunchKernelGGL((route_select_kernel<16, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // Path of a route call. Both two-launch paths write and re-read T x E partial
@@ -620,14 +649,10 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
     }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
-    if (select_tokens_per_block(T) == 16)
-      hipLaunchKernelGGL((route_select_kernel<kMaxSlices, 16>), dim3((T + 15) / 16), dim3(kThreads),
-                         0, s, static_cast<const float*>(ws), bias, T, E, k, nks, topk_idx, topk_w,
-                         pp);
-    else
-      hipLaunchKernelGGL((route_select_kernel<kMaxSlices, 4>), dim3((T + 3) / 4), dim3(kThreads), 0,
-                         s, static_cast<const float*>(ws), bias, T, E, k, nks, topk_idx, topk_w, pp);
-    err = hipGetLastError();
+    const float* wsf = static_cast<const float*>(ws);
+    err = select_tokens_per_block(T) == 16
+              ? launch_select<16>(nks, wsf, bias, T, E, k, topk_idx, topk_w, pp, s)
+              : launch_select<4>(nks, wsf, bias, T, E, k, topk_idx, topk_w, pp, s);
   } else if (!bf16) {
     const int grid = (T + 15) / 16;
     hipLaunchKernelGGL(route_f32_kernel, dim3(grid), dim3(kThreads), 0, s,
