@@ -41,6 +41,8 @@ __device__ __forceinline__ int expert_of(const int32_t* idx, int a, int E) {
 constexpr int kThreads = 256;
 constexpr int kBlockTokens = 256;  // tokens per hist/rank workgroup (64 per wave)
 
+// KP: k rounded up to a power of two (each thread holds KP ids).
+template <int KP>
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int E, int k, int nb,
                                                         int32_t* __restrict__ blk) {
@@ -49,11 +51,23 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   __syncthreads();
   const int a0 = blockIdx.x * kBlockTokens * k;
   const int a1 = min(T, (blockIdx.x + 1) * kBlockTokens) * k;
-  for (int a = a0 + threadIdx.x; a < a1; a += kThreads) atomicAdd(&h[expert_of(idx, a, E)], 1);
+  // a1 - a0 <= kThreads * k: every id of the block is one of this thread's
+  // KP, all loaded before the first count
+  int ids[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int a = a0 + threadIdx.x + kThreads * i;
+    const int e = expert_of(idx, min(a, a1 - 1), E);  // unconditional load, in bounds
+    ids[i] = a < a1 ? e : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    if (ids[i] >= 0) atomicAdd(&h[ids[i]], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += kThreads) blk[(size_t)e * nb + blockIdx.x] = h[e];
 }
 
+template <int KP>
 __global__ __launch_bounds__(kThreads) void rank_kernel(
     const int32_t* __restrict__ idx, int T, int E, int k, int nb, int cap,
     const int32_t* __restrict__ blk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -70,7 +84,18 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   __syncthreads();
   const int tw0 = b * kBlockTokens + wave * 64;  // first token of this wave
   const int a0 = min(tw0, T) * k, a1 = min(tw0 + 64, T) * k;
-  for (int a = a0 + lane; a < a1; a += 64) atomicAdd(&wcnt[wave][expert_of(idx, a, E)], 1);
+  // a1 - a0 <= 64 * k: the wave's ids, KP per lane, all loaded up front
+  // (row-major (t, j) order: id i of lane l is assignment a0 + 64 i + l)
+  int ids[KP];
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int a = a0 + lane + 64 * i;
+    const int e = expert_of(idx, max(min(a, a1 - 1), 0), E);  // unconditional load, in bounds
+    ids[i] = a < a1 ? e : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < KP; ++i)
+    if (ids[i] >= 0) atomicAdd(&wcnt[wave][ids[i]], 1);
   __syncthreads();
 
   // Totals over all blocks and this block's prefix over earlier blocks. A
@@ -132,10 +157,13 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   int bits = 1;
   while ((1 << bits) < E + 1) ++bits;  // ids 0..E-1 plus the idle-lane id E
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int c0 = a0; c0 < a1; c0 += 64) {
+#pragma unroll
+  for (int i = 0; i < KP; ++i) {
+    const int c0 = a0 + 64 * i;
+    if (c0 >= a1) break;
     const int a = c0 + lane;
     const bool valid = a < a1;
-    const int e = valid ? expert_of(idx, a, E) : E;
+    const int e = valid ? ids[i] : E;
     uint64_t peers = ~0ull;
     for (int bt = 0; bt < bits; ++bt) {
       const uint64_t bal = __ballot((e >> bt) & 1);
@@ -194,6 +222,22 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const V* __restrict__
 
 }  // namespace
 
+template <int KP>
+hipError_t launch_hist(const int32_t* idx, int T, int E, int k, int nb, int32_t* blk,
+                       hipStream_t s) {
+  hipLaunchKernelGGL(hist_kernel<KP>, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb, blk);
+  return hipGetLastError();
+}
+
+template <int KP>
+hipError_t launch_rank(const int32_t* idx, int T, int E, int k, int nb, int cap,
+                       const int32_t* blk, int32_t* counts, int32_t* offsets, int32_t* perm,
+                       int32_t* inv, hipStream_t s) {
+  hipLaunchKernelGGL(rank_kernel<KP>, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb, cap, blk,
+                     counts, offsets, perm, inv);
+  return hipGetLastError();
+}
+
 int dispatch_blocks(int T) { return (T + kBlockTokens - 1) / kBlockTokens; }
 
 size_t dispatch_ws_bytes(int T, int E) {
@@ -208,13 +252,16 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H,
   int32_t* blk = static_cast<int32_t*>(ws);
   hipError_t err;
   if (nb > 1) {  // one block (T <= 256) counts its own histogram in the rank kernel
-    hipLaunchKernelGGL(hist_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, blk);
-    err = hipGetLastError();
+    err = k <= 1   ? launch_hist<1>(topk_idx, T, E, k, nb, blk, s)
+          : k <= 2 ? launch_hist<2>(topk_idx, T, E, k, nb, blk, s)
+          : k <= 4 ? launch_hist<4>(topk_idx, T, E, k, nb, blk, s)
+                   : launch_hist<8>(topk_idx, T, E, k, nb, blk, s);
     if (err != hipSuccess) return err;
   }
-  hipLaunchKernelGGL(rank_kernel, dim3(nb), dim3(kThreads), 0, s, topk_idx, T, E, k, nb, cap,
-                     blk, counts, offsets, perm, inv);
-  err = hipGetLastError();
+  err = k <= 1   ? launch_rank<1>(topk_idx, T, E, k, nb, cap, blk, counts, offsets, perm, inv, s)
+        : k <= 2 ? launch_rank<2>(topk_idx, T, E, k, nb, cap, blk, counts, offsets, perm, inv, s)
+        : k <= 4 ? launch_rank<4>(topk_idx, T, E, k, nb, cap, blk, counts, offsets, perm, inv, s)
+                 : launch_rank<8>(topk_idx, T, E, k, nb, cap, blk, counts, offsets, perm, inv, s);
   if (err != hipSuccess || xs == nullptr) return err;  // no xs: ranks only (gather fused downstream)
   const int row_bytes = H * (bf16 ? 2 : 4);
   const int grid = (T + 3) / 4;
