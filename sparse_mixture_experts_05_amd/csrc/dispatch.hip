@@ -197,15 +197,16 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const V* __restrict__
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * (kThreads / kWave) + (threadIdx.x >> 6);
   if (t >= T) return;
+  // loads from indices clamped into the buffers (no branch and no wait per
+  // load); the stores below skip the entries past k and past the row
   int dst[8];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dst[j] = j < k ? inv[(size_t)t * k + j] : 0;
+  for (int j = 0; j < 8; ++j) dst[j] = inv[(size_t)t * k + min(j, k - 1)];
   const V* src = x + (size_t)t * vec_per_row;
   for (int c = lane; c < vec_per_row; c += 4 * kWave) {
     V v[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-      if (c + u * kWave < vec_per_row) v[u] = src[c + u * kWave];
+    for (int u = 0; u < 4; ++u) v[u] = src[min(c + u * kWave, vec_per_row - 1)];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       if (j < k) {
