@@ -644,11 +644,9 @@ __global__ __launch_bounds__(kThreads) void gemm_small_reduce_kernel(GemmArgs ar
     const int row = q / BN, col = q % BN;
     if (t.n0 + col >= N) continue;
     float v[kMaxSmallSplit];
-    // all loads first (slices past nks re-read the last one: no branch, no
-    // wait per load), then the sum in slice order
 #pragma unroll
-    for (int s = 0; s < kMaxSmallSplit; ++s)
-      v[s] = P[(size_t)min(s, nks - 1) * BM * BN + row * BN + col];
+    for (int s = 0; s < kMaxSmallSplit; ++s)  // all loads first, then the sum in slice order
+      if (s < nks) v[s] = P[(size_t)s * BM * BN + row * BN + col];
     float y = 0.0f;
 #pragma unroll
     for (int s = 0; s < kMaxSmallSplit; ++s)
