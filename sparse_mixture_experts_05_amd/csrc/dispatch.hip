@@ -10,12 +10,13 @@
 //
 // Three launches (two when T <= 256: one block counts its own histogram),
 // all deterministic (no order-dependent atomics):
-//   hist    - one workgroup per 256-token block: LDS-privatised histogram,
-//             written expert-major as blk[e * nb + b].
+//   hist    - one workgroup per block of bt tokens (64 for 256 < T <= 4096
+//             and k >= 4, else 256): LDS-privatised histogram, written
+//             expert-major as blk[e * nb + b].
 //   rank    - one workgroup per block: every workgroup reads the whole
 //             [E x nb] table (tiny, L2 resident) to get the expert offsets
 //             (exclusive scan over experts) and its own prefix over earlier
-//             blocks; then each wave walks its 64 tokens' assignments in order,
+//             blocks; then each wave walks its bt/4 tokens' assignments in order,
 //             64 at a time, ranking equal expert ids with ballots (a lane's
 //             rank = earlier lanes with the same id) on top of per-wave running
 //             counters. Writes perm and inv (block 0 also counts and offsets).
@@ -39,18 +40,18 @@ __device__ __forceinline__ int expert_of(const int32_t* idx, int a, int E) {
 }
 
 constexpr int kThreads = 256;
-constexpr int kBlockTokens = 256;  // tokens per hist/rank workgroup (64 per wave)
 
-// KP: k rounded up to a power of two (each thread holds KP ids).
-template <int KP>
+// KP: k rounded up to a power of two (each thread holds KP ids); BT: tokens
+// per block.
+template <int KP, int BT>
 __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restrict__ idx, int T,
                                                         int E, int k, int nb,
                                                         int32_t* __restrict__ blk) {
   __shared__ int h[256];
   for (int e = threadIdx.x; e < E; e += kThreads) h[e] = 0;
   __syncthreads();
-  const int a0 = blockIdx.x * kBlockTokens * k;
-  const int a1 = min(T, (blockIdx.x + 1) * kBlockTokens) * k;
+  const int a0 = blockIdx.x * BT * k;
+  const int a1 = min(T, (blockIdx.x + 1) * BT) * k;
   // a1 - a0 <= kThreads * k: every id of the block is one of this thread's
   // KP, all loaded before the first count
   int ids[KP];
@@ -67,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void hist_kernel(const int32_t* __restric
   for (int e = threadIdx.x; e < E; e += kThreads) blk[(size_t)e * nb + blockIdx.x] = h[e];
 }
 
-template <int KP>
+template <int KP, int BT>
 __global__ __launch_bounds__(kThreads) void rank_kernel(
     const int32_t* __restrict__ idx, int T, int E, int k, int nb, int cap,
     const int32_t* __restrict__ blk, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
@@ -82,9 +83,10 @@ __global__ __launch_bounds__(kThreads) void rank_kernel(
   // Per-wave counts of this block (order-free integer adds).
   for (int w = 0; w < 4; ++w) wcnt[w][tid] = 0;
   __syncthreads();
-  const int tw0 = b * kBlockTokens + wave * 64;  // first token of this wave
-  const int a0 = min(tw0, T) * k, a1 = min(tw0 + 64, T) * k;
-  // a1 - a0 <= 64 * k: the wave's ids, KP per lane, all loaded up front
+  constexpr int wt = BT / 4;              // tokens per wave (at most 64)
+  const int tw0 = b * BT + wave * wt;     // first token of this wave
+  const int a0 = min(tw0, T) * k, a1 = min(tw0 + wt, T) * k;
+  // a1 - a0 <= wt * k <= 64 * k: the wave's ids, KP per lane, all loaded up front
   // (row-major (t, j) order: id i of lane l is assignment a0 + 64 i + l)
   int ids[KP];
 #pragma unroll
@@ -223,10 +225,20 @@ __global__ __launch_bounds__(kThreads) void scatter_kernel(const V* __restrict__
 
 }  // namespace
 
+// Tokens per hist/rank workgroup. Up to 256 tokens one workgroup does it all
+// (no histogram launch). Up to 4096 tokens with k >= 4, 64-token blocks spread
+// the ranking over up to 64 workgroups (each wave still ranks 64 or more ids).
+// Otherwise 256-token blocks: they keep each wave's 64 lanes busy at small k,
+// and keep short the [E x nb] table rows that every rank workgroup reads.
+int dispatch_block_tokens(int T, int k) { return T > 256 && T <= 4096 && k >= 4 ? 64 : 256; }
+
 template <int KP>
 hipError_t launch_hist(const int32_t* idx, int T, int E, int k, int nb, int32_t* blk,
                        hipStream_t s) {
-  hipLaunchKernelGGL(hist_kernel<KP>, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb, blk);
+  if (dispatch_block_tokens(T, k) == 64)
+    hipLaunchKernelGGL((hist_kernel<KP, 64>), dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb, blk);
+  else
+    hipLaunchKernelGGL((hist_kernel<KP, 256>), dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb, blk);
   return hipGetLastError();
 }
 
@@ -234,22 +246,29 @@ template <int KP>
 hipError_t launch_rank(const int32_t* idx, int T, int E, int k, int nb, int cap,
                        const int32_t* blk, int32_t* counts, int32_t* offsets, int32_t* perm,
                        int32_t* inv, hipStream_t s) {
-  hipLaunchKernelGGL(rank_kernel<KP>, dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb, cap, blk,
-                     counts, offsets, perm, inv);
+  if (dispatch_block_tokens(T, k) == 64)
+    hipLaunchKernelGGL((rank_kernel<KP, 64>), dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb,
+                       cap, blk, counts, offsets, perm, inv);
+  else
+    hipLaunchKernelGGL((rank_kernel<KP, 256>), dim3(nb), dim3(kThreads), 0, s, idx, T, E, k, nb,
+                       cap, blk, counts, offsets, perm, inv);
   return hipGetLastError();
 }
 
-int dispatch_blocks(int T) { return (T + kBlockTokens - 1) / kBlockTokens; }
+int dispatch_blocks(int T, int k) {
+  const int bt = dispatch_block_tokens(T, k);
+  return (T + bt - 1) / bt;
+}
 
-size_t dispatch_ws_bytes(int T, int E) {
-  const size_t b = (size_t)E * dispatch_blocks(T) * sizeof(int32_t);
+size_t dispatch_ws_bytes(int T, int E, int k) {
+  const size_t b = (size_t)E * dispatch_blocks(T, k) * sizeof(int32_t);
   return (b + 255) & ~size_t(255);
 }
 
 hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
                            int cap, bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, void* xs, void* ws, hipStream_t s) {
-  const int nb = dispatch_blocks(T);
+  const int nb = dispatch_blocks(T, k);
   int32_t* blk = static_cast<int32_t*>(ws);
   hipError_t err;
   if (nb > 1) {  // one block (T <= 256) counts its own histogram in the rank kernel

@@ -12,8 +12,8 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
                         int k, bool bf16, int32_t* topk_idx, float* topk_w, float* prob_mean,
                         void* ws, hipStream_t s);
 
-int dispatch_blocks(int T);
-size_t dispatch_ws_bytes(int T, int E);
+int dispatch_blocks(int T, int k);
+size_t dispatch_ws_bytes(int T, int E, int k);
 hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
                            int cap, bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, void* xs, void* ws, hipStream_t s);

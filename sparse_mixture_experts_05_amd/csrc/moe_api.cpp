@@ -68,7 +68,7 @@ int moe_route(const void* x, const void* wg, const float* bias, int T, int H, in
 
 size_t moe_dispatch_workspace_bytes(int T, int E, int k) {
   if (check_tokens(T, 64, E, k) != MOE_OK) return 0;
-  return moe::dispatch_ws_bytes(T, E);
+  return moe::dispatch_ws_bytes(T, E, k);
 }
 
 int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k, int dtype,
@@ -79,7 +79,7 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
   if (xs && (!x || !aligned16(x) || !aligned16(xs))) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
-  if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_dispatch(topk_idx, x, T, H, E, k, -1, dtype == MOE_BF16, counts,
                                        offsets, perm, inv, xs, ws, as_stream(stream)));
 }
@@ -92,7 +92,7 @@ int moe_dispatch_capped(const int32_t* topk_idx, const void* x, int T, int H, in
   if (xs && (!x || !aligned16(x) || !aligned16(xs))) return MOE_ERR_INVALID_ARG;
   const int st = check_tokens(T, H, E, k);
   if (st != MOE_OK) return st;
-  if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E)) return MOE_ERR_WORKSPACE;
+  if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_dispatch(topk_idx, x, T, H, E, k, capacity, dtype == MOE_BF16,
                                        counts, offsets, perm, inv, xs, ws, as_stream(stream)));
 }

@@ -139,6 +139,15 @@ def test_dispatch_validation_and_workspace():
     need = L.moe_dispatch_workspace_bytes(4096, 128, 8)
     assert need >= 128 * 16 * 4 and need % 256 == 0
     assert L.moe_dispatch_workspace_bytes(4096, 300, 8) == 0
+    # one [E x blocks] int32 table: 64-token blocks for 256 < T <= 4096 and
+    # k >= 4, else 256-token blocks (one block up to T = 256)
+    al = lambda b: -(-b // 256) * 256
+    assert need == al(128 * 64 * 4)
+    assert L.moe_dispatch_workspace_bytes(4096, 8, 2) == al(8 * 16 * 4)
+    assert L.moe_dispatch_workspace_bytes(257, 128, 4) == al(128 * 5 * 4)
+    assert L.moe_dispatch_workspace_bytes(256, 128, 8) == al(128 * 1 * 4)
+    assert L.moe_dispatch_workspace_bytes(4097, 128, 8) == al(128 * 17 * 4)
+    assert L.moe_dispatch_workspace_bytes(16384, 256, 8) == al(256 * 64 * 4)
     args = [FAKE, FAKE, 4096, 4096, 128, 8, 1, FAKE, FAKE, FAKE, FAKE, FAKE]
     assert L.moe_dispatch(*args, None, need, None) == -3
     assert L.moe_dispatch(*args, FAKE, need - 1, None) == -3
