@@ -83,16 +83,16 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
   for (int c0 = cbeg + lane; c0 < cend; c0 += U * kWave) {
+    // every load unconditional, from a column clamped into the segment and a
+    // row clamped into the buffer (a dropped row reads row 0 and adds
+    // nothing), so all U * KM loads are in flight before the first wait
     uint4 v[U][KM], sh[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = c0 + u * kWave;
-      if (c < cend) {
+      const int c = min(c0 + u * kWave, cend - 1);
 #pragma unroll
-        for (int j = 0; j < KM; ++j)
-          if (keep[j]) v[u][j] = ld_row<NT>(&ys[(size_t)row[j] * vpr + c]);
-        if (ysh != nullptr) sh[u] = ld_row<NT>(&ysh[(size_t)t * vpr + c]);
-      }
+      for (int j = 0; j < KM; ++j) v[u][j] = ld_row<NT>(&ys[(size_t)row[j] * vpr + c]);
+      if (ysh != nullptr) sh[u] = ld_row<NT>(&ysh[(size_t)t * vpr + c]);
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
