@@ -82,17 +82,36 @@ __global__ __launch_bounds__(kThreads) void combine_bf16_kernel(
     row[j] = min(max(r, 0), T * k - 1);
     wt[j] = j < k ? w[(size_t)t * k + j] : 0.0f;
   }
+  // The wave works on one token, so which slots are kept is the same on
+  // every lane: a scalar test picks the load form.
+  int kmask = 0;
+#pragma unroll
+  for (int j = 0; j < KM; ++j) kmask |= keep[j] ? 1 << j : 0;
+  const bool all_kept = __builtin_amdgcn_readfirstlane(kmask) == (1 << KM) - 1;
   for (int c0 = cbeg + lane; c0 < cend; c0 += U * kWave) {
-    // every load unconditional, from a column clamped into the segment and a
-    // row clamped into the buffer (a dropped row reads row 0 and adds
-    // nothing), so all U * KM loads are in flight before the first wait
     uint4 v[U][KM], sh[U];
+    if (all_kept) {
+      // every load unconditional, from a column clamped into the segment, so
+      // all U * KM loads are in flight before the first wait
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int c = min(c0 + u * kWave, cend - 1);
+      for (int u = 0; u < U; ++u) {
+        const int c = min(c0 + u * kWave, cend - 1);
 #pragma unroll
-      for (int j = 0; j < KM; ++j) v[u][j] = ld_row<NT>(&ys[(size_t)row[j] * vpr + c]);
-      if (ysh != nullptr) sh[u] = ld_row<NT>(&ysh[(size_t)t * vpr + c]);
+        for (int j = 0; j < KM; ++j) v[u][j] = ld_row<NT>(&ys[(size_t)row[j] * vpr + c]);
+        if (ysh != nullptr) sh[u] = ld_row<NT>(&ysh[(size_t)t * vpr + c]);
+      }
+    } else {
+      // dropped or padding slots (k below KM): load only the kept rows
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + u * kWave;
+        if (c < cend) {
+#pragma unroll
+          for (int j = 0; j < KM; ++j)
+            if (keep[j]) v[u][j] = ld_row<NT>(&ys[(size_t)row[j] * vpr + c]);
+          if (ysh != nullptr) sh[u] = ld_row<NT>(&ysh[(size_t)t * vpr + c]);
+        }
+      }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
