@@ -1,17 +1,23 @@
 """Benchmark of the MoE FFN layer forward on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--only]
+                    [--warm] [--graph] [--drop] [--no-cpu-baseline]
 
 A step is one pass of the whole layer over one batch: route, dispatch, grouped
 expert FFN, combine and load stats (left on the device), all on one stream
 with inputs already resident in HBM. W untimed warm-up steps, then exactly K
-timed steps between two device synchronisations; HIP events on the same
-stream time every call of every timed step.
+timed steps between two device synchronisations; HIP events on the launch
+stream time every call of every step. Caches are cold: a 1 GiB fill kernel
+(more than the 256 MB last-level cache and all L2s) runs before every timed
+step, outside the events, and the step time is the event span of the five
+calls. The same K steps are then timed warm, as a labelled secondary.
 
-Default workload: the Mixtral-8x7B-shaped layer (T=4096, H=4096, E=8, top-2,
+Headline workload: the Mixtral-8x7B-shaped layer (T=4096, H=4096, E=8, top-2,
 d_ff=14336, bf16 with fp32 accumulation), random weights and inputs from the
-seeded generator. Prints one JSON line:
-  value        tokens/s of the whole layer (T*K / elapsed)
+seeded generator. Unless --only, the same run also times the fine-grained
+(E=128, top-8, shared expert, Zipf bias) and heavy-skew (T=16384, E=256)
+layers and the decode sweep (T = 1..128, graph replay). Prints one JSON line:
+  value        tokens/s of the headline layer (T / cold step time)
   roofline     the dominant kernel, the bf16 MFMA grouped GEMM (launched twice
                per step: up and down projections, 2*rows*H*F flops each),
                against the dense bf16 MFMA peak of 2500 TFLOP/s
@@ -19,8 +25,10 @@ seeded generator. Prints one JSON line:
                fraction of its roofline; route, dispatch and combine also as a
                fraction of a plain device copy timed in the same run
                (measured_copy_GB/s)
-With --flush every step starts from cold caches (a 1 GiB write first).
-  cpu_baseline the float64 CPU oracle on a bounded sample of the same workload
+  warm         the headline layer with warm caches
+  workloads    cold and warm summaries of the other 4096+-token layers
+  decode       per-T graph-replayed latency and the FFN's weight-read rate
+  cpu_baseline the float64 CPU oracle on a bounded sample of the headline layer
 """
 from __future__ import annotations
 
@@ -114,32 +122,279 @@ def read_traffic():
     return float(m_b.group(1))
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo, the field lscpu prints)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(cfg, L, n_tokens, min_seconds=0.0):
     """The oracle as it stands on the first n_tokens tokens of the same layer,
-    passes repeated until min_seconds have gone by."""
-    import numpy as np
+    passes repeated until min_seconds have gone by; each oracle stage is timed
+    on its own (route, dispatch, expert FFNs with the shared expert, combine,
+    statistics), in the order the oracle's whole-layer function runs them."""
     from threadpoolctl import threadpool_info
 
     import oracle
 
     Ls = dict(L)
     Ls["x"] = L["x"][:n_tokens]
+    E = np.asarray(L["wg"]).shape[0]
+    stages = dict(route=0.0, dispatch=0.0, expert_ffn=0.0, combine=0.0, load_stats=0.0)
     passes = 0
     t0 = time.perf_counter()
     while True:
-        r = oracle.layer(Ls, cfg.k)
-        oracle.load_stats(r["counts"], n_tokens, cfg.k, cfg.cf)
+        t = time.perf_counter()
+        idx, w, _, _ = oracle.route(Ls["x"], Ls["wg"], Ls["bias"], cfg.k)
+        t1 = time.perf_counter()
+        counts, _, _, _, _ = oracle.dispatch(idx, Ls["x"], E)
+        t2 = time.perf_counter()
+        y = oracle.expert_outputs(Ls["x"], idx, Ls["w1"], Ls["w2"])
+        ysh = oracle.shared_outputs(Ls["x"], Ls["ws1"], Ls["ws2"])
+        t3 = time.perf_counter()
+        oracle.combine(y, w, ysh)
+        t4 = time.perf_counter()
+        oracle.load_stats(counts, n_tokens, cfg.k, cfg.cf)
+        t5 = time.perf_counter()
+        for name, a, b in [("route", t, t1), ("dispatch", t1, t2), ("expert_ffn", t2, t3),
+                           ("combine", t3, t4), ("load_stats", t4, t5)]:
+            stages[name] += b - a
+        del y, ysh
         passes += 1
         dt = time.perf_counter() - t0
         if dt >= min_seconds:
             break
-    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    pool = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
     what = f"{passes} passes over " if passes > 1 else ""
-    return {"value": passes * n_tokens / dt, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+    return {"value": passes * n_tokens / dt, "unit": "tokens/s",
+            # the oracle's arithmetic runs in the BLAS pool; it cannot use more
+            # threads than the process may run on
+            "cores": int(min(pool, affinity)), "kind": "oracle",
             "sample": f"{what}the first {n_tokens} of {cfg.T} tokens of the same layer through "
                       f"the whole float64 oracle (route, dispatch, FFN, combine, stats); {dt:.1f} s",
+            "affinity_cpus": int(affinity), "blas_threads": int(pool), "cpu_model": cpu_model(),
+            "stage_seconds_per_pass": {k: v / passes for k, v in stages.items()},
             "seconds": dt}
+
+
+NAMES = ["route", "dispatch", "expert_ffn", "combine", "load_stats"]
+
+
+class Layer:
+    """Device buffers of one workload, allocated once, and its five calls."""
+
+    def __init__(self, cfg, L, moe, torch, copy_gather=False, drop=False):
+        import torch as _t  # noqa: F401
+        dev = lambda a: None if a is None else (
+            torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda() if a.dtype == np.uint16
+            else torch.from_numpy(a).cuda())
+        self.cfg, self.moe, self.torch = cfg, moe, torch
+        self.copy_gather = copy_gather
+        self.x, self.wg, self.bias = dev(L["x"]), dev(L["wg"]), dev(L["bias"])
+        self.w1, self.w2, self.ws1, self.ws2 = dev(L["w1"]), dev(L["w2"]), dev(L["ws1"]), dev(L["ws2"])
+        T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
+        rows = T * k
+        dt_code = 1 if cfg.dtype == "bf16" else 0
+        dtype = self.x.dtype
+        c = "cuda"
+        self.idx = torch.empty((T, k), dtype=torch.int32, device=c)
+        self.wts = torch.empty((T, k), dtype=torch.float32, device=c)
+        self.dsp = dict(counts=torch.empty(E, dtype=torch.int32, device=c),
+                        offsets=torch.empty(E + 1, dtype=torch.int32, device=c),
+                        perm=torch.empty(rows, dtype=torch.int32, device=c),
+                        inv=torch.empty(rows, dtype=torch.int32, device=c),
+                        xs=torch.empty((rows, H), dtype=dtype, device=c) if copy_gather else None)
+        self.ws_r = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, k, dt_code)),
+                                dtype=torch.uint8, device=c)
+        self.ws_d = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, E, k)),
+                                dtype=torch.uint8, device=c)
+        self.ws_f = torch.empty(max(1, moe.moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs,
+                                                                          dt_code)),
+                                dtype=torch.uint8, device=c)
+        self.ys = torch.empty((rows, H), dtype=dtype, device=c)
+        self.ysh = torch.empty((T, H), dtype=dtype, device=c) if Fs else None
+        self.out = torch.empty((T, H), dtype=dtype, device=c)
+        from sparse_mixture_experts_05_amd.binding import STATS_BYTES
+        self.st = torch.empty(STATS_BYTES, dtype=torch.uint8, device=c)
+        self.ovf = torch.empty(E, dtype=torch.int32, device=c)
+        self.strag = torch.empty(E, dtype=torch.int32, device=c)
+        self.cap = moe.moe_capacity(T, k, E, cfg.cf) if drop else None
+        self.stream = torch.cuda.current_stream()
+
+    def step(self, ev=None):
+        moe, s, cfg = self.moe, self.stream, self.cfg
+        rec = (lambda i: ev[i].record(s)) if ev is not None else (lambda i: None)
+        rec(0)
+        moe.moe_route(self.x, self.wg, self.bias, cfg.k, topk_idx=self.idx, topk_w=self.wts,
+                      ws=self.ws_r, stream=s)
+        rec(1)
+        moe.moe_dispatch(self.idx, self.x, cfg.E, out=self.dsp, ws=self.ws_d, stream=s,
+                         capacity=self.cap)
+        rec(2)
+        if self.copy_gather:
+            moe.moe_expert_ffn(self.dsp["xs"], self.dsp["offsets"], self.w1, self.w2, x=self.x,
+                               ws1=self.ws1, ws2=self.ws2, T=cfg.T, ys=self.ys, ysh=self.ysh,
+                               ws=self.ws_f, stream=s)
+        else:
+            moe.moe_expert_ffn_gather(self.x, self.dsp["perm"], cfg.k, self.dsp["offsets"],
+                                      self.w1, self.w2, ws1=self.ws1, ws2=self.ws2, ys=self.ys,
+                                      ysh=self.ysh, ws=self.ws_f, stream=s)
+        rec(3)
+        moe.moe_combine(self.ys, self.dsp["inv"], self.wts, self.ysh, out=self.out, stream=s)
+        rec(4)
+        moe.moe_load_stats(self.dsp["counts"], cfg.T, cfg.k, cfg.cf, stats=self.st,
+                           overflow=self.ovf, straggler_ids=self.strag, stream=s, read_back=False)
+        rec(5)
+
+    def graph(self, drop=False):
+        return self.moe.MoELayerGraph(self.wg, self.bias, self.w1, self.w2, self.cfg.k, self.cfg.T,
+                                      ws1=self.ws1, ws2=self.ws2, capacity_factor=self.cfg.cf,
+                                      drop=drop)
+
+
+def timed_steps(layer, torch, steps, flush_buf):
+    """K timed eager steps with HIP events around every call (on the launch
+    stream). With flush_buf, a fill kernel over it (larger than the last-level
+    cache and all L2s) runs before every step, outside the events. Returns the
+    per-call samples (ms), the per-step event spans (ms) and the wall time (s)."""
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        if flush_buf is not None:
+            flush_buf.fill_(s & 0xFF)   # a fill kernel, not a memset
+        layer.step(events[s])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    samples = {n: np.array([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])
+               for i, n in enumerate(NAMES)}
+    spans = np.array([events[s][0].elapsed_time(events[s][5]) for s in range(steps)])
+    return samples, spans, elapsed
+
+
+def kernel_table(cfg, samples, work, copy_gather=False):
+    """Per-call mean / p10 / median / p90 and the fraction of each call's roofline."""
+    per = {n: float(v.mean()) for n, v in samples.items()}
+    bf16 = cfg.dtype == "bf16"
+    peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
+    ffn_ms = per["expert_ffn"]
+    # two launches of the same GEMM kernel per step, equal algorithmic flops each
+    achieved = (work["ffn_flops"] / 2) / ((ffn_ms / 2) * 1e-3) / 1e12
+    k = {
+        "route": {"ms": per["route"], "GB/s": work["route_bytes"] / per["route"] / 1e6},
+        "dispatch": {"ms": per["dispatch"], "GB/s": work["dispatch_bytes"] / per["dispatch"] / 1e6},
+        "expert_ffn": {"ms": ffn_ms, "TFLOP/s": achieved, "mfma_frac": achieved / peak,
+                       "weight_stream_GB/s": work["ffn_weight_bytes"] / ffn_ms / 1e6},
+        "combine": {"ms": per["combine"], "GB/s": work["combine_bytes"] / per["combine"] / 1e6},
+        "load_stats": {"ms": per["load_stats"]},
+    }
+    for n in ["route", "dispatch", "combine"]:
+        k[n]["hbm_frac"] = k[n]["GB/s"] / HBM_PEAK_GBS
+    k["expert_ffn"]["weight_hbm_frac"] = k["expert_ffn"]["weight_stream_GB/s"] / HBM_PEAK_GBS
+    if not copy_gather:
+        k["dispatch"]["moves"] = ("ids and indices only (the FFN gathers the token rows "
+                                  "through perm), so launch latency bounds it")
+    for n in NAMES:
+        p10, p50, p90 = np.percentile(samples[n], [10, 50, 90])
+        k[n].update(p10_ms=float(p10), median_ms=float(p50), p90_ms=float(p90))
+    return k, achieved, peak
+
+
+def run_workload(name, args, moe, torch, flush_buf, headline=False):
+    """Cold-cache (and warm) timing of one workload; returns a result dict."""
+    from synth import get_config, make_layer
+    cfg = get_config(name)
+    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
+    L = make_layer(cfg)
+    layer = Layer(cfg, L, moe, torch, copy_gather=args.copy_gather and headline,
+                  drop=args.drop and headline)
+    print(f"[bench] {cfg.name}: warmup {args.warmup}", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        layer.step()
+    torch.cuda.synchronize()
+    print(f"[bench] {cfg.name}: timing {args.steps} steps, cold caches", file=sys.stderr, flush=True)
+    cold, cold_spans, cold_elapsed = timed_steps(layer, torch, args.steps, flush_buf)
+    print(f"[bench] {cfg.name}: timing {args.steps} steps, warm caches", file=sys.stderr, flush=True)
+    warm, warm_spans, warm_elapsed = timed_steps(layer, torch, args.steps, None)
+    counts = layer.dsp["counts"].cpu().numpy()
+    kept = np.diff(layer.dsp["offsets"].cpu().numpy()) if layer.cap is not None else None
+    work = algorithmic_work(cfg, counts, kept, fused=not layer.copy_gather)
+    res = {"cfg": cfg, "L": L, "layer": layer, "work": work}
+    res["cold"] = kernel_table(cfg, cold, work, layer.copy_gather)
+    res["warm"] = kernel_table(cfg, warm, work, layer.copy_gather)
+    res["cold_ms"] = float(cold_spans.mean())
+    res["warm_ms"] = warm_elapsed * 1e3 / args.steps
+    res["cold_spans"] = cold_spans
+    res["elapsed_cold"] = cold_elapsed
+    return res
+
+
+def summary(res, which="cold"):
+    """Compact per-workload record for the JSON line."""
+    cfg = res["cfg"]
+    k, achieved, peak = res[which]
+    ms = res["cold_ms"] if which == "cold" else res["warm_ms"]
+    return {"tokens/s": cfg.T / (ms * 1e-3), "ms_per_step": ms,
+            "ffn_TFLOP/s": achieved, "ffn_mfma_frac": achieved / peak,
+            "route_hbm_frac": k["route"]["hbm_frac"], "combine_hbm_frac": k["combine"]["hbm_frac"],
+            "kernels_median_ms": {n: k[n]["median_ms"] for n in NAMES}}
+
+
+def decode_sweep(args, moe, torch, flush_buf):
+    """The decode-shaped sweep: per T, graph-replayed layer latency from cold
+    caches (a flush before every replay, events around the replay) and, from
+    cold eager steps, the FFN's weight-read rate against HBM."""
+    from synth import DECODE_TOKENS, get_config, make_layer
+    full = get_config("decode")
+    print(f"[bench] decode sweep: generating inputs", file=sys.stderr, flush=True)
+    L = make_layer(full)
+    out = {}
+    for T in DECODE_TOKENS:
+        cfg = get_config(f"decode@T{T}")
+        Lt = dict(L)
+        Lt["x"] = L["x"][:T].copy()
+        layer = Layer(cfg, Lt, moe, torch)
+        for _ in range(args.warmup):
+            layer.step()
+        steps = max(args.steps, 30)
+        cold, _, _ = timed_steps(layer, torch, steps, flush_buf)
+        counts = layer.dsp["counts"].cpu().numpy()
+        work = algorithmic_work(cfg, counts)
+        k, _, _ = kernel_table(cfg, cold, work)
+        g = layer.graph()
+        g.x.copy_(layer.x)
+        for _ in range(args.warmup):
+            g.graph.replay()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for s in range(steps):
+            flush_buf.fill_(s & 0xFF)
+            ev[s][0].record()
+            g.graph.replay()
+            ev[s][1].record()
+        torch.cuda.synchronize()
+        lat = np.array([a.elapsed_time(b) for a, b in ev])
+        p10, p50, p90 = np.percentile(lat, [10, 50, 90])
+        out[f"T{T}"] = {"graph_latency_ms_median": float(p50), "p10_ms": float(p10),
+                        "p90_ms": float(p90), "tokens/s": T / (p50 * 1e-3),
+                        "eager_kernels_median_ms": {n: k[n]["median_ms"] for n in NAMES},
+                        "ffn_weight_GB/s": work["ffn_weight_bytes"] / k["expert_ffn"]["median_ms"] / 1e6,
+                        "ffn_weight_hbm_frac": work["ffn_weight_bytes"] / k["expert_ffn"]["median_ms"]
+                        / 1e6 / HBM_PEAK_GBS}
+        print(f"[bench] decode T={T}: graph latency {p50 * 1e3:.1f} us", file=sys.stderr, flush=True)
+        del g, layer
+        torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -150,14 +405,17 @@ def main():
     ap.add_argument("--workload", default="mixtral_8x7b")
     ap.add_argument("--cpu-tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only", action="store_true",
+                    help="the headline workload only (no fine-grained / heavy-skew sub-results, "
+                         "no decode sweep)")
     ap.add_argument("--graph", action="store_true",
-                    help="time replays of the five calls captured in one HIP graph")
+                    help="headline value from replays of the five calls captured in one HIP graph")
     ap.add_argument("--drop", action="store_true",
-                    help="enforce the expert capacity int(T*k/E*cf): dispatch drops the "
-                         "assignments past it (a variant, not the headline layer)")
-    ap.add_argument("--flush", action="store_true",
-                    help="cold caches: write a 1 GiB buffer before every step (outside the "
-                         "per-call events); value then comes from the event span of each step")
+                    help="enforce the expert capacity int(T*k/E*cf) on the headline workload: "
+                         "dispatch drops the assignments past it (a variant, not the headline layer)")
+    ap.add_argument("--warm", action="store_true",
+                    help="headline value from warm caches (default: cold, a 1 GiB fill kernel "
+                         "before every step, outside the per-call events)")
     ap.add_argument("--copy-gather", action="store_true",
                     help="dispatch copies the rows into xs and the FFN reads xs (the default "
                          "FFN reads x through perm: moe_expert_ffn_gather)")
@@ -175,151 +433,41 @@ def main():
     import torch
 
     import sparse_mixture_experts_05_amd as moe
-    from synth import get_config, make_layer
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     moe.lib()  # fail loudly if the HIP library is missing
-    cfg = get_config(args.workload)
-    print(f"[bench] workload {cfg.name}: generating inputs", file=sys.stderr, flush=True)
-    L = make_layer(cfg)
+    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
 
-    def dev(a):
-        if a is None:
-            return None
-        if a.dtype == np.uint16:
-            return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
-        return torch.from_numpy(a).cuda()
-
-    x, wg, bias = dev(L["x"]), dev(L["wg"]), dev(L["bias"])
-    w1, w2, ws1, ws2 = dev(L["w1"]), dev(L["w2"]), dev(L["ws1"]), dev(L["ws2"])
-    T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
-    rows = T * k
-    dt_code = 1 if cfg.dtype == "bf16" else 0
-    dtype = x.dtype
-    # every buffer allocated once, outside the timed region
-    idx = torch.empty((T, k), dtype=torch.int32, device="cuda")
-    wts = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    dsp = dict(counts=torch.empty(E, dtype=torch.int32, device="cuda"),
-               offsets=torch.empty(E + 1, dtype=torch.int32, device="cuda"),
-               perm=torch.empty(rows, dtype=torch.int32, device="cuda"),
-               inv=torch.empty(rows, dtype=torch.int32, device="cuda"),
-               xs=torch.empty((rows, H), dtype=dtype, device="cuda") if args.copy_gather else None)
-    ws_r = torch.empty(max(1, moe.moe_route_workspace_bytes(T, H, E, k, dt_code)),
-                       dtype=torch.uint8, device="cuda")
-    ws_d = torch.empty(max(1, moe.moe_dispatch_workspace_bytes(T, E, k)), dtype=torch.uint8,
-                       device="cuda")
-    ws_f = torch.empty(max(1, moe.moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dt_code)),
-                       dtype=torch.uint8, device="cuda")
-    ys = torch.empty((rows, H), dtype=dtype, device="cuda")
-    ysh = torch.empty((T, H), dtype=dtype, device="cuda") if Fs else None
-    out = torch.empty((T, H), dtype=dtype, device="cuda")
-    from sparse_mixture_experts_05_amd.binding import STATS_BYTES
-    st = torch.empty(STATS_BYTES, dtype=torch.uint8, device="cuda")
-    ovf = torch.empty(E, dtype=torch.int32, device="cuda")
-    strag = torch.empty(E, dtype=torch.int32, device="cuda")
-    stream = torch.cuda.current_stream()
-    cap = moe.moe_capacity(T, k, E, cfg.cf) if args.drop else None
-
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        moe.moe_route(x, wg, bias, k, topk_idx=idx, topk_w=wts, ws=ws_r, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
-        moe.moe_dispatch(idx, x, E, out=dsp, ws=ws_d, stream=stream, capacity=cap)
-        if ev is not None:
-            ev[2].record(stream)
-        if args.copy_gather:
-            moe.moe_expert_ffn(dsp["xs"], dsp["offsets"], w1, w2, x=x, ws1=ws1, ws2=ws2, T=T,
-                               ys=ys, ysh=ysh, ws=ws_f, stream=stream)
-        else:
-            moe.moe_expert_ffn_gather(x, dsp["perm"], k, dsp["offsets"], w1, w2, ws1=ws1,
-                                      ws2=ws2, ys=ys, ysh=ysh, ws=ws_f, stream=stream)
-        if ev is not None:
-            ev[3].record(stream)
-        moe.moe_combine(ys, dsp["inv"], wts, ysh, out=out, stream=stream)
-        if ev is not None:
-            ev[4].record(stream)
-        moe.moe_load_stats(dsp["counts"], T, k, cfg.cf, stats=st, overflow=ovf,
-                           straggler_ids=strag, stream=stream, read_back=False)
-        if ev is not None:
-            ev[5].record(stream)
-
-    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
-    if args.graph:
-        # per-call times from an eager pass; the timed steps are graph replays
-        for s_ in range(args.steps):
-            step(events[s_])
-        torch.cuda.synchronize()
-        graph = moe.MoELayerGraph(wg, bias, w1, w2, k, T, ws1=ws1, ws2=ws2, capacity_factor=cfg.cf,
-                                  drop=args.drop)
-        graph.x.copy_(x)
-        for _ in range(args.warmup):
-            graph.graph.replay()
-        torch.cuda.synchronize()
-    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if args.flush else None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(args.steps):
-        if flush_buf is not None:
-            flush_buf.fill_(s & 0xFF)  # a fill kernel (no memset): > MALL + all L2s
-        if args.graph:
-            graph.graph.replay()
-        else:
-            step(events[s])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    if args.graph:
-        dsp = graph.dsp
-
-    names = ["route", "dispatch", "expert_ffn", "combine", "load_stats"]
-    samples = {n: np.array([events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)])
-               for i, n in enumerate(names)}
-    per = {n: float(v.mean()) for n, v in samples.items()}
-    layer_ms = np.array([events[s][0].elapsed_time(events[s][5]) for s in range(args.steps)])
-    counts = dsp["counts"].cpu().numpy()
-    kept = np.diff(dsp["offsets"].cpu().numpy()) if args.drop else None
-    work = algorithmic_work(cfg, counts, kept, fused=not args.copy_gather)
-    if args.flush and not args.graph:
-        # the flush sits outside the per-call events: time the layer itself
-        ms_step = float(layer_ms.mean())
-        value = T / (ms_step * 1e-3)
+    head = run_workload(args.workload, args, moe, torch, flush_buf, headline=True)
+    cfg, work, layer = head["cfg"], head["work"], head["layer"]
+    T = cfg.T
+    kernels, achieved, peak = head["warm" if args.warm else "cold"]
+    if args.warm:
+        ms_step = head["warm_ms"]
     else:
-        ms_step = elapsed * 1e3 / args.steps
-        value = T * args.steps / elapsed
-
-    ffn_ms = per["expert_ffn"]
+        # the flush sits outside the per-call events: the step is the event span
+        ms_step = head["cold_ms"]
+    value = T / (ms_step * 1e-3)
+    if args.graph:
+        g = layer.graph(drop=args.drop)
+        g.x.copy_(layer.x)
+        for _ in range(args.warmup):
+            g.graph.replay()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        for s in range(args.steps):
+            if not args.warm:
+                flush_buf.fill_(s & 0xFF)
+            ev[s][0].record()
+            g.graph.replay()
+            ev[s][1].record()
+        torch.cuda.synchronize()
+        ms_step = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        value = T / (ms_step * 1e-3)
+        del g
     bf16 = cfg.dtype == "bf16"
-    peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
-    # two launches of the same GEMM kernel per step, equal algorithmic flops each
-    per_launch_flops = work["ffn_flops"] / 2
-    per_launch_ms = ffn_ms / 2
-    achieved = per_launch_flops / (per_launch_ms * 1e-3) / 1e12
-    traffic = read_traffic()
-    kernels = {
-        "route": {"ms": per["route"], "GB/s": work["route_bytes"] / per["route"] / 1e6},
-        "dispatch": {"ms": per["dispatch"], "GB/s": work["dispatch_bytes"] / per["dispatch"] / 1e6},
-        "expert_ffn": {"ms": ffn_ms, "TFLOP/s": achieved * 1.0,
-                       "mfma_frac": achieved / peak,
-                       "weight_stream_GB/s": work["ffn_weight_bytes"] / ffn_ms / 1e6},
-        "combine": {"ms": per["combine"], "GB/s": work["combine_bytes"] / per["combine"] / 1e6},
-        "load_stats": {"ms": per["load_stats"]},
-    }
-    for n in ["route", "dispatch", "combine"]:
-        kernels[n]["hbm_frac"] = kernels[n]["GB/s"] / HBM_PEAK_GBS
-    if not args.copy_gather:
-        kernels["dispatch"]["moves"] = ("ids and indices only (the FFN gathers the token rows "
-                                        "through perm), so launch latency bounds it")
-    for n in names:
-        p10, p50, p90 = np.percentile(samples[n], [10, 50, 90])
-        kernels[n].update(p10_ms=float(p10), median_ms=float(p50), p90_ms=float(p90))
     result = {
         "metric": "MoE layer tokens/sec at 1 GPU + MFMA util % (FFN) + HBM GB/s (route/dispatch)",
         "value": value,
@@ -333,20 +481,35 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if bf16 else "f32",
         "data": "synthetic (seeded Gaussian inputs and random-init weights)",
-        "config": {"workload": cfg.name, "tokens": T, "hidden": H, "experts": E, "top_k": k,
-                   "d_ff": F, "shared_d_ff": Fs, "routing_bias_amplitude": cfg.bias_amp,
-                   "capacity_factor": cfg.cf, "parallelism": "single GPU",
-                   "capacity_dropping": bool(args.drop),
+        "config": {"workload": cfg.name, "tokens": T, "hidden": cfg.H, "experts": cfg.E,
+                   "top_k": cfg.k, "d_ff": cfg.F, "shared_d_ff": cfg.Fs,
+                   "routing_bias_amplitude": cfg.bias_amp, "capacity_factor": cfg.cf,
+                   "parallelism": "single GPU", "capacity_dropping": bool(args.drop),
                    "gather": "dispatch copy (xs)" if args.copy_gather else
                              "fused into the FFN (x read through perm)",
                    "launch": "hip graph replay" if args.graph else "eager",
-                   "caches": "flushed before every step" if args.flush else "warm"},
-        "roofline": {"bound": "mfma", "kernel": gemm_kernel_name(cfg), "achieved": achieved,
-                     "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic},
+                   "caches": "warm" if args.warm else
+                             "cold: a 1 GiB fill kernel before every step, outside the events"},
+        "roofline": {"bound": "mfma" if bf16 else "alu", "kernel": gemm_kernel_name(cfg),
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
+                     "frac": achieved / peak, "traffic": read_traffic()},
         "kernels": kernels,
         "mfma_util_pct_ffn": 100.0 * achieved / peak,
+        "warm": summary(head, "warm"),
     }
+    del head["layer"], layer
+    torch.cuda.empty_cache()
+    if not args.only:
+        subs = {}
+        for name in ["fine_grained_zipf", "heavy_skew"]:
+            if name == args.workload:
+                continue
+            r = run_workload(name, args, moe, torch, flush_buf)
+            subs[name] = {"cold": summary(r, "cold"), "warm": summary(r, "warm")}
+            del r
+            torch.cuda.empty_cache()
+        result["workloads"] = subs
+        result["decode"] = decode_sweep(args, moe, torch, flush_buf)
     # Context for the datasheet fractions of the HBM-bound steps: a plain
     # 512 MiB device copy (1 GiB of reads and writes, beyond the last-level
     # cache) timed with events on the same stream; copy_frac = a step's GB/s
@@ -376,6 +539,7 @@ def main():
         del src, dst
     if not args.no_cpu_baseline:
         # a first small sample sizes a second one to about CPU_TARGET_S seconds
+        L = head["L"]
         n = min(args.cpu_tokens, T)
         print(f"[bench] cpu baseline on {n} tokens", file=sys.stderr, flush=True)
         cb = cpu_baseline(cfg, L, n)

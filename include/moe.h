@@ -92,9 +92,6 @@ typedef struct {
  *   topk_w[t,j] = exp(s[t,idx_j] - m) / sum_j' exp(s[t,idx_j'] - m), m = max_e s[t,e]
  *               (the softmax over all E experts renormalised over the k chosen
  *                ones; the full-E denominator cancels)
- * x        [T,H] dtype          device, read
- * wg       [E,H] dtype          device, read
- * bias     [E]   fp32 or NULL   device, read (NULL = no routing bias)
  *   prob_mean[e] = (1/T) sum_t p[t,e], p[t,e] = exp(s[t,e] - m) / sum_e' exp(s[t,e'] - m)
  *               (the P_i of [DIAG] section 4.1: mean router probability of the
  *                biased softmax over all E experts; fp32 sums per workgroup in
@@ -144,6 +141,20 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
                  void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_capacity - the per-expert capacity of [DIAG] section 3 (its
+ * diagnostics listing: the mean assignments per expert times the capacity
+ * factor, truncated to an integer):
+ *   capacity = int(((double)(T*k) / (double)E) * capacity_factor)
+ * evaluated in double in that order, the value moe_load_stats reports in
+ * moe_load_stats_t.capacity and the one to pass to moe_dispatch_capped.
+ * Host-only: reads no device memory and enqueues nothing.
+ * Returns -1 if T < 1, k < 1, E < 1 or capacity_factor is not a finite
+ * value > 0; a capacity above INT32_MAX is returned as INT32_MAX (every
+ * assignment is then kept, since T*k < 2^31).
+ */
+int64_t moe_capacity(int T, int k, int E, double capacity_factor);
+
+/*
  * moe_dispatch_capped - moe_dispatch with each expert's capacity enforced
  * ([DIAG] section 3 counts the assignments past an expert's capacity
  * int(T*k/E*cf); section 5 describes dropping them). Every expert keeps its
@@ -156,8 +167,9 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
  *   inv[t*k+j]  = the buffer row of a kept assignment, -1 for a dropped one
  * moe_expert_ffn then runs on the kept rows (pass rows = T*k: an upper bound)
  * and moe_combine skips the dropped assignments without renormalising the
- * kept weights. capacity >= 0 (0 drops every assignment). Other arguments,
- * the workspace and errors as moe_dispatch.
+ * kept weights. capacity >= 0 (0 drops every assignment); the layer's value
+ * is moe_capacity(T, k, E, capacity_factor). Other arguments, the workspace
+ * and errors as moe_dispatch.
  */
 int moe_dispatch_capped(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
                         int capacity, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,

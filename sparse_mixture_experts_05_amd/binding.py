@@ -35,6 +35,7 @@ SIGNATURES = {
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "moe_load_stats": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
     "moe_bias_update": (_i, [_vp, _i, ctypes.c_float, _vp, _vp, _vp]),
+    "moe_capacity": (ctypes.c_int64, [_i, _i, _i, _d]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
 }
 
@@ -95,6 +96,28 @@ def _dev(t: torch.Tensor | None, name: str, dtype=None):
     return t.data_ptr()
 
 
+def _want(t, name: str, shape, dtype=None):
+    """Shape (and dtype) check of a tensor argument before any pointer reaches
+    the library: the kernels index by the sizes passed with the pointers, so a
+    mismatched tensor would be read or written out of bounds. None passes."""
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _dims(t, name: str, ndim: int):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError(f"{name} must be a torch tensor")
+    if t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dimensions, got shape {tuple(t.shape)}")
+    return tuple(t.shape)
+
+
 def _dtype_code(t: torch.Tensor) -> int:
     if t.dtype == torch.bfloat16:
         return MOE_BF16
@@ -118,8 +141,13 @@ def moe_route(x, wg, bias, k: int, topk_idx=None, topk_w=None, ws=None, stream=N
 
     prob_mean: optional fp32 [E] device tensor that receives the mean router
     probability of every expert over the T tokens."""
-    T, H = x.shape
-    E = wg.shape[0]
+    T, H = _dims(x, "x", 2)
+    E = _dims(wg, "wg", 2)[0]
+    _want(wg, "wg", (E, H), x.dtype)
+    _want(bias, "bias", (E,), torch.float32)
+    _want(topk_idx, "topk_idx", (T, k), torch.int32)
+    _want(topk_w, "topk_w", (T, k), torch.float32)
+    _want(prob_mean, "prob_mean", (E,), torch.float32)
     if topk_idx is None:
         topk_idx = torch.empty((T, k), dtype=torch.int32, device=x.device)
     if topk_w is None:
@@ -141,9 +169,10 @@ def moe_bias_update(counts, bias, gamma: float, load_frac=None, stream=None):
     """Dynamic routing-bias step in place on ``bias`` (fp32 [E]) from the expert
     counts (int32 [E]); writes the load fractions into ``load_frac`` if given.
     Returns load_frac."""
-    E = counts.shape[0]
-    if bias.shape[0] != E or (load_frac is not None and load_frac.shape[0] != E):
-        raise ValueError("counts, bias and load_frac must all have E entries")
+    E = _dims(counts, "counts", 1)[0]
+    _want(counts, "counts", (E,), torch.int32)
+    _want(bias, "bias", (E,), torch.float32)
+    _want(load_frac, "load_frac", (E,), torch.float32)
     _check("moe_bias_update", lib().moe_bias_update(
         _dev(counts, "counts", torch.int32), E, float(gamma), _dev(bias, "bias", torch.float32),
         _dev(load_frac, "load_frac", torch.float32), _stream(stream)))
@@ -167,9 +196,12 @@ def _workspace(nbytes: int, device, ws=None):
 
 
 def moe_capacity(T: int, k: int, E: int, capacity_factor: float) -> int:
-    """Expert capacity int((T*k/E) * cf), the same double operations as the
-    statistics kernel."""
-    return int(((T * k) / E) * float(capacity_factor))
+    """Expert capacity, computed by the library (moe_capacity)."""
+    cap = lib().moe_capacity(int(T), int(k), int(E), float(capacity_factor))
+    if cap < 0:
+        raise ValueError(f"moe_capacity: invalid arguments T={T} k={k} E={E} "
+                         f"capacity_factor={capacity_factor}")
+    return int(cap)
 
 
 def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=None,
@@ -178,8 +210,20 @@ def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=N
     each expert keeps its first ``capacity`` assignments (moe_dispatch_capped).
     With ``gather=False`` no rows are copied and xs is None (for
     moe_expert_ffn_gather); a given ``out`` without "xs" (or xs None) does the same."""
-    T, H = x.shape
-    k = topk_idx.shape[1]
+    T, H = _dims(x, "x", 2)
+    k = _dims(topk_idx, "topk_idx", 2)[1]
+    _want(topk_idx, "topk_idx", (T, k), torch.int32)
+    if out is not None:
+        _want(out.get("counts"), "counts", (E,), torch.int32)
+        _want(out.get("offsets"), "offsets", (E + 1,), torch.int32)
+        _want(out.get("perm"), "perm", (T * k,), torch.int32)
+        _want(out.get("inv"), "inv", (T * k,), torch.int32)
+        _want(out.get("xs"), "xs", (T * k, H), x.dtype)
+        for key in ["counts", "offsets", "perm", "inv"]:
+            if out.get(key) is None:
+                raise ValueError(f"out[{key!r}] is required")
+    if capacity is not None and not 0 <= int(capacity) < 2 ** 31:
+        raise ValueError(f"capacity {capacity} outside [0, 2^31)")
     dev = x.device
     if out is None:
         out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
@@ -207,11 +251,22 @@ def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=N
 def moe_expert_ffn(xs, offsets, w1, w2, x=None, ws1=None, ws2=None, T=None, ys=None, ysh=None,
                    ws=None, stream=None):
     """Returns (ys [rows,H], ysh [T,H] or None)."""
-    rows, H = xs.shape
-    E, F, _ = w1.shape
-    Fs = 0 if ws1 is None else ws1.shape[0]
+    rows, H = _dims(xs, "xs", 2)
+    E, F, _ = _dims(w1, "w1", 3)
+    Fs = 0 if ws1 is None else _dims(ws1, "ws1", 2)[0]
     if T is None:
         T = x.shape[0] if x is not None else rows
+    _want(offsets, "offsets", (E + 1,), torch.int32)
+    _want(w1, "w1", (E, F, H), xs.dtype)
+    _want(w2, "w2", (E, H, F), xs.dtype)
+    _want(x, "x", (T, H), xs.dtype)
+    if Fs > 0:
+        if x is None or ws2 is None:
+            raise ValueError("the shared expert needs x, ws1 and ws2")
+        _want(ws1, "ws1", (Fs, H), xs.dtype)
+        _want(ws2, "ws2", (H, Fs), xs.dtype)
+        _want(ysh, "ysh", (T, H), xs.dtype)
+    _want(ys, "ys", (rows, H), xs.dtype)
     dt = _dtype_code(xs)
     dev = xs.device
     if ys is None:
@@ -233,10 +288,24 @@ def moe_expert_ffn_gather(x, perm, k: int, offsets, w1, w2, ws1=None, ws2=None, 
                           ys=None, ysh=None, ws=None, stream=None):
     """moe_expert_ffn reading routed row p from x[perm[p] // k] (no xs copy).
     Returns (ys [rows,H], ysh [T,H] or None); rows defaults to T*k."""
-    T, H = x.shape
-    E, F, _ = w1.shape
-    Fs = 0 if ws1 is None else ws1.shape[0]
+    T, H = _dims(x, "x", 2)
+    E, F, _ = _dims(w1, "w1", 3)
+    Fs = 0 if ws1 is None else _dims(ws1, "ws1", 2)[0]
     rows = T * k if rows is None else rows
+    if not 1 <= rows <= T * k:
+        raise ValueError(f"rows {rows} outside [1, T*k = {T * k}]")
+    if _dims(perm, "perm", 1)[0] < rows or perm.dtype != torch.int32:
+        raise ValueError(f"perm must be int32 with at least rows = {rows} entries")
+    _want(offsets, "offsets", (E + 1,), torch.int32)
+    _want(w1, "w1", (E, F, H), x.dtype)
+    _want(w2, "w2", (E, H, F), x.dtype)
+    if Fs > 0:
+        if ws2 is None:
+            raise ValueError("the shared expert needs ws1 and ws2")
+        _want(ws1, "ws1", (Fs, H), x.dtype)
+        _want(ws2, "ws2", (H, Fs), x.dtype)
+        _want(ysh, "ysh", (T, H), x.dtype)
+    _want(ys, "ys", (rows, H), x.dtype)
     dt = _dtype_code(x)
     dev = x.device
     if ys is None:
@@ -256,8 +325,13 @@ def moe_expert_ffn_gather(x, perm, k: int, offsets, w1, w2, ws1=None, ws2=None, 
 
 def moe_combine(ys, inv, topk_w, ysh=None, out=None, stream=None):
     """Returns out [T,H]."""
-    T, k = topk_w.shape
-    H = ys.shape[1]
+    T, k = _dims(topk_w, "topk_w", 2)
+    H = _dims(ys, "ys", 2)[1]
+    _want(topk_w, "topk_w", (T, k), torch.float32)
+    _want(ys, "ys", (T * k, H))
+    _want(inv, "inv", (T * k,), torch.int32)
+    _want(ysh, "ysh", (T, H), ys.dtype)
+    _want(out, "out", (T, H), ys.dtype)
     if out is None:
         out = torch.empty((T, H), dtype=ys.dtype, device=ys.device)
     _check("moe_combine", lib().moe_combine(
@@ -270,7 +344,12 @@ def moe_combine(ys, inv, topk_w, ysh=None, out=None, stream=None):
 def moe_load_stats(counts, T: int, k: int, capacity_factor: float, stats=None, overflow=None,
                    straggler_ids=None, stream=None, read_back: bool = True):
     """Enqueue the diagnostics; with read_back, synchronise and return a dict."""
-    E = counts.shape[0]
+    E = _dims(counts, "counts", 1)[0]
+    _want(counts, "counts", (E,), torch.int32)
+    if stats is not None and stats.numel() * stats.element_size() < STATS_BYTES:
+        raise ValueError(f"stats must hold at least {STATS_BYTES} bytes")
+    _want(overflow, "overflow", (E,), torch.int32)
+    _want(straggler_ids, "straggler_ids", (E,), torch.int32)
     dev = counts.device
     if stats is None:
         stats = torch.empty(STATS_BYTES, dtype=torch.uint8, device=dev)
@@ -284,7 +363,13 @@ def moe_load_stats(counts, T: int, k: int, capacity_factor: float, stats=None, o
         _stream(stream)))
     if not read_back:
         return dict(stats=stats, overflow=overflow, straggler_ids=straggler_ids)
-    raw = MoELoadStats.from_buffer_copy(bytes(stats.cpu().numpy().tobytes()))
+    return read_stats(stats, overflow, straggler_ids)
+
+
+def read_stats(stats, overflow, straggler_ids) -> dict:
+    """Synchronising copy of moe_load_stats' device outputs into a dict (the
+    struct fields, overflow, the straggler ids and the -1 padding after them)."""
+    raw = MoELoadStats.from_buffer_copy(bytes(stats.cpu().numpy().tobytes()[:STATS_BYTES]))
     d = {name: getattr(raw, name) for name, _ in MoELoadStats._fields_}
     d["overflow"] = overflow.cpu().tolist()
     ids = straggler_ids.cpu().tolist()

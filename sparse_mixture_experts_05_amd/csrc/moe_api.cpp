@@ -84,6 +84,15 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
                                        offsets, perm, inv, xs, ws, as_stream(stream)));
 }
 
+int64_t moe_capacity(int T, int k, int E, double capacity_factor) {
+  if (T < 1 || k < 1 || E < 1) return -1;
+  if (!(capacity_factor > 0.0) || !std::isfinite(capacity_factor)) return -1;
+  // the same double operations as the statistics kernel: (T*k)/E first, then *cf
+  const double cap = ((double)((long long)T * k) / (double)E) * capacity_factor;
+  if (cap >= 2147483647.0) return 2147483647;
+  return (int64_t)cap;
+}
+
 int moe_dispatch_capped(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
                         int capacity, int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,
                         int32_t* inv, void* xs, void* ws, size_t ws_bytes, void* stream) {

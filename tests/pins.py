@@ -520,4 +520,40 @@ def check_prob_mean_k_equals_E_matches_weights():
     assert abs(P.sum() - 1.0) < 1e-12
 
 
+# ------------------------------------------------------------------ inputs
+
+def check_widen_bf16_bit_patterns():
+    """bf16 inputs are uint16 bit patterns (sign, 8 exponent bits, 7 fraction
+    bits: the top half of an IEEE binary32); widen() must give their exact value.
+    Hand-decoded patterns, then all 65536 patterns against torch's own
+    bfloat16 -> float32 conversion (NaNs compared as NaNs)."""
+    hand = {
+        0x0000: 0.0, 0x3F80: 1.0, 0xBF80: -1.0, 0xC000: -2.0, 0x4040: 3.0,
+        0x3F81: 1.0 + 2.0 ** -7,                    # one unit in the last place above 1
+        0x3E80: 0.25,
+        0x0001: 2.0 ** -133,                        # smallest subnormal: 2^-126 * 2^-7
+        0x0080: 2.0 ** -126,                        # smallest normal
+        0x7F7F: (2.0 - 2.0 ** -7) * 2.0 ** 127,     # largest finite
+        0x7F80: math.inf, 0xFF80: -math.inf,
+    }
+    bits = np.array(list(hand), dtype=np.uint16)
+    got = O.widen(bits)
+    assert got.dtype == np.float64
+    for b, v in zip(hand, got):
+        assert v == hand[b], (hex(b), v, hand[b])
+    neg0 = O.widen(np.array([0x8000], dtype=np.uint16))[0]
+    assert neg0 == 0.0 and math.copysign(1.0, neg0) < 0
+    with np.errstate(invalid="ignore"):   # signalling NaN patterns
+        assert np.isnan(O.widen(np.array([0x7FC0, 0xFFC1], dtype=np.uint16))).all()
+        every = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+        ref = torch.from_numpy(every.view(np.int16)).view(torch.bfloat16).float().double().numpy()
+        got = O.widen(every)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    # float32 inputs pass through exactly
+    f = _rng(7).standard_normal(64).astype(np.float32)
+    assert np.array_equal(O.widen(f), f.astype(np.float64))
+
+
 ALL_CHECKS = [v for k, v in sorted(globals().items()) if k.startswith("check_")]

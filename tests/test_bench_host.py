@@ -74,3 +74,9 @@ def test_cpu_baseline_repeats_short_samples():
     passes = int(cb["sample"].split(" passes")[0])
     assert passes > 1
     assert abs(cb["value"] - passes * cfg.T / cb["seconds"]) <= 1e-9 * cb["value"]
+    # the threads it used, the CPU it ran on and where the time went
+    assert 1 <= cb["cores"] <= cb["affinity_cpus"] and cb["cpu_model"]
+    st = cb["stage_seconds_per_pass"]
+    assert set(st) == {"route", "dispatch", "expert_ffn", "combine", "load_stats"}
+    assert all(v >= 0 for v in st.values())
+    assert sum(st.values()) * passes <= cb["seconds"] * 1.001

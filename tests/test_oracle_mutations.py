@@ -220,7 +220,30 @@ def m_capped_renormalises(mp):
     mp.setattr(O, "layer_rows", layer_rows)
 
 
-MUTATIONS = [m_no_renormalise, m_select_smallest, m_bias_selection_only, m_ties_to_higher_id,
+_widen = O.widen
+
+
+def m_widen_as_float16(mp):
+    """Read the 16-bit patterns as IEEE half precision instead of bf16."""
+    def widen(a):
+        a = None if a is None else np.asarray(a)
+        if a is not None and a.dtype == np.uint16:
+            return a.view(np.float16).astype(np.float64)
+        return _widen(a)
+    mp.setattr(O, "widen", widen)
+
+
+def m_widen_shift_15(mp):
+    """Shift the bf16 bits into the float32 word one place short."""
+    def widen(a):
+        a = None if a is None else np.asarray(a)
+        if a is not None and a.dtype == np.uint16:
+            return (a.astype(np.uint32) << 15).view(np.float32).astype(np.float64)
+        return _widen(a)
+    mp.setattr(O, "widen", widen)
+
+
+MUTATIONS = [m_widen_as_float16, m_widen_shift_15, m_no_renormalise, m_select_smallest, m_bias_selection_only, m_ties_to_higher_id,
              m_unstable_dispatch, m_offsets_inclusive, m_gelu_tanh, m_gelu_dropped, m_gelu_sign,
              m_w2_layout_misread, m_w1_layout_misread, m_combine_drops_shared, m_combine_weights_swapped, m_capacity_ceil,
              m_gini_index_from_zero, m_straggler_ge, m_bias_update_sign_flipped,
