@@ -38,6 +38,7 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "plan.hpp"
 
 
 namespace moe {
@@ -78,16 +79,7 @@ __device__ __forceinline__ size_t a_row(const GemmArgs& a, int group, int p) {
   return (size_t)p;
 }
 
-struct Tile {
-  int group;  // 0 routed, 1 shared
-  int e;      // expert (routed)
-  int row0;   // first row of the tile in A / C
-  int M;      // valid rows in this tile (<= BM)
-  int n0;     // first column
-  int spl;    // K slices of this tile (1: the whole K in one workgroup)
-  int ks;     // this workgroup's slice
-  int unit0;  // partial-tile index of slice 0 (split tiles), else -1
-};
+using plan::Tile;
 
 // Field-wise select (a reference into the kernel arguments chosen at run time
 // would force a private-memory copy of the whole struct).
@@ -154,106 +146,40 @@ __device__ bool find_tile(const GemmArgs& a, Tile& t) {
   return t.e >= 0;
 }
 
-// Blocked, XCD-aware tile order (large tiles). Groups are the E experts and
-// then the shared expert. A group with c rows has ceil(c/BM) row tiles; if BM
-// does not divide c the last one is partial (it skips the 32-row sub-tiles
-// past the segment end).
-//
-// Inside a group tiles are visited in n-blocks of GN column tiles, row tile by
-// row tile inside an n-block (consecutive tiles share A rows and cycle
-// through GN weight panels). A partial row tile sits in the n-blocks with the
-// full ones, so it reads each weight panel while the others of its n-block
-// do, not again after every panel has left the caches. Workgroups are handed
-// to the 8 XCDs round robin (workgroup g runs on XCD g % 8); XCD x takes the
-// contiguous run [x*C, (x+1)*C) of this order (C = ceil(tiles/8)), so the ~32
-// tiles an XCD runs at once form a compact block whose operand panels its L2
-// shares.
-//
-// Split K in the last round: an XCD runs S = C tiles, kSlots at a time.
-// When the last round holds tail = S mod kSlots tiles and that is at most half
-// a round, each of those tiles is cut into spl K slices (one workgroup each,
-// spl = kSlots / tail, at most kMaxSplit, and every slice keeps at least
-// kMinSliceStages K stages). A slice writes its fp32 partial tile to a.part;
-// a second launch (mode 1) sums the spl partials of each tail tile in slice
-// order and runs the epilogue. The partition depends only on the counts, so
-// results repeat bit for bit. Only long K qualifies (every group's K at least
-// kSplitMinK): a short tail tile does not repay the partial round trip and
-// the extra launch (measured on the fine-grained and heavy-skew layers).
-constexpr int kXcds = 8;
-constexpr int kSlots = 32;    // CUs per XCD: workgroups one round of an XCD runs
-constexpr int kMaxSplit = 8;
-constexpr int kMinSliceStages = 32;  // a slice writes a 256 KB partial: keep it worth it
-constexpr int kSplitMinK = 8192;
+// The big-tile schedule (tile order, split-K last round, short-segment
+// pairs) is plain integer arithmetic in plan.hpp, shared with host checks.
+using plan::kBlockCols;
+using plan::kMaxSplit;
+using plan::kReduceSlots;
+using plan::kSBM;
+using plan::kSBN;
+using plan::kSlots;
+using plan::kXcds;
 constexpr int kBigWaves = 8;
-// GN of the tile order: column tiles per n-block. Measured against 8 (FFN,
-// same box, two alternating runs): Mixtral-shaped 2162-2166 -> 2133 us,
-// fine-grained 1227-1231 -> 1216 us, heavy-skew unchanged; 16 was 3% slower
-// on the Mixtral-shaped layer, 2 1-2% slower on the heavy-skew one.
-constexpr int kBlockCols = 4;
 constexpr size_t kPartTiles = (size_t)kXcds * kSlots;  // split units at most
+constexpr int kTableInt4 = plan::kEntryInts / 4;       // int4 per table entry
 
-// Small segments inside a big-tile launch. A routed segment of at most 32
-// rows would fill one of the 8 sub-tile rows of a 256x256 tile while the tile
-// streams the whole weight panel and copies 256 (clamped) A rows. Such
-// segments run as 32 x 128 tiles (kSBM x kSBN) instead, two per workgroup (one
-// per half of the 8 waves, each with its own LDS ring), and their slots are
-// spread evenly through each XCD's sequence among the big tiles. Measured on
-// the fine-grained and heavy-skew layers: 1-2% off the FFN; a 128-row limit
-// (up to 4 strips re-reading the same weights) was 3% slower than none. Not in
-// split-K launches, and not for the shared group (the two tiles of a
-// workgroup must have the same K: they meet the same barriers). If the
-// launch's slots cannot hold the pairs, every segment takes big tiles.
-constexpr int kSmallRows = 33;
-constexpr int kSBM = 32, kSBN = 128;
+__device__ __forceinline__ plan::Shape shape_of(const GemmArgs& a) {
+  return plan::Shape{a.E,         a.rows,      a.shared_M,
+                     a.routed.N,  a.routed.K,  a.shared.N,
+                     a.shared.K,  a.part != nullptr ? 1 : 0, a.slots};
+}
 
-// Tables of the big-tile schedule (per workgroup, in LDS).
-struct SchedLds {
-  int pf[257];               // inclusive scan of the big tiles by group (small mode)
-  int pa[257];               // the same when every segment takes big tiles
-  int ps[257];               // inclusive scan of the small tiles by group
-  int goff[257], gcnt[257];  // first row and rows of each group
-};
-
-struct BigSched {
-  const int* pf;     // big-tile scan in use
-  int F, CF;         // big tiles in all; per XCD
-  int P, CP;         // small-tile pairs in all; per XCD
-  int R, tail, spl;  // whole rounds per XCD, tiles of the last round, K slices of those
-};
-
-// Computes the schedule of a big-tile launch: the same for every workgroup,
-// and for every tile a workgroup runs.
+// The schedule of a big-tile launch, computed by every workgroup of the
+// planning launch: thread g fills the table entries of group g (thread 255
+// also carries group 256, the shared expert next to 256 routed experts), the
+// tables are scanned in LDS, and plan::finish_schedule derives the rest.
 template <int BM, int BN>
-__device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
+__device__ plan::Sched big_schedule(const plan::Shape& sh, const int32_t* offsets,
+                                    plan::Tables& L) {
   // Only the first 256 threads take part (the workgroup may be larger);
   // every thread still meets every barrier.
   const int tid = threadIdx.x;
   const bool act = tid < 256;
-  const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
-  const int ntr = (a.routed.N + BN - 1) / BN;
-  const int nts = (a.shared.N + BN - 1) / BN;
-  const int nsr = (a.routed.N + kSBN - 1) / kSBN;
-  const bool small_ok = a.part == nullptr;
-  // thread e: expert e; thread E: the shared group; thread 255 also carries
-  // the shared group as group 256 when E == 256
-  auto rows_of = [&](int grp, int& off, int& cnt) {
-    if (grp < a.E) {
-      off = min(max(a.offsets[grp], 0), a.rows);
-      cnt = min(max(a.offsets[grp + 1], off), a.rows) - off;
-    } else {
-      off = 0;
-      cnt = a.shared_M;
-    }
-  };
   int off = 0, cnt = 0, all = 0, big = 0, sml = 0;
-  if (act && tid < ng) {
-    rows_of(tid, off, cnt);
-    all = ((cnt + BM - 1) / BM) * (tid < a.E ? ntr : nts);
-    const bool small = small_ok && tid < a.E && cnt > 0 && cnt < kSmallRows;
-    big = small ? 0 : all;
-    sml = small ? ((cnt + kSBM - 1) / kSBM) * nsr : 0;
-  }
-  const int xtiles = (tid == 255 && ng == 257) ? ((a.shared_M + BM - 1) / BM) * nts : 0;
+  if (act) plan::group_entry<BM, BN>(sh, offsets, tid, off, cnt, all, big, sml);
+  int o2 = 0, c2 = 0, all2 = 0, big2 = 0, sml2 = 0;
+  if (tid == 255) plan::group_entry<BM, BN>(sh, offsets, 256, o2, c2, all2, big2, sml2);
   if (act) {
     L.goff[tid] = off;
     L.gcnt[tid] = cnt;
@@ -262,8 +188,8 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
     L.ps[tid] = sml;
   }
   if (tid == 255) {
-    L.goff[256] = 0;
-    L.gcnt[256] = ng == 257 ? a.shared_M : 0;
+    L.goff[256] = o2;
+    L.gcnt[256] = c2;
   }
   __syncthreads();
   for (int d = 1; d < 256; d <<= 1) {
@@ -279,167 +205,42 @@ __device__ BigSched big_schedule(const GemmArgs& a, SchedLds& L) {
     __syncthreads();
   }
   if (tid == 255) {
-    L.pa[256] = L.pa[255] + xtiles;
-    L.pf[256] = L.pf[255] + xtiles;
-    L.ps[256] = L.ps[255];
+    L.pa[256] = L.pa[255] + all2;
+    L.pf[256] = L.pf[255] + big2;
+    L.ps[256] = L.ps[255] + sml2;
   }
   __syncthreads();
-  const int last = ng <= 256 ? ng - 1 : 256;
-  BigSched S;
-  const int Fs = L.pf[last], Ps = (L.ps[last] + 1) / 2;
-  const int CFs = (Fs + kXcds - 1) / kXcds, CPs = (Ps + kXcds - 1) / kXcds;
-  if (Ps > 0 && kXcds * (CFs + CPs) <= a.slots && CFs + CPs < (1 << 15)) {
-    S.pf = L.pf;
-    S.F = Fs;
-    S.P = Ps;
-  } else {
-    S.pf = L.pa;
-    S.F = L.pa[last];
-    S.P = 0;
-  }
-  S.CF = (S.F + kXcds - 1) / kXcds;
-  S.CP = (S.P + kXcds - 1) / kXcds;
-  S.R = S.CF / kSlots;
-  S.tail = S.CF - S.R * kSlots;
-  S.spl = 1;
-  if (a.part != nullptr && S.tail > 0 && 2 * S.tail <= kSlots) {  // a.part: K long enough
-    int ktmin = a.routed.K / 64;
-    if (a.shared_M > 0) ktmin = min(ktmin, a.shared.K / 64);
-    S.spl = max(1, min(min(kSlots / S.tail, kMaxSplit), ktmin / kMinSliceStages));
-  }
-  return S;
+  return plan::finish_schedule(sh, L);
 }
 
-// The first entry of an inclusive scan over groups [0, ng) above q.
-__device__ __forceinline__ int scan_find(const int* scan, int ng, int q) {
-  int lo = 0, hi = ng - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    if (scan[mid] > q) hi = mid;
-    else lo = mid + 1;
-  }
-  return lo;
-}
-
-// Small tile u of the launch (u < number of small tiles).
-__device__ __forceinline__ void small_tile_of(const GemmArgs& a, const SchedLds& L, int u,
-                                              Tile& t) {
-  const int grp = scan_find(L.ps, a.E, u);
-  const int li = u - (grp ? L.ps[grp - 1] : 0);
-  const int c = L.gcnt[grp];
-  const int nrs = (c + kSBM - 1) / kSBM;  // row strips of the segment
-  const int r = li % nrs;
-  t.group = 0;
-  t.e = grp;
-  t.row0 = L.goff[grp] + r * kSBM;
-  t.M = min(kSBM, c - r * kSBM);
-  t.n0 = (li / nrs) * kSBN;
-  t.spl = 1;
-  t.ks = 0;
-  t.unit0 = -1;
-}
-
-// Slot `slot` on XCD x, resolved by one thread from the schedule tables.
-// mode 0: the launch's work, kind 0 = one big tile (or K slice of a split
-// tail tile) in ta, kind 1 = a pair of small tiles (ta, and tb unless
-// tb.M == 0); mode 1: the split tail tile number `slot` to reduce (kind 0).
-// Returns -1 if the slot holds nothing.
-// An XCD runs CF big-tile slots and CP pair slots; pair slots sit at the
-// positions s where floor((s + 1) * CP / n) steps (n = CF + CP), evenly
-// spread.
+// Writes the tile table of one big-tile launch (plan::encode_entry, four int4
+// per workgroup slot): slots [0, a.slots) for the GEMM launch (workgroup g:
+// slot g / 8 on XCD g % 8), then kReduceSlots for its split-K reduce. Every
+// workgroup computes the same schedule (group scans, from offsets), then each
+// thread resolves one slot: the GEMM workgroups read one entry instead of each
+// redoing the schedule.
 template <int BM, int BN, int GN>
-__device__ int resolve_slot(const GemmArgs& a, const BigSched& S, const SchedLds& L, int x,
-                            int slot, int mode, Tile& ta, Tile& tb) {
-  const int ng = a.E + (a.shared_M > 0 ? 1 : 0);
-  const int ntr = (a.routed.N + BN - 1) / BN;
-  const int nts = (a.shared.N + BN - 1) / BN;
-  const int F = S.F, CF = S.CF, R = S.R, tail = S.tail, spl = S.spl;
-  int ks = 0, unit0 = -1;
-  if (mode == 0) {
-    if (S.CP > 0) {  // pairs (never with split K, whose slices sit past CF)
-      const int n = CF + S.CP;
-      if (slot >= n) return -1;
-      // slot < n < 2^15 and CP < 2^15 (pairs only then): the products fit 32 bits
-      const int pb = (int)((unsigned)(slot * S.CP) / (unsigned)n);
-      if ((int)((unsigned)((slot + 1) * S.CP) / (unsigned)n) > pb) {  // a pair slot
-        const int p = pb * kXcds + x;
-        if (p >= S.P) return -1;
-        const int nsm = L.ps[a.E - 1];
-        small_tile_of(a, L, 2 * p, ta);
-        if (2 * p + 1 < nsm) small_tile_of(a, L, 2 * p + 1, tb);
-        else tb.M = 0;
-        return 1;
-      }
-      slot -= pb;  // big-tile slots before this one
-    }
-    if (spl > 1 && slot >= R * kSlots) {
-      const int u = slot - R * kSlots;
-      if (u >= tail * spl) return -1;
-      const int tt = u / spl;
-      ks = u - tt * spl;
-      slot = R * kSlots + tt;
-      unit0 = x * kSlots + tt * spl;
-    }
-  } else {
-    if (spl <= 1 || slot >= tail) return -1;
-    unit0 = x * kSlots + slot * spl;
-    slot = R * kSlots + slot;
-  }
-  if (slot >= CF) return -1;
-  const int q = x * CF + slot;
-  if (q >= F) return -1;
-  const int grp = scan_find(S.pf, ng, q);
-  const int excl = grp ? S.pf[grp - 1] : 0;
-  const int o = L.goff[grp], c = L.gcnt[grp];
-  const int mt_g = (c + BM - 1) / BM;  // row tiles of the group, the last one maybe partial
-  const int nt_g = grp < a.E ? ntr : nts;
-  const int local = q - excl;
-  const int blk = local / (mt_g * GN);
-  const int w = min(GN, nt_g - blk * GN);
-  const int li = local - blk * mt_g * GN;
-  ta.row0 = o + (li / w) * BM;
-  ta.M = min(BM, c - (li / w) * BM);
-  ta.n0 = (blk * GN + li % w) * BN;
-  ta.group = grp < a.E ? 0 : 1;
-  ta.e = grp < a.E ? grp : 0;
-  ta.spl = unit0 >= 0 ? spl : 1;
-  ta.ks = ks;
-  ta.unit0 = unit0;
-  return 0;
-}
-
-// Split tail tiles a reduce launch can hold: half a round of every XCD.
-constexpr int kReduceSlots = kXcds * kSlots / 2;
-constexpr int kTableInt4 = 4;  // int4 per table entry
-
-// Writes the tile table of one big-tile launch, four int4 per workgroup slot:
-// {kind, group a, expert a, row0 a}, {M a, n0 a, spl, ks},
-// {unit0, group b, expert b, row0 b}, {M b, n0 b, 0, 0} (kind -1: nothing,
-// 0: a big tile in a, 1: small tiles a and b, b absent if M b = 0); slots
-// [0, a.slots) for the GEMM launch (workgroup g: slot g / 8 on XCD g % 8), then
-// kReduceSlots for its split-K reduce. Every workgroup computes the same
-// schedule (group scans, from offsets), then each thread resolves one slot:
-// the GEMM workgroups read one entry instead of each redoing the schedule.
-template <int BM, int BN, int GN>
-__device__ void plan_launch(const GemmArgs& a, int4* table, SchedLds& L) {
-  const BigSched S = big_schedule<BM, BN>(a, L);
+__device__ void plan_launch(const GemmArgs& a, int4* table, plan::Tables& L) {
+  const plan::Shape sh = shape_of(a);
+  const plan::Sched S = big_schedule<BM, BN>(sh, a.offsets, L);
   const int i = blockIdx.x * kThreads + threadIdx.x;
   if (i >= a.slots + kReduceSlots) return;
   const int mode = i < a.slots ? 0 : 1;
   const int g = mode ? i - a.slots : i;
   Tile ta{}, tb{};
-  const int kind = resolve_slot<BM, BN, GN>(a, S, L, g % kXcds, g / kXcds, mode, ta, tb);
-  int4* e = table + kTableInt4 * i;
-  e[0] = make_int4(kind, ta.group, ta.e, ta.row0);
-  e[1] = make_int4(ta.M, ta.n0, ta.spl, ta.ks);
-  e[2] = make_int4(ta.unit0, tb.group, tb.e, tb.row0);
-  e[3] = make_int4(kind == 1 ? tb.M : 0, tb.n0, 0, 0);
+  const int kind = plan::resolve_slot<BM, BN, GN>(sh, S, L, g % kXcds, g / kXcds, mode, ta, tb);
+  int e[plan::kEntryInts];
+  plan::encode_entry(kind, ta, tb, e);
+  int4* dst = table + kTableInt4 * i;
+#pragma unroll
+  for (int q = 0; q < kTableInt4; ++q)
+    dst[q] = make_int4(e[4 * q], e[4 * q + 1], e[4 * q + 2], e[4 * q + 3]);
 }
 
 // One launch plans both GEMMs of the FFN (blockIdx.y: 0 up, 1 down).
 template <int BM, int BN, int GN>
 __global__ __launch_bounds__(kThreads) void big_plan_kernel(GemmArgs up, GemmArgs down) {
-  __shared__ SchedLds L;
+  __shared__ plan::Tables L;
   if (blockIdx.y == 0)
     plan_launch<BM, BN, GN>(up, const_cast<int4*>(up.table), L);
   else
@@ -1133,15 +934,12 @@ FfnLayout ffn_layout(const void* xs, const int32_t* gather, int gk, const int32_
   if (Lo.big) {
     int4* tab = static_cast<int4*>(at(Lo.table));
     for (GemmArgs* a : {&up, &down}) {
-      // split K only where every group's K is long (see kSplitMinK)
-      const bool long_k = a->routed.K >= kSplitMinK && (a->shared_M == 0 || a->shared.K >= kSplitMinK);
-      a->part = long_k ? static_cast<float*>(at(Lo.part)) : nullptr;
-      // worst-case tiles rounded up to whole slots of every XCD; a split last
-      // round adds at most one round of kSlots per XCD
-      dim3 grid;
-      grid_of<256, 256>(*a, rows, E, grid);
-      a->slots = (int)((grid.x + kXcds - 1) / kXcds * kXcds) +
-                 (a->part ? kXcds * kSlots : 0);
+      // split K only where every group's K is long (plan::split_ok), and the
+      // launch's workgroups from the same shape the planner sees
+      plan::Shape sh{E, rows, a->shared_M, a->routed.N, a->routed.K, a->shared.N, a->shared.K, 0, 0};
+      sh.split = plan::split_ok(sh) ? 1 : 0;
+      a->part = sh.split ? static_cast<float*>(at(Lo.part)) : nullptr;
+      a->slots = plan::launch_slots<256, 256>(sh);
       a->table = tab ? tab + table_bytes / sizeof(int4) : nullptr;
       table_bytes += (size_t)(a->slots + kReduceSlots) * kTableInt4 * sizeof(int4);
     }

@@ -1,133 +1,121 @@
-"""Coverage of the big-tile schedule of the grouped GEMM (host logic check).
+"""Coverage of the big-tile schedule of the grouped GEMM (host check, no GPU).
 
-The planner of csrc/ffn.hip (big_schedule, resolve_slot, small_tile_of) runs on
-the device; this file transcribes its integer arithmetic step for step and
-checks, over random expert-count vectors, shapes and both launch kinds (split
-K in the last round; small-segment pairs), that the workgroup slots cover every
-32-row x 128-column block of every segment and of the shared group exactly once, each split
-tile in all its K slices, that small tiles stay inside their segments, and
-that the reduce slots are exactly the split tail tiles. It must follow the
-device code when that changes; the GPU tests check the device code itself.
+The planner's arithmetic lives in the library's csrc/plan.hpp; the device
+planner (big_plan_kernel) and this check run the same functions. The test
+compiles plan.hpp with a small host shim (tests/plan_host.cpp) and checks,
+over random expert-count vectors, shapes and both launch kinds (split K in the
+last round; short-segment pairs), the table it writes:
+  * every 32-row x 128-column block of every segment and of the shared group
+    is computed exactly once (each split tile in all of its K slices),
+  * short-segment tiles stay inside their segments, big tiles inside the
+    buffer and the column range,
+  * the reduce slots are exactly the split tail tiles, each once.
 """
+import ctypes
+import os
+import subprocess
+
 import numpy as np
-# constants of ffn.hip: XCDs, CUs per XCD, split limits, small-segment rows, tile shapes, n-block
-kX, kSlots, kMaxSplit, kMinSlice, kSmallRows, kSBM, kSBN, BM, BN, GN = 8, 32, 8, 32, 33, 32, 128, 256, 256, 4
-kReduce = kX * kSlots // 2
-def cdiv(a, b): return (a + b - 1) // b
-def sched(counts, Nr, Kr, shared_M, Ns, Ks, part, slots):
-    E = len(counts); ng = E + (1 if shared_M > 0 else 0)
-    off = np.concatenate([[0], np.cumsum(counts)])
-    goff = list(off[:E]) + ([0] if shared_M else []); gcnt = list(counts) + ([shared_M] if shared_M else [])
-    ntr, nts, nsr = cdiv(Nr, BN), cdiv(Ns, BN), cdiv(Nr, kSBN)
-    small_ok = part is None
-    pa, pf, ps = [], [], []
-    for g in range(ng):
-        c = gcnt[g]; allt = cdiv(c, BM) * (ntr if g < E else nts)
-        sm = small_ok and g < E and 0 < c < kSmallRows
-        pa.append(allt); pf.append(0 if sm else allt); ps.append(cdiv(c, kSBM) * nsr if sm else 0)
-    pa, pf, ps = np.cumsum(pa), np.cumsum(pf), np.cumsum(ps)
-    Fs, Ps = pf[-1], (ps[E - 1] + 1) // 2
-    if Ps > 0 and kX * (cdiv(Fs, kX) + cdiv(Ps, kX)) <= slots and cdiv(Fs, kX) + cdiv(Ps, kX) < (1 << 15): use, F, P = pf, Fs, Ps
-    else: use, F, P = pa, pa[-1], 0
-    CF, CP = cdiv(F, kX), cdiv(P, kX)
-    R, tail = CF // kSlots, CF - (CF // kSlots) * kSlots
-    spl = 1
-    if part is not None and tail > 0 and 2 * tail <= kSlots:
-        ktmin = Kr // 64
-        if shared_M > 0: ktmin = min(ktmin, Ks // 64)
-        spl = max(1, min(min(kSlots // tail, kMaxSplit), ktmin // kMinSlice))
-    return dict(E=E, ng=ng, goff=goff, gcnt=gcnt, use=use, ps=ps, F=F, P=P, CF=CF, CP=CP, R=R, tail=tail, spl=spl, ntr=ntr, nts=nts)
-def find(scan, n, q):
-    lo, hi = 0, n - 1
-    while lo < hi:
-        mid = (lo + hi) // 2
-        if scan[mid] > q: hi = mid
-        else: lo = mid + 1
-    return lo
-def small_of(S, u):
-    g = find(S["ps"], S["E"], u); li = u - (S["ps"][g - 1] if g else 0); c = S["gcnt"][g]; nrs = cdiv(c, kSBM)
-    r = li % nrs
-    return ("s", g, S["goff"][g] + r * kSBM, min(kSBM, c - r * kSBM), (li // nrs) * kSBN)
-def resolve(S, x, slot, mode):
-    CF, R, tail, spl = S["CF"], S["R"], S["tail"], S["spl"]; ks, unit0 = 0, -1
-    if mode == 0:
-        if S["CP"] > 0:
-            n = CF + S["CP"]
-            if slot >= n: return None
-            pb = slot * S["CP"] // n
-            if (slot + 1) * S["CP"] // n > pb:
-                p = pb * kX + x
-                if p >= S["P"]: return None
-                nsm = S["ps"][S["E"] - 1]
-                a = small_of(S, 2 * p); b = small_of(S, 2 * p + 1) if 2 * p + 1 < nsm else None
-                return ("pair", a, b)
-            slot -= pb
-        if spl > 1 and slot >= R * kSlots:
-            u = slot - R * kSlots
-            if u >= tail * spl: return None
-            tt = u // spl; ks = u - tt * spl; slot = R * kSlots + tt; unit0 = x * kSlots + tt * spl
-    else:
-        if spl <= 1 or slot >= tail: return None
-        unit0 = x * kSlots + slot * spl; slot = R * kSlots + slot
-    if slot >= CF: return None
-    q = x * CF + slot
-    if q >= S["F"]: return None
-    use = S["use"]; g = find(use, S["ng"], q); excl = use[g - 1] if g else 0
-    o, c = S["goff"][g], S["gcnt"][g]; mt = cdiv(c, BM); nt = S["ntr"] if g < S["E"] else S["nts"]
-    local = q - excl; blk = local // (mt * GN); w = min(GN, nt - blk * GN); li = local - blk * mt * GN
-    return ("big", g, o + (li // w) * BM, min(BM, c - (li // w) * BM), (blk * GN + li % w) * BN, spl if unit0 >= 0 else 1, ks, unit0)
-def check(counts, Nr, Kr, shared_M, Ns, Ks, part):
-    E = len(counts); rows = int(sum(counts))
-    grid = (rows // BM + min(E, rows)) * cdiv(Nr, BN) + (cdiv(shared_M, BM) * cdiv(Ns, BN) if shared_M else 0)
-    slots = cdiv(grid, kX) * kX + (kX * kSlots if part else 0)
-    S = sched(counts, Nr, Kr, shared_M, Ns, Ks, part, slots)
-    cover = {}  # (group, row, col) element blocks -> list of k slices
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "sparse_mixture_experts_05_amd", "csrc")
+BM = BN = 256
+SBM, SBN = 32, 128  # short-segment tiles (plan.hpp kSBM, kSBN)
+
+
+@pytest.fixture(scope="module")
+def planner(tmp_path_factory):
+    out = str(tmp_path_factory.mktemp("plan") / "plan_host.so")
+    cmd = ["g++", "-O2", "-std=c++17", "-shared", "-fPIC", f"-I{CSRC}",
+           os.path.join(ROOT, "tests", "plan_host.cpp"), "-o", out]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    L = ctypes.CDLL(out)
+    i, p = ctypes.c_int, ctypes.c_void_p
+    L.moe_plan_slots.restype = i
+    L.moe_plan_slots.argtypes = [i] * 7 + [ctypes.POINTER(i)]
+    L.moe_plan_table.restype = None
+    L.moe_plan_table.argtypes = [p] + [i] * 9 + [p]
+    return L
+
+
+def plan(L, counts, Nr, Kr, shared_M, Ns, Ks):
+    """(table [slots + reduce, 16], slots, split) of one launch."""
+    E = len(counts)
+    rows = int(sum(counts))
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    split = ctypes.c_int(0)
+    slots = L.moe_plan_slots(E, rows, shared_M, Nr, Kr, Ns, Ks, ctypes.byref(split))
+    n = slots + L.moe_plan_reduce_slots()
+    table = np.full((n, L.moe_plan_entry_ints()), -7, dtype=np.int32)
+    L.moe_plan_table(offsets.ctypes.data, E, rows, shared_M, Nr, Kr, Ns, Ks, split.value, slots,
+                     table.ctypes.data)
+    return table, slots, split.value
+
+
+def check(L, counts, Nr, Kr, shared_M, Ns, Ks):
+    E = len(counts)
+    goff = list(np.concatenate([[0], np.cumsum(counts)])[:E]) + [0]
+    gcnt = list(counts) + [shared_M]
+    table, slots, split = plan(L, counts, Nr, Kr, shared_M, Ns, Ks)
+    cover = {}  # (group, row, col) blocks -> list of (k slice, slices)
     red = set()
+    pairs = 0
     for g in range(slots):
-        r = resolve(S, g % kX, g // kX, 0)
-        if r is None: continue
-        if r[0] == "pair":
-            for t in r[1:]:
-                if t is None: continue
-                _, gr, row0, M, n0 = t
-                assert 0 < M <= kSBM and row0 >= S["goff"][gr] and row0 + M <= S["goff"][gr] + S["gcnt"][gr]
+        e = table[g]
+        kind = e[0]
+        if kind < 0:
+            continue
+        if kind == 1:
+            pairs += 1
+            assert not split  # no pairs in split-K launches
+            for (grp, ex, row0, M, n0) in [(e[1], e[2], e[3], e[4], e[5]),
+                                           (e[9], e[10], e[11], e[12], e[13])]:
+                if M == 0:
+                    continue
+                assert grp == 0 and 0 < M <= SBM
+                assert goff[ex] <= row0 and row0 + M <= goff[ex] + gcnt[ex]
+                assert gcnt[ex] < 33  # only short segments take small tiles
                 for rr in range(row0, row0 + M, 32):
-                    for cc in range(n0, min(n0 + kSBN, Nr), 128):
-                        cover.setdefault((gr, rr, cc), []).append((0, 1))
-        else:
-            _, gr, row0, M, n0, sp, ks, unit0 = r
-            N = Nr if gr < E else Ns
-            for rr in range(row0, row0 + M, 32):
-                for cc in range(n0, min(n0 + BN, N), 128):
-                    cover.setdefault((gr, rr, cc), []).append((ks, sp))
-            if unit0 >= 0: red.add(unit0)
+                    for cc in range(n0, min(n0 + SBN, Nr), 128):
+                        cover.setdefault((ex, rr, cc), []).append((0, 1))
+            continue
+        assert kind == 0
+        grp, ex, row0, M, n0, spl, ks, unit0 = e[1:9]
+        gi = ex if grp == 0 else E
+        N = Nr if grp == 0 else Ns
+        assert 0 < M <= BM and goff[gi] <= row0 and row0 + M <= goff[gi] + gcnt[gi]
+        assert 0 <= n0 < N and n0 % BN == 0
+        assert (spl == 1 and ks == 0 and unit0 == -1) or (split and 0 <= ks < spl and unit0 >= 0)
+        for rr in range(row0, row0 + M, 32):
+            for cc in range(n0, min(n0 + BN, N), 128):
+                cover.setdefault((gi, rr, cc), []).append((ks, spl))
+        if unit0 >= 0:
+            red.add(int(unit0))
     # reduce slots: exactly the split tail tiles, each once
     seen = set()
-    for i in range(kReduce):
-        r = resolve(S, i % kX, i // kX, 1)
-        if r is not None:
-            assert r[7] in red and r[7] not in seen
-            seen.add(r[7])
+    for e in table[slots:]:
+        if e[0] < 0:
+            continue
+        assert e[0] == 0 and e[6] > 1
+        assert int(e[8]) in red and int(e[8]) not in seen
+        seen.add(int(e[8]))
     assert seen == red
     expect = set()
-    for gr in range(E):
-        base = S["goff"][gr]; c = S["gcnt"][gr]
-        if c == 0: continue
-        step = kSBM if (S["P"] > 0 and 0 < c < kSmallRows) else BM
-        for t0 in range(base, base + c, step):
-            for rr in range(t0, min(t0 + step, base + c), 32):
-                for cc in range(0, Nr, 128): expect.add((gr, rr, cc))
-    if shared_M:
-        for rr in range(0, shared_M, 32):
-            for cc in range(0, Ns, 128): expect.add((E, rr, cc))
-    assert set(cover) == expect, (len(set(cover) ^ expect))
-    for k, v in cover.items():
+    for gi in range(E + (1 if shared_M else 0)):
+        N = Nr if gi < E else Ns
+        for rr in range(goff[gi], goff[gi] + gcnt[gi], 32):
+            for cc in range(0, N, 128):
+                expect.add((gi, rr, cc))
+    assert set(cover) == expect, len(set(cover) ^ expect)
+    for key, v in cover.items():
         sp = v[0][1]
-        assert sorted(x[0] for x in v) == list(range(sp)), (k, v)
-    return S["P"], S["spl"]
+        assert sorted(x[0] for x in v) == list(range(sp)), (key, v)
+    return pairs, split and any(table[g][6] > 1 for g in range(slots) if table[g][0] == 0)
 
 
-def test_schedule_covers_every_block_once():
+def test_schedule_covers_every_block_once(planner):
     rng = np.random.default_rng(0)
     stats = {"pairs": 0, "split": 0}
     for trial in range(120):
@@ -140,9 +128,29 @@ def test_schedule_covers_every_block_once():
         Fs = int(rng.choice([0, F]))
         T = rows // max(1, int(rng.choice([1, 2, 8])))
         for (Nr, Kr, Ns, Ks) in [(F, H, Fs, H), (H, F, H, Fs)]:
-            part = "p" if (Kr >= 8192 and (Fs == 0 or Ks >= 8192)) else None
-            P, spl = check(counts, Nr, Kr, T if Fs else 0, Ns, Ks, part)
-            stats["pairs"] += P > 0
-            stats["split"] += spl > 1
+            pairs, split = check(planner, counts, Nr, Kr, T if Fs else 0, Ns, Ks)
+            stats["pairs"] += pairs > 0
+            stats["split"] += bool(split)
     # both launch kinds were exercised
     assert stats["pairs"] > 20 and stats["split"] > 20, stats
+
+
+def test_schedule_of_the_workload_shapes(planner):
+    """The three big-tile workloads with their expected routing shapes: the
+    Mixtral-shaped down projection splits its last round; the fine-grained
+    layer's short segments run in pairs; E = 256 with a shared expert (257
+    groups) is covered too."""
+    rng = np.random.default_rng(1)
+    mix = np.array([982, 1067, 1010, 1040, 1001, 1023, 1050, 1019])
+    assert check(planner, mix, 4096, 14336, 0, 4096, 14336)[1]   # split tail
+    assert not check(planner, mix, 14336, 4096, 0, 14336, 4096)[1]
+    fg = rng.multinomial(32768, rng.dirichlet(np.full(128, 0.05)))
+    assert check(planner, fg, 1536, 4096, 4096, 1536, 4096)[0] > 0  # pairs
+    check(planner, fg, 4096, 1536, 4096, 4096, 1536)
+    hs = rng.multinomial(131072, rng.dirichlet(np.full(256, 0.05)))
+    check(planner, hs, 1024, 4096, 0, 1024, 4096)
+    check(planner, hs, 4096, 1024, 16384, 4096, 1024)               # 257 groups
+    # edge cases: one row in all, everything in one expert, empty experts
+    check(planner, np.array([1]), 512, 256, 0, 512, 256)
+    check(planner, np.array([0, 0, 5000, 0]), 4096, 8192, 0, 4096, 8192)
+    check(planner, np.array([0] * 255 + [300]), 1024, 4096, 300, 1024, 4096)
