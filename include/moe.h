@@ -65,7 +65,8 @@ typedef enum {
   MOE_ERR_INVALID_ARG = -1, /* null or misaligned pointer, non-positive size, bad enum */
   MOE_ERR_UNSUPPORTED = -2, /* shape outside the supported range */
   MOE_ERR_WORKSPACE = -3,   /* workspace missing or smaller than the query */
-  MOE_ERR_HIP = -4          /* a HIP launch failed */
+  MOE_ERR_HIP = -4,         /* a HIP launch failed */
+  MOE_ERR_SCRATCH = -5      /* beyond the fixed scratch of moe_dispatch_noalloc */
 } moe_status;
 
 /* Load diagnostics of one step ([DIAG] section 3). Written to device memory. */
@@ -139,6 +140,27 @@ size_t moe_dispatch_workspace_bytes(int T, int E, int k);
 int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, int k, int dtype,
                  int32_t* counts, int32_t* offsets, int32_t* perm, int32_t* inv, void* xs,
                  void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * moe_dispatch_noalloc - moe_dispatch for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc): the same kernels and results, bit for bit, with the
+ * histogram table in a fixed 1 MiB device array of the library instead of a
+ * caller workspace. The library itself never allocates in this call.
+ * Limit: the table needs E * ceil(T / 256) * 4 bytes (64-token blocks for
+ * 256 < T <= 4096 with k >= 4), which must fit 1 MiB: every T <= 2^26 / E
+ * (T <= 262144 at E = 256). A larger request returns MOE_ERR_SCRATCH and
+ * enqueues nothing.
+ * Each GPU holds one copy of the array until the process ends, and every call
+ * on that GPU shares it: two calls that may run at the same time on one GPU
+ * (on different streams, or from different host threads) race and give wrong
+ * results; calls ordered on one stream do not. Nothing in the array needs
+ * clearing between calls (the histogram launch writes every entry the rank
+ * launch reads). Arguments, outputs and other errors as moe_dispatch.
+ */
+int moe_dispatch_noalloc(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
+                         int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* inv, void* xs, void* stream);
 
 /*
  * moe_capacity - the per-expert capacity of [DIAG] section 3 (its

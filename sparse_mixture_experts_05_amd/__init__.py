@@ -9,12 +9,13 @@ dynamic routing-bias step that feeds the next layer call. Every step runs in
 the HIP kernels; this package only marshals tensors, sizes and the current stream.
 """
 from .binding import (MoEError, MoELayerGraph, lib, moe_bias_update, moe_capacity, moe_combine,
-                      moe_dispatch, moe_expert_ffn, moe_expert_ffn_gather,
+                      moe_dispatch, moe_dispatch_noalloc, moe_expert_ffn, moe_expert_ffn_gather,
                       moe_layer_forward, moe_load_stats, moe_route, moe_status_string,
                       moe_dispatch_workspace_bytes, moe_expert_ffn_workspace_bytes,
                       moe_route_workspace_bytes)
 
-__all__ = ["MoEError", "MoELayerGraph", "lib", "moe_route", "moe_dispatch", "moe_expert_ffn",
+__all__ = ["MoEError", "MoELayerGraph", "lib", "moe_route", "moe_dispatch",
+           "moe_dispatch_noalloc", "moe_expert_ffn",
            "moe_expert_ffn_gather", "moe_combine",
            "moe_load_stats", "moe_bias_update", "moe_capacity", "moe_layer_forward", "moe_status_string",
            "moe_dispatch_workspace_bytes", "moe_expert_ffn_workspace_bytes",

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libmoe.so")
 
 MOE_F32, MOE_BF16 = 0, 1
 STATUS = {0: "MOE_OK", -1: "MOE_ERR_INVALID_ARG", -2: "MOE_ERR_UNSUPPORTED",
-          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP"}
+          -3: "MOE_ERR_WORKSPACE", -4: "MOE_ERR_HIP", -5: "MOE_ERR_SCRATCH"}
 
 _vp, _i, _sz, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
 
@@ -36,6 +36,7 @@ SIGNATURES = {
     "moe_load_stats": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
     "moe_bias_update": (_i, [_vp, _i, ctypes.c_float, _vp, _vp, _vp]),
     "moe_capacity": (ctypes.c_int64, [_i, _i, _i, _d]),
+    "moe_dispatch_noalloc": (_i, [_vp, _vp, _i, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_status_string": (ctypes.c_char_p, [_i]),
 }
 
@@ -245,6 +246,37 @@ def moe_dispatch(topk_idx, x, E: int, out=None, ws=None, stream=None, capacity=N
         _check("moe_dispatch_capped", lib().moe_dispatch_capped(
             _dev(topk_idx, "topk_idx", torch.int32), _dev(x, "x"), T, H, E, k, int(capacity),
             *tail))
+    return out
+
+
+def moe_dispatch_noalloc(topk_idx, x, E: int, out=None, stream=None, gather: bool = True):
+    """moe_dispatch on the library's fixed device scratch (no workspace): for
+    callers that cannot allocate device memory. The same dict as moe_dispatch;
+    ``out`` (preallocated outputs) avoids every allocation here too."""
+    T, H = _dims(x, "x", 2)
+    k = _dims(topk_idx, "topk_idx", 2)[1]
+    _want(topk_idx, "topk_idx", (T, k), torch.int32)
+    if out is not None:
+        _want(out.get("counts"), "counts", (E,), torch.int32)
+        _want(out.get("offsets"), "offsets", (E + 1,), torch.int32)
+        _want(out.get("perm"), "perm", (T * k,), torch.int32)
+        _want(out.get("inv"), "inv", (T * k,), torch.int32)
+        _want(out.get("xs"), "xs", (T * k, H), x.dtype)
+        for key in ["counts", "offsets", "perm", "inv"]:
+            if out.get(key) is None:
+                raise ValueError(f"out[{key!r}] is required")
+    dev = x.device
+    if out is None:
+        out = dict(counts=torch.empty(E, dtype=torch.int32, device=dev),
+                   offsets=torch.empty(E + 1, dtype=torch.int32, device=dev),
+                   perm=torch.empty(T * k, dtype=torch.int32, device=dev),
+                   inv=torch.empty(T * k, dtype=torch.int32, device=dev),
+                   xs=torch.empty((T * k, H), dtype=x.dtype, device=dev) if gather else None)
+    _check("moe_dispatch_noalloc", lib().moe_dispatch_noalloc(
+        _dev(topk_idx, "topk_idx", torch.int32), _dev(x, "x"), T, H, E, k, _dtype_code(x),
+        _dev(out["counts"], "counts", torch.int32), _dev(out["offsets"], "offsets", torch.int32),
+        _dev(out["perm"], "perm", torch.int32), _dev(out["inv"], "inv", torch.int32),
+        _dev(out.get("xs"), "xs", x.dtype), _stream(stream)))
     return out
 
 

@@ -27,6 +27,8 @@
 // an assignment whose rank among its expert's assignments (token order) is
 // cap or more is dropped: inv = -1, no buffer row. offsets then describe the
 // kept rows (min(count, cap) per expert); counts stay the raw counts.
+#include <mutex>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -289,6 +291,61 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H,
                      static_cast<const uint4*>(x), inv, T, row_bytes / 16, k,
                      static_cast<uint4*>(xs));
   return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- no-alloc variant
+
+namespace {
+
+// Scratch of moe_dispatch_noalloc, for callers that cannot allocate: the
+// [E x blocks] histogram table lives in this fixed device array instead of a
+// caller workspace. Every GPU the library runs on holds its own copy until the
+// process ends. Host code never passes the array's name to a kernel (on the
+// host it is only a stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device.
+constexpr size_t kNoAllocScratchBytes = size_t(1) << 20;
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+
+}  // namespace
+
+size_t noalloc_scratch_bytes() { return kNoAllocScratchBytes; }
+
+// Device address of the current device's copy of `scratch`, looked up on the
+// first call on that device (with it current) and kept per device.
+hipError_t noalloc_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  std::lock_guard<std::mutex> lock(mu);
+  if (ptr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr) return hipErrorInvalidSymbol;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+// moe_dispatch on the fixed scratch: the same kernels, the table in `scratch`
+// (its address from noalloc_scratch, never the array's name). Every entry of
+// the table is written by the histogram launch before the rank launch reads
+// it, so nothing needs clearing between calls. The caller has checked that
+// dispatch_ws_bytes(T, E, k) fits kNoAllocScratchBytes.
+hipError_t launch_dispatch_noalloc(const int32_t* topk_idx, const void* x, int T, int H, int E,
+                                   int k, bool bf16, int32_t* counts, int32_t* offsets,
+                                   int32_t* perm, int32_t* inv, void* xs, hipStream_t s) {
+  if (dispatch_ws_bytes(T, E, k) > kNoAllocScratchBytes) return hipErrorInvalidValue;
+  void* ws = nullptr;
+  const hipError_t e = noalloc_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return launch_dispatch(topk_idx, x, T, H, E, k, -1, bf16, counts, offsets, perm, inv, xs, ws, s);
 }
 
 }  // namespace moe

@@ -18,6 +18,11 @@ hipError_t launch_dispatch(const int32_t* topk_idx, const void* x, int T, int H,
                            int cap, bool bf16, int32_t* counts, int32_t* offsets, int32_t* perm,
                            int32_t* inv, void* xs, void* ws, hipStream_t s);
 
+size_t noalloc_scratch_bytes();
+hipError_t launch_dispatch_noalloc(const int32_t* topk_idx, const void* x, int T, int H, int E,
+                                   int k, bool bf16, int32_t* counts, int32_t* offsets,
+                                   int32_t* perm, int32_t* inv, void* xs, hipStream_t s);
+
 size_t ffn_ws_bytes(int rows, int T, int E, int H, int F, int Fs, bool bf16);
 hipError_t launch_expert_ffn(const void* xs, const int32_t* gather, int gk,
                              const int32_t* offsets, int rows, int E, int H, int F, const void* w1,

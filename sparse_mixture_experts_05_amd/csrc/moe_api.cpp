@@ -44,6 +44,7 @@ const char* moe_status_string(int status) {
     case MOE_ERR_UNSUPPORTED: return "unsupported shape (needs 1<=E<=256, 1<=k<=min(E,8), H%64==0, F%64==0, T*k<2^31)";
     case MOE_ERR_WORKSPACE: return "workspace missing or smaller than the size query returned";
     case MOE_ERR_HIP: return "HIP launch failed";
+    case MOE_ERR_SCRATCH: return "request exceeds the fixed 1 MiB scratch of moe_dispatch_noalloc (needs E * ceil(T / 256) * 4 <= 1 MiB; use moe_dispatch with a workspace)";
     default: return "unknown status";
   }
 }
@@ -82,6 +83,19 @@ int moe_dispatch(const int32_t* topk_idx, const void* x, int T, int H, int E, in
   if (!ws || ws_bytes < moe::dispatch_ws_bytes(T, E, k)) return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_dispatch(topk_idx, x, T, H, E, k, -1, dtype == MOE_BF16, counts,
                                        offsets, perm, inv, xs, ws, as_stream(stream)));
+}
+
+int moe_dispatch_noalloc(const int32_t* topk_idx, const void* x, int T, int H, int E, int k,
+                         int dtype, int32_t* counts, int32_t* offsets, int32_t* perm,
+                         int32_t* inv, void* xs, void* stream) {
+  if (!topk_idx || !counts || !offsets || !perm || !inv || !dtype_ok(dtype))
+    return MOE_ERR_INVALID_ARG;
+  if (xs && (!x || !aligned16(x) || !aligned16(xs))) return MOE_ERR_INVALID_ARG;
+  const int st = check_tokens(T, H, E, k);
+  if (st != MOE_OK) return st;
+  if (moe::dispatch_ws_bytes(T, E, k) > moe::noalloc_scratch_bytes()) return MOE_ERR_SCRATCH;
+  return from_hip(moe::launch_dispatch_noalloc(topk_idx, x, T, H, E, k, dtype == MOE_BF16, counts,
+                                               offsets, perm, inv, xs, as_stream(stream)));
 }
 
 int64_t moe_capacity(int T, int k, int E, double capacity_factor) {

@@ -38,7 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_status_strings():
-    for code in [0, -1, -2, -3, -4]:
+    for code in [0, -1, -2, -3, -4, -5]:
         assert moe.moe_status_string(code)
     assert moe.moe_status_string(17) == "unknown status"
 
@@ -350,3 +350,22 @@ def test_binding_rejects_mismatched_shapes():
         with pytest.raises(ValueError) as info:
             call()
         assert "GPU tensor" not in str(info.value), (name, str(info.value))
+
+
+def test_dispatch_noalloc_validation():
+    """moe_dispatch_noalloc: moe_dispatch's checks, and a histogram table
+    (E * ceil(T / 256) * 4 bytes, 64-token blocks for 256 < T <= 4096 with
+    k >= 4) beyond its fixed 1 MiB scratch is refused with MOE_ERR_SCRATCH,
+    all before any HIP call."""
+    L = moe.lib()
+    f = L.moe_dispatch_noalloc
+    assert f(None, None, 16, 64, 8, 2, 1, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert f(FAKE, None, 16, 64, 8, 2, 7, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert f(FAKE, None, 16, 64, 8, 2, 1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == -1  # xs needs x
+    assert f(FAKE, None, 16, 64, 300, 2, 1, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    for E in [1, 8, 128, 256]:
+        T_max = (1 << 26) // E        # the largest T whose table fits 1 MiB
+        assert L.moe_dispatch_workspace_bytes(T_max, E, 1) <= 1 << 20
+        assert L.moe_dispatch_workspace_bytes(T_max + 256, E, 1) > 1 << 20
+        assert f(FAKE, None, T_max + 256, 64, E, 1, 1, FAKE, FAKE, FAKE, FAKE, None, None) == -5
+    assert "scratch" in moe.moe_status_string(-5)
