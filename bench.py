@@ -89,10 +89,15 @@ def algorithmic_work(cfg, counts=None, kept=None, fused=True):
 
 def gemm_kernel_name(cfg):
     """The grouped-GEMM kernel the FFN launches run (the rule of the library's
-    launcher: 256x256 tiles once there are 64 rows per expert on average)."""
+    launcher: 256x256 tiles once there are 64 rows per expert on average, on
+    the 4-wave kernel while every operand buffer is under 4 GiB)."""
     if cfg.dtype != "bf16":
         return "gemm_f32_kernel"
-    return "gemm_bf16_big_kernel" if cfg.T * cfg.k >= 64 * cfg.E else "gemm_bf16_kernel"
+    if cfg.T * cfg.k < 64 * cfg.E:
+        return "gemm_bf16_kernel"
+    rows = cfg.T * cfg.k
+    wide = max(cfg.T * cfg.H, rows * cfg.H, rows * cfg.F, cfg.T * cfg.Fs) * 2 >= 1 << 32
+    return "gemm_bf16_big_kernel" if wide else "gemm_bf16_w4_kernel"
 
 
 def code_sha256(path):

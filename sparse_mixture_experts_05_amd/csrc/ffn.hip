@@ -35,6 +35,7 @@
 // fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "common.hpp"
 #include "kernels.hpp"
@@ -66,6 +67,7 @@ struct GemmArgs {
   int slots;         // big kernel: workgroups of the launch (= reduce table start)
   const int32_t* gather;  // routed rows read through perm: A row p = token perm[p] / gk, or null
   int gk, gT;             // experts per token and tokens of that gather
+  int wide;               // an A operand buffer of 4 GiB or more (big tiles: 8-wave kernel)
 };
 
 // Row of the A operand that buffer row p of a group reads: p itself, or for
@@ -80,6 +82,18 @@ __device__ __forceinline__ size_t a_row(const GemmArgs& a, int group, int p) {
 }
 
 using plan::Tile;
+
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N-1>{}):
+// a loop whose index is a compile-time constant in every step, so register
+// arrays indexed by it stay in registers.
+template <typename F, int... I>
+__device__ __forceinline__ void static_for_impl(F&& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
 
 // Field-wise select (a reference into the kernel arguments chosen at run time
 // would force a private-memory copy of the whole struct).
@@ -459,6 +473,91 @@ __global__ __launch_bounds__(kThreads) void gemm_small_reduce_kernel(GemmArgs ar
 
 // ----------------------------------------------------------------- bf16 MFMA, large tiles
 
+// Epilogue of a 256-column big tile computed by NW waves in a 2 x (NW/2)
+// grid (wave tile (BM/2) x (BN/(NW/2)) of 32x32 accumulators): one K slice of
+// a split tail tile writes its fp32 partial tile; otherwise erf-GeLU (up
+// projection), bf16 rounding and coalesced row stores through an LDS tile.
+template <int BM, int BN, int NW, bool GELU, int SM, int SN>
+__device__ __forceinline__ void big_tile_epilogue(const GemmArgs& args, const Tile& t, uint16_t* C,
+                                                  int N, int M, int nvalid,
+                                                  f32x16_t (&acc)[SM][SN], uint8_t* smem) {
+  constexpr int WN_ = NW / 2;
+  constexpr int WTM = BM / 2, WTN = BN / WN_;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN_, wn = wave % WN_;
+  if (t.unit0 >= 0) {
+    // one K slice of a split tail tile: the fp32 partial tile, row-major,
+    // goes to its slot; the reduce launch sums the slices and runs the epilogue
+    float* P = args.part + (size_t)(t.unit0 + t.ks) * BM * BN;
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
+          const int col = wn * WTN + j * 32 + (lane & 31);
+          P[(size_t)row * BN + col] = acc[i][j][v];
+        }
+    return;
+  }
+
+  // Epilogue through LDS. 32x32 D layout: lane holds column lane%32 and rows
+  // (v/4)*8 + (lane/32)*4 + v%4. Each lane converts its rows (v, v+1) of its
+  // column to a bf16 pair in one instruction; lanes 2m and 2m+1 (adjacent
+  // columns) swap those words with DPP, and a byte permute leaves the even
+  // lane the pair (row R(v), its column and the next) and the odd lane the
+  // same for row R(v) + 1. The pairs go to a [BM x BN] bf16 tile in LDS (the
+  // operand stages are free by then), 512-byte rows whose 16-dword groups are
+  // XOR-swizzled by row bits 0 and 2: the four rows one write instruction
+  // touches (r, r+1, r+4, r+5) land in four different bank quarters. Those
+  // two row bits are the lane's parity and lane / 32 for every value, so the
+  // swizzled address is a per-lane base plus a constant. Then every wave
+  // stores whole rows, 16 bytes per lane (two 512-byte rows per instruction).
+  static_assert(BN == 256, "C tile in LDS: 512-byte rows");
+  constexpr int CROWB = BN * 2;
+  const int odd = lane & 1, hi = lane >> 5;
+  const int cg = odd | (hi << 1);  // == (row & 1) | ((row >> 2) & 1) << 1 for this lane's rows
+  const int rbase = wm * WTM + hi * 4 + odd;
+  int cbase[SN];
+#pragma unroll
+  for (int j = 0; j < SN; ++j)
+    cbase[j] = rbase * CROWB + (((wn * WTN + j * 32) / 32) ^ cg) * 64 + ((lane & 31) >> 1) * 4;
+  // even lane: low halves of (own, partner); odd lane: high halves of (partner, own)
+  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
+  lds_barrier();  // every wave has read the last stage
+#pragma unroll
+  for (int i = 0; i < SM; ++i)
+#pragma unroll
+    for (int j = 0; j < SN; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; v += 2) {
+        float y0 = acc[i][j][v], y1 = acc[i][j][v + 1];
+        if constexpr (GELU) {
+          y0 = gelu_erf_fast(y0);
+          y1 = gelu_erf_fast(y1);
+        }
+        const uint32_t own = cvt_bf16x2(y0, y1);  // (row R(v), row R(v) + 1) of this column
+        const uint32_t partner = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xF, 0xF, false);
+        const uint32_t pair = __builtin_amdgcn_perm(partner, own, sel);
+        const int roff = (i * 32 + (v >> 2) * 8 + (v & 3)) * CROWB;
+        *reinterpret_cast<uint32_t*>(smem + cbase[j] + roff) = pair;
+        // one accumulator pair at a time: keeps the scheduler from reading
+        // every accumulator out to VGPRs ahead of its conversion
+        if constexpr (NW == 4) __builtin_amdgcn_sched_barrier(0);
+      }
+  lds_barrier();
+  const int cl = lane & 31;
+  const bool cok = cl * 8 < nvalid;  // N % 64 == 0: 8-column chunks are all or nothing
+#pragma unroll 4
+  for (int it = 0; it < BM / NW / 2; ++it) {
+    const int row = wave * (BM / NW) + it * 2 + hi;
+    const int rg = (row & 1) | (((row >> 2) & 1) << 1);
+    const u32x4_t v = ld16(smem + row * CROWB + (((cl >> 2) ^ rg) << 6) + ((cl & 3) << 4));
+    if (cok && row < M) st16(C + (size_t)row * N + cl * 8, v);
+  }
+}
+
 // Large-tile kernel: BM x BN tile, NW waves in a 2 x (NW/2) grid, each wave a
 // (BM/2) x (BN/(NW/2)) block of 32x32x16 MFMAs. Two LDS stages of BK = 64; a
 // row of a staged tile is 64 bf16 = 8 chunks of 16 bytes.
@@ -614,74 +713,231 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
   else
     main_loop(std::integral_constant<bool, true>{});
 
-  if (t.unit0 >= 0) {
-    // one K slice of a split tail tile: the fp32 partial tile, row-major,
-    // goes to its slot; the reduce launch sums the slices and runs the epilogue
-    float* P = args.part + (size_t)(t.unit0 + t.ks) * BM * BN;
-#pragma unroll
-    for (int i = 0; i < SM; ++i)
-#pragma unroll
-      for (int j = 0; j < SN; ++j)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int row = wm * WTM + i * 32 + (v >> 2) * 8 + (lane >> 5) * 4 + (v & 3);
-          const int col = wn * WTN + j * 32 + (lane & 31);
-          P[(size_t)row * BN + col] = acc[i][j][v];
-        }
+  big_tile_epilogue<BM, BN, NW, GELU>(args, t, C, N, M, nvalid, acc, smem);
+}
+
+// Large-tile kernel, one wave per SIMD (the default for bf16 launches with
+// enough rows): a 256x256 tile, 4 waves, wave w a 128x128 block (rows
+// (w/2)*128, columns (w%2)*128) of 4x4 v_mfma_f32_32x32x16_bf16 accumulators
+// (all 256 accumulation registers). Against the 8-wave kernel a wave reads
+// 8 KB of fragments per 16-deep k slice for 16 MFMAs (6 KB for 8 there): a
+// third less LDS read traffic per flop.
+//
+// With one wave per SIMD nothing else feeds the matrix core, so the stage is
+// hand-ordered: every other instruction sits between two MFMAs
+// (sched_barrier fences keep the order the source gives).
+//   - k slices 1-3 of stage kt each carry the 8 fragment reads of the next
+//     slice; after the stage's one barrier, the slice that finishes the stage
+//     (k slice 0 of stage kt+1 in registers) carries the 8 reads of the next
+//     stage's first slice.
+//   - The A rows (tokens) sit in two LDS stage buffers, the B rows (weights)
+//     in three. The copies of stage kt+2 go out one every two MFMAs or so: its
+//     B rows during the first three slices of stage kt (into the buffer of
+//     stage kt-1, freed by the barrier that ended it), its A rows during the
+//     last slice, after the barrier that frees their buffer.
+//   Measured (FFN alone, one box, alternating runs): issuing all 16 copies of
+//   a stage in the last slice left that slice at about half the MFMA rate
+//   (per-slice s_memtime stamps: the other three ran at the full rate, the
+//   copy waits and the barrier cost 0.4 % and 3 %); spreading them took the
+//   dense 8192 x 14336 x 4096 up and down projections from 1052 to 1121
+//   TFLOP/s, the fine-grained layer's FFN from 696-712 to 766-777 and the
+//   heavy-skew layer's from 906 to 986-1003. A copy every four MFMAs over the
+//   whole stage (half of the A rows one slice later) gained nothing more.
+//   - Copies take a 32-bit row offset in a VGPR and a scalar base (the host
+//     launches this kernel only when every operand buffer is under 4 GiB) and
+//     the LDS address in M0, one s_mov and one global_load_lds each.
+//   - A segment's last, partial row tile skips the MFMAs of its empty 32-row
+//     sub-tiles (a wave-uniform test); its copies and barriers are unchanged.
+// Segments of at most 32 rows (table kind 1) run their two 32x128 tiles one
+// after the other on all four waves. Split-K slices and the epilogue are the
+// 8-wave kernel's.
+template <bool GELU>
+__global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs args) {
+  constexpr int NW = 4, BM = 256, BN = 256, BK = 64;
+  constexpr int ROWB = BK * 2;                     // 128 bytes = 8 chunks of 16
+  constexpr int WTM = BM / 2, WTN = BN / 2;
+  constexpr int SM = WTM / 32, SN = WTN / 32;
+  constexpr int RPI = 64 * 16 / ROWB;              // 8 rows per copy instruction
+  constexpr int A_INST = BM / RPI / NW;            // copies per wave per stage
+  constexpr int B_INST = BN / RPI / NW;
+  constexpr int A_STAGE = BM * ROWB, B_STAGE = BN * ROWB;
+  constexpr int LDS_BYTES = 2 * A_STAGE + 3 * B_STAGE;
+  static_assert(A_INST == 8 && B_INST == 8 && SM == 4 && SN == 4, "tile shape");
+  static_assert(LDS_BYTES <= 160 * 1024, "LDS of one workgroup");
+  static_assert(BM * BN * 2 <= LDS_BYTES, "the epilogue's C tile fits the stage buffers");
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
+
+  Tile t, tb;
+  const int kind = table_entry(args, blockIdx.x, t, tb);
+  if (kind < 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (kind == 1) {
+    static_assert(SmallTileShape<kSBM, kSBN>::LDS <= LDS_BYTES, "small ring");
+    small_tile<kSBM, kSBN, 1, 4>(args, t, smem, wave, true);
+    if (tb.M > 0) {
+      __syncthreads();  // every wave is done with the ring before it is refilled
+      small_tile<kSBM, kSBN, 1, 4>(args, tb, smem, wave, true);
+    }
     return;
   }
+  const Group G = pick_group(args, t.group);
+  const int N = G.N, K = G.K;
+  const uint16_t* A = static_cast<const uint16_t*>(G.A);
+  const uint16_t* B = static_cast<const uint16_t*>(G.B) + (size_t)t.e * N * K + (size_t)t.n0 * K;
+  uint16_t* C = static_cast<uint16_t*>(G.C) + (size_t)t.row0 * N + t.n0;
+  const int M = t.M;
+  const int nvalid = N - t.n0;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
 
-  // Epilogue through LDS. 32x32 D layout: lane holds column lane%32 and rows
-  // (v/4)*8 + (lane/32)*4 + v%4. Each lane converts its rows (v, v+1) of its
-  // column to a bf16 pair in one instruction; lanes 2m and 2m+1 (adjacent
-  // columns) swap those words with DPP, and a byte permute leaves the even
-  // lane the pair (row R(v), its column and the next) and the odd lane the
-  // same for row R(v) + 1. The pairs go to a [BM x BN] bf16 tile in LDS (the
-  // operand stages are free by then), 512-byte rows whose 16-dword groups are
-  // XOR-swizzled by row bits 0 and 2: the four rows one write instruction
-  // touches (r, r+1, r+4, r+5) land in four different bank quarters. Those
-  // two row bits are the lane's parity and lane / 32 for every value, so the
-  // swizzled address is a per-lane base plus a constant. Then every wave
-  // stores whole rows, 16 bytes per lane (two 512-byte rows per instruction).
-  static_assert(BM * BN * 2 <= 2 * STAGE && BN == 256, "C tile in LDS: 512-byte rows");
-  constexpr int CROWB = BN * 2;
-  const int odd = lane & 1, hi = lane >> 5;
-  const int cg = odd | (hi << 1);  // == (row & 1) | ((row >> 2) & 1) << 1 for this lane's rows
-  const int rbase = wm * WTM + hi * 4 + odd;
-  int cbase[SN];
+  // Copy plan: copy q of a wave fills 8 rows of a stage buffer, lane i row
+  // (wave * 8 + q) * 8 + i / 8, slot i & 7, which holds chunk (i & 7) ^
+  // ((r >> 1) & 7) of the row (the XOR swizzle of the 8-wave kernel: the 16
+  // lanes a 128-bit LDS read serves together hit all 64 banks once). ov holds
+  // the byte offset of the lane's chunk of K stage 0 (A rows, then B rows);
+  // rows past the segment end or the column range are clamped.
+  const int lrow = lane >> 3;
+  uint32_t ov[A_INST + B_INST];
 #pragma unroll
-  for (int j = 0; j < SN; ++j)
-    cbase[j] = rbase * CROWB + (((wn * WTN + j * 32) / 32) ^ cg) * 64 + ((lane & 31) >> 1) * 4;
-  // even lane: low halves of (own, partner); odd lane: high halves of (partner, own)
-  const uint32_t sel = odd ? 0x03020706u : 0x05040100u;
-  lds_barrier();  // every wave has read the last stage
+  for (int q = 0; q < A_INST; ++q) {
+    const int r = (wave * A_INST + q) * RPI + lrow;
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    ov[q] = (uint32_t)((a_row(args, t.group, t.row0 + min(r, M - 1)) * K + c * 8) * 2);
+  }
+#pragma unroll
+  for (int q = 0; q < B_INST; ++q) {
+    const int r = (wave * B_INST + q) * RPI + lrow;
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
+    ov[A_INST + q] = (uint32_t)(((size_t)min(r, nvalid - 1) * K + c * 8) * 2);
+  }
+  const int KT0 = K / BK;
+  const int kbase = t.ks * KT0 / t.spl, kend = (t.ks + 1) * KT0 / t.spl;
+  const int KT = kend - kbase;
+  const int last = KT - 1;
+  const uint32_t lds0 = (uint32_t)reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint8_t*)smem);
+  const uint8_t* A8 = reinterpret_cast<const uint8_t*>(A);
+  const uint8_t* B8 = reinterpret_cast<const uint8_t*>(B);
+  auto a_buf = [&](int kt) { return smem + (kt & 1) * A_STAGE; };
+  auto b_buf = [&](int slot) { return smem + 2 * A_STAGE + slot * B_STAGE; };
+  // copy q of stage kt (q < 8: A rows into A buffer kt & 1; else B rows into
+  // B buffer bslot)
+  auto copy = [&](int kt, int bslot, int q) {
+    const uint32_t kb = (uint32_t)(kbase + kt) * (BK * 2);
+    const uint32_t m0 =
+        q < A_INST ? lds0 + (uint32_t)((kt & 1) * A_STAGE + (wv * A_INST + q) * RPI * ROWB)
+                   : lds0 + (uint32_t)(2 * A_STAGE + bslot * B_STAGE +
+                                       (wv * B_INST + q - A_INST) * RPI * ROWB);
+    const uint8_t* base = (q < A_INST ? A8 : B8) + kb;
+    asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(ov[q]), "s"(base), "s"(m0)
+                 : "memory");
+  };
+
+  f32x16_t acc[SM][SN];
 #pragma unroll
   for (int i = 0; i < SM; ++i)
 #pragma unroll
     for (int j = 0; j < SN; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; v += 2) {
-        float y0 = acc[i][j][v], y1 = acc[i][j][v + 1];
-        if constexpr (GELU) {
-          y0 = gelu_erf_fast(y0);
-          y1 = gelu_erf_fast(y1);
+      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+
+  int fa[SM], fb[SN];  // LDS byte offsets of this lane's fragment rows in a buffer
+#pragma unroll
+  for (int i = 0; i < SM; ++i) fa[i] = (wm * WTM + i * 32 + (lane & 31)) * ROWB;
+#pragma unroll
+  for (int j = 0; j < SN; ++j) fb[j] = (wn * WTN + j * 32 + (lane & 31)) * ROWB;
+  const int sw = (lane >> 1) & 7;  // == (row >> 1) & 7 for every fragment row of this lane
+  const int khalf = lane >> 5;
+  // row sub-tiles of this wave that hold data: all of them except in a
+  // segment's last, partial row tile (a wave-uniform count)
+  const int nsub = __builtin_amdgcn_readfirstlane(min(SM, max(0, (M - wm * WTM + 31) / 32)));
+
+  u32x4_t ca[SM], cb[SN], na[SM], nb[SN];
+  // fragment read r of k slice ks (0..7: b0, a0, b1, b2, b3, a1, a2, a3, the
+  // order of first use)
+  auto read_r = [&](const uint8_t* sa, const uint8_t* sb, int ks, int r, u32x4_t (&fa_)[SM],
+                    u32x4_t (&fb_)[SN]) {
+    const int off = ((ks * 2 + khalf) ^ sw) << 4;
+    if (r == 0) fb_[0] = ld16(sb + fb[0] + off);
+    else if (r == 1) fa_[0] = ld16(sa + fa[0] + off);
+    else if (r <= 4) fb_[r - 1] = ld16(sb + fb[r - 1] + off);
+    else fa_[r - 4] = ld16(sa + fa[r - 4] + off);
+  };
+  auto main_loop = [&](auto partial_tag) {
+    constexpr bool PARTIAL = decltype(partial_tag)::value;
+    auto mfma_m = [&](int m, const u32x4_t (&fa_)[SM], const u32x4_t (&fb_)[SN]) {
+      const int i = m >> 2, j = m & 3;
+      if (!PARTIAL || i < nsub)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa_[i]), as_bf16x8(fb_[j]),
+                                                            acc[i][j], 0, 0, 0);
+    };
+    // One k slice: 16 MFMAs on (fa_, fb_); after each of the first 8 a read
+    // of k slice rks of buffers (rsa, rsb) into (ra_, rb_); copies q0 .. q1-1
+    // spread evenly over the 16 MFMAs (A rows of stage akt for q < 8, B rows
+    // of stage bkt into slot bslot for q >= 8).
+    auto slice = [&](const u32x4_t (&fa_)[SM], const u32x4_t (&fb_)[SN], const uint8_t* rsa,
+                     const uint8_t* rsb, int rks, u32x4_t (&ra_)[SM], u32x4_t (&rb_)[SN],
+                     auto q0c, auto q1c, int akt, int bkt, int bslot) {
+      constexpr int q0 = decltype(q0c)::value, nq = decltype(q1c)::value - q0;
+      static_for<16>([&](auto mc) {
+        constexpr int m = decltype(mc)::value;
+        mfma_m(m, fa_, fb_);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (m < 8) {
+          read_r(rsa, rsb, rks, m, ra_, rb_);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        const uint32_t own = cvt_bf16x2(y0, y1);  // (row R(v), row R(v) + 1) of this column
-        const uint32_t partner = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xF, 0xF, false);
-        const uint32_t pair = __builtin_amdgcn_perm(partner, own, sel);
-        const int roff = (i * 32 + (v >> 2) * 8 + (v & 3)) * CROWB;
-        *reinterpret_cast<uint32_t*>(smem + cbase[j] + roff) = pair;
-      }
-  lds_barrier();
-  const int cl = lane & 31;
-  const bool cok = cl * 8 < nvalid;  // N % 64 == 0: 8-column chunks are all or nothing
-#pragma unroll 4
-  for (int it = 0; it < BM / NW / 2; ++it) {
-    const int row = wave * (BM / NW) + it * 2 + hi;
-    const int rg = (row & 1) | (((row >> 2) & 1) << 1);
-    const u32x4_t v = ld16(smem + row * CROWB + (((cl >> 2) ^ rg) << 6) + ((cl & 3) << 4));
-    if (cok && row < M) st16(C + (size_t)row * N + cl * 8, v);
-  }
+        if constexpr (nq > 0 && (m * nq) / 16 != ((m + 1) * nq) / 16) {
+          constexpr int q = q0 + (m * nq) / 16;
+          copy(q < A_INST ? akt : bkt, bslot, q);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      });
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I8 = std::integral_constant<int, 8>;
+    using I11 = std::integral_constant<int, 11>;
+    using I14 = std::integral_constant<int, 14>;
+    using I16 = std::integral_constant<int, 16>;
+    // prologue: stages 0 and 1 and the B rows of stage 2 in flight, in the
+    // order the waits count them; stage 0 landed everywhere
+    static_for<A_INST + B_INST>([&](auto q) { copy(0, 0, decltype(q)::value); });
+    static_for<A_INST + B_INST>([&](auto q) { copy(min(1, last), 1, decltype(q)::value); });
+    static_for<B_INST>([&](auto q) { copy(min(2, last), 2, A_INST + decltype(q)::value); });
+    wait_vmcnt<A_INST + 2 * B_INST>();
+    lds_barrier();
+    static_for<8>([&](auto r) { read_r(a_buf(0), b_buf(0), 0, decltype(r)::value, ca, cb); });
+    // One code path for every stage: past the end the copies fetch the last
+    // stage again into buffers nobody reads any more and the reads fetch a
+    // stale buffer (both in bounds and harmless); the copies are drained
+    // before the epilogue reuses the LDS.
+    int bs = 0;  // B slot of stage kt (kt mod 3)
+    for (int kt = 0; kt < KT; ++kt) {
+      const int bs1 = bs == 2 ? 0 : bs + 1;
+      const int bsp = bs == 0 ? 2 : bs - 1;  // slot of stage kt-1 = stage kt+2
+      const int k2 = min(kt + 2, last);
+      const uint8_t* sa = a_buf(kt);
+      const uint8_t* sb = b_buf(bs);
+      slice(ca, cb, sa, sb, 1, na, nb, I8{}, I11{}, 0, k2, bsp);
+      slice(na, nb, sa, sb, 2, ca, cb, I11{}, I14{}, 0, k2, bsp);
+      slice(ca, cb, sa, sb, 3, na, nb, I14{}, I16{}, 0, k2, bsp);
+      // stage kt+1 landed for this wave (only the B copies of stage kt+2
+      // issued above may still be in flight), then for everyone; stage kt
+      // fully read, so A buffer kt & 1 is free
+      wait_vmcnt<B_INST>();
+      lds_barrier();
+      slice(na, nb, a_buf(kt + 1), b_buf(bs1), 0, ca, cb, I0{}, I8{}, k2, 0, 0);
+      bs = bs1;
+    }
+    wait_vmcnt<0>();
+  };
+  if (M == BM)
+    main_loop(std::integral_constant<bool, false>{});
+  else
+    main_loop(std::integral_constant<bool, true>{});
+  big_tile_epilogue<BM, BN, NW, GELU>(args, t, C, N, M, nvalid, acc, smem);
 }
 
 
@@ -849,13 +1105,21 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     const int nks = a.part != nullptr ? small_splits(a, rows, E) : 1;
     return run_bf16<kSmallBM, kSmallBN, 1, 2>(a, rows, E, nks, s);
   }
-  // big tiles: the table was written by big_plan_kernel
-  if (a.gelu)
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves, true>), dim3(a.slots),
-                       dim3(kBigWaves * 64), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves, false>), dim3(a.slots),
-                       dim3(kBigWaves * 64), 0, s, a);
+  // big tiles: the table was written by big_plan_kernel. The 4-wave kernel
+  // addresses its operand rows with 32-bit offsets; a launch with an operand
+  // buffer of 4 GiB or more takes the 8-wave kernel.
+  if (a.wide) {
+    if (a.gelu)
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves, true>), dim3(a.slots),
+                         dim3(kBigWaves * 64), 0, s, a);
+    else
+      hipLaunchKernelGGL((gemm_bf16_big_kernel<256, 256, kBigWaves, false>), dim3(a.slots),
+                         dim3(kBigWaves * 64), 0, s, a);
+  } else if (a.gelu) {
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<true>), dim3(a.slots), dim3(256), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((gemm_bf16_w4_kernel<false>), dim3(a.slots), dim3(256), 0, s, a);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || a.part == nullptr) return err;
   hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>), dim3(kReduceSlots * kReduceParts),
@@ -932,6 +1196,13 @@ FfnLayout ffn_layout(const void* xs, const int32_t* gather, int gk, const int32_
     Lo.table = Lo.part + align256(need);
   }
   if (Lo.big) {
+    // 32-bit row offsets of the 4-wave kernel: every A buffer under 4 GiB
+    const size_t es2 = es;
+    const size_t a_up = (size_t)(gather ? T : rows) * H * es2, a_down = (size_t)rows * F * es2;
+    const size_t s_up = (size_t)T * H * es2, s_down = (size_t)T * Fs * es2;
+    const size_t lim = size_t(1) << 32;
+    up.wide = (a_up >= lim || (shared && s_up >= lim)) ? 1 : 0;
+    down.wide = (a_down >= lim || (shared && s_down >= lim)) ? 1 : 0;
     int4* tab = static_cast<int4*>(at(Lo.table));
     for (GemmArgs* a : {&up, &down}) {
       // split K only where every group's K is long (plan::split_ok), and the

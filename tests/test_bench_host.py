@@ -53,7 +53,8 @@ def test_capacity_dropping_counts_kept_rows_only():
 
 
 def test_gemm_kernel_name_follows_the_launcher_rule():
-    assert bench.gemm_kernel_name(get_config("mixtral_8x7b")) == "gemm_bf16_big_kernel"
+    assert bench.gemm_kernel_name(get_config("mixtral_8x7b")) == "gemm_bf16_w4_kernel"
+    assert bench.gemm_kernel_name(get_config("heavy_skew")) == "gemm_bf16_w4_kernel"
     assert bench.gemm_kernel_name(get_config("decode@T16")) == "gemm_bf16_kernel"
     assert bench.gemm_kernel_name(get_config("tiny_fp32")) == "gemm_f32_kernel"
 

@@ -92,3 +92,38 @@ def test_ffn_segments(case):
         assert np.isfinite(gsh).all()
         err = np.linalg.norm(gsh - ref) / np.linalg.norm(ref)
         assert err <= TOL_BF16_REL_L2, err
+
+
+def test_ffn_with_an_operand_buffer_past_4_gib():
+    """The 4-wave big-tile kernel addresses its operand rows with 32-bit byte
+    offsets; a launch whose A buffer reaches 4 GiB takes the 8-wave kernel.
+    Here h (131072 rows x F = 16384, bf16) is exactly 4 GiB: the up projection
+    runs on the 4-wave kernel, the down projection on the 8-wave one. Rows at
+    both ends of the buffer (their h offsets straddle 2^32 bytes) are checked
+    one by one against the oracle's expert FFN, and every row must be written."""
+    H, F, E = 64, 16384, 2
+    counts = np.array([65536, 65536])
+    rows = int(counts.sum())
+    rng = np.random.default_rng([11, 4, 32])
+    xs = _bf16(rng, (rows, H), 1.0)
+    w1 = _bf16(rng, (E, F, H), H ** -0.5)
+    w2 = _bf16(rng, (E, H, F), F ** -0.5)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    assert rows * F * 2 >= 1 << 32
+    print(f"\n[gpu] ffn with a 4 GiB h buffer: E={E} rows={rows} H={H} F={F}", flush=True)
+    ys = torch.full((rows, H), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_expert_ffn(to_dev(xs), to_dev(offsets), to_dev(w1), to_dev(w2), ys=ys)
+    torch.cuda.synchronize()
+    got = bf16_bits_to_f32(to_host(ys)).astype(np.float64)
+    assert np.isfinite(got).all(), "rows left unwritten"
+    pick = np.unique(np.concatenate([np.arange(0, 300), np.arange(65400, 65700),
+                                     np.arange(rows - 300, rows),
+                                     rng.choice(rows, 200, replace=False)]))
+    for e in range(E):
+        sel = pick[(pick >= offsets[e]) & (pick < offsets[e + 1])]
+        ref = oracle.expert_ffn(xs[sel], w1[e], w2[e])
+        err = np.linalg.norm(got[sel] - ref) / np.linalg.norm(ref)
+        rows_err = np.linalg.norm(got[sel] - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        assert err <= TOL_BF16_REL_L2 and rows_err.max() <= TOL_BF16_REL_L2, (e, err, rows_err.max())
+    del ys
+    torch.cuda.empty_cache()
