@@ -67,7 +67,8 @@ struct GemmArgs {
   int slots;         // big kernel: workgroups of the launch (= reduce table start)
   const int32_t* gather;  // routed rows read through perm: A row p = token perm[p] / gk, or null
   int gk, gT;             // experts per token and tokens of that gather
-  int wide;               // an A operand buffer of 4 GiB or more (big tiles: 8-wave kernel)
+  int wide;               // an A operand buffer of 4 GiB or more: the 8-wave kernel
+                          // (which alone takes short segments as tile pairs)
 };
 
 // Row of the A operand that buffer row p of a group reads: p itself, or for
@@ -176,7 +177,7 @@ constexpr int kTableInt4 = plan::kEntryInts / 4;       // int4 per table entry
 __device__ __forceinline__ plan::Shape shape_of(const GemmArgs& a) {
   return plan::Shape{a.E,         a.rows,      a.shared_M,
                      a.routed.N,  a.routed.K,  a.shared.N,
-                     a.shared.K,  a.part != nullptr ? 1 : 0, a.slots};
+                     a.shared.K,  a.part != nullptr ? 1 : 0, a.slots, a.wide};
 }
 
 // The schedule of a big-tile launch, computed by every workgroup of the
@@ -748,9 +749,10 @@ __global__ __launch_bounds__(NW * 64, 1) void gemm_bf16_big_kernel(GemmArgs args
 //     the LDS address in M0, one s_mov and one global_load_lds each.
 //   - A segment's last, partial row tile skips the MFMAs of its empty 32-row
 //     sub-tiles (a wave-uniform test); its copies and barriers are unchanged.
-// Segments of at most 32 rows (table kind 1) run their two 32x128 tiles one
-// after the other on all four waves. Split-K slices and the epilogue are the
-// 8-wave kernel's.
+// Short segments take 256x256 tiles too (the plan has no tile pairs for this
+// kernel): copy-bound with their empty sub-tiles' MFMAs skipped, they cost
+// about a quarter of the time per column of a pair of 32x128 small tiles run
+// one after the other. Split-K slices and the epilogue are the 8-wave kernel's.
 template <bool GELU>
 __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs args) {
   constexpr int NW = 4, BM = 256, BN = 256, BK = 64;
@@ -767,19 +769,11 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs args) {
   static_assert(BM * BN * 2 <= LDS_BYTES, "the epilogue's C tile fits the stage buffers");
   __shared__ __attribute__((aligned(16))) uint8_t smem[LDS_BYTES];
 
+  // every slot holds one big tile or nothing: this kernel's plan has no
+  // short-segment pairs (Shape::pairs = 0)
   Tile t, tb;
-  const int kind = table_entry(args, blockIdx.x, t, tb);
-  if (kind < 0) return;
+  if (table_entry(args, blockIdx.x, t, tb) != 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (kind == 1) {
-    static_assert(SmallTileShape<kSBM, kSBN>::LDS <= LDS_BYTES, "small ring");
-    small_tile<kSBM, kSBN, 1, 4>(args, t, smem, wave, true);
-    if (tb.M > 0) {
-      __syncthreads();  // every wave is done with the ring before it is refilled
-      small_tile<kSBM, kSBN, 1, 4>(args, tb, smem, wave, true);
-    }
-    return;
-  }
   const Group G = pick_group(args, t.group);
   const int N = G.N, K = G.K;
   const uint16_t* A = static_cast<const uint16_t*>(G.A);
@@ -1207,7 +1201,8 @@ FfnLayout ffn_layout(const void* xs, const int32_t* gather, int gk, const int32_
     for (GemmArgs* a : {&up, &down}) {
       // split K only where every group's K is long (plan::split_ok), and the
       // launch's workgroups from the same shape the planner sees
-      plan::Shape sh{E, rows, a->shared_M, a->routed.N, a->routed.K, a->shared.N, a->shared.K, 0, 0};
+      plan::Shape sh{E, rows, a->shared_M, a->routed.N, a->routed.K, a->shared.N, a->shared.K, 0, 0,
+                     a->wide};
       sh.split = plan::split_ok(sh) ? 1 : 0;
       a->part = sh.split ? static_cast<float*>(at(Lo.part)) : nullptr;
       a->slots = plan::launch_slots<256, 256>(sh);

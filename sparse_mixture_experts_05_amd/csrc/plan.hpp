@@ -62,17 +62,21 @@ constexpr int kStageK = 64;          // K elements per stage of the GEMM main lo
 // on the Mixtral-shaped layer, 2 1-2% slower on the heavy-skew one.
 constexpr int kBlockCols = 4;
 
-// Small segments inside a big-tile launch. A routed segment of at most 32
-// rows would fill one of the 8 sub-tile rows of a 256x256 tile while the tile
-// streams the whole weight panel and copies 256 (clamped) A rows. Such
-// segments run as 32 x 128 tiles (kSBM x kSBN) instead, two per workgroup (one
-// per half of the 8 waves, each with its own LDS ring), and their slots are
-// spread evenly through each XCD's sequence among the big tiles. Measured on
-// the fine-grained and heavy-skew layers: 1-2% off the FFN; a 128-row limit
-// (up to 4 strips re-reading the same weights) was 3% slower than none. Not in
-// split-K launches, and not for the shared group (the two tiles of a
-// workgroup must have the same K: they meet the same barriers). If the
-// launch's slots cannot hold the pairs, every segment takes big tiles.
+// Small segments inside a big-tile launch of the 8-wave kernel. A routed
+// segment of at most 32 rows would fill one of the 8 sub-tile rows of a
+// 256x256 tile while the tile streams the whole weight panel and copies 256
+// (clamped) A rows. Such segments run as 32 x 128 tiles (kSBM x kSBN) instead,
+// two per workgroup (one per half of the 8 waves, each with its own LDS ring),
+// and their slots are spread evenly through each XCD's sequence among the big
+// tiles. Measured on the fine-grained and heavy-skew layers: 1-2% off the FFN;
+// a 128-row limit (up to 4 strips re-reading the same weights) was 3% slower
+// than none. Not in split-K launches, and not for the shared group (the two
+// tiles of a workgroup must have the same K: they meet the same barriers). If
+// the launch's slots cannot hold the pairs, every segment takes big tiles.
+// The 4-wave kernel takes no pairs (Shape::pairs = 0): with one wave per
+// SIMD it would run the two small tiles one after the other, and a 256x256
+// tile of a short segment (copy-bound, its MFMAs on empty sub-tiles skipped)
+// costs a quarter of the time per column.
 constexpr int kSmallRows = 33;
 constexpr int kSBM = 32, kSBN = 128;
 
@@ -93,6 +97,7 @@ struct Shape {
   int routed_N, routed_K, shared_N, shared_K;
   int split;       // 1: the launch may split its last round over K
   int slots;       // workgroups of the launch
+  int pairs;       // 1: short segments may run as pairs of small tiles
 };
 
 struct Tile {
@@ -157,7 +162,7 @@ MOE_HD inline void group_entry(const Shape& s, const int32_t* offsets, int grp, 
     cnt = s.shared_M;
   }
   all = cdiv(cnt, BM) * (grp < s.E ? cdiv(s.routed_N, BN) : cdiv(s.shared_N, BN));
-  const bool small = !s.split && grp < s.E && cnt > 0 && cnt < kSmallRows;
+  const bool small = s.pairs && !s.split && grp < s.E && cnt > 0 && cnt < kSmallRows;
   big = small ? 0 : all;
   sml = small ? cdiv(cnt, kSBM) * cdiv(s.routed_N, kSBN) : 0;
 }

@@ -8,9 +8,11 @@ namespace P = moe::plan;
 extern "C" {
 
 // Split flag and workgroup slots of a 256x256-tile launch, as the library's
-// launcher sizes them.
-int moe_plan_slots(int E, int rows, int shared_M, int Nr, int Kr, int Ns, int Ks, int* split) {
-  P::Shape s{E, rows, shared_M, Nr, Kr, Ns, Ks, 0, 0};
+// launcher sizes them (pairs: short segments may take tile pairs, the 8-wave
+// kernel's plan; 0 for the 4-wave kernel).
+int moe_plan_slots(int E, int rows, int shared_M, int Nr, int Kr, int Ns, int Ks, int pairs,
+                   int* split) {
+  P::Shape s{E, rows, shared_M, Nr, Kr, Ns, Ks, 0, 0, pairs};
   s.split = P::split_ok(s) ? 1 : 0;
   *split = s.split;
   return P::launch_slots<256, 256>(s);
@@ -18,8 +20,8 @@ int moe_plan_slots(int E, int rows, int shared_M, int Nr, int Kr, int Ns, int Ks
 
 // The launch's whole tile table: (slots + reduce slots) entries of 16 ints.
 void moe_plan_table(const int32_t* offsets, int E, int rows, int shared_M, int Nr, int Kr, int Ns,
-                    int Ks, int split, int slots, int* table) {
-  const P::Shape s{E, rows, shared_M, Nr, Kr, Ns, Ks, split, slots};
+                    int Ks, int split, int slots, int pairs, int* table) {
+  const P::Shape s{E, rows, shared_M, Nr, Kr, Ns, Ks, split, slots, pairs};
   P::plan_table_serial<256, 256, P::kBlockCols>(s, offsets, table);
 }
 

@@ -34,42 +34,42 @@ def planner(tmp_path_factory):
     L = ctypes.CDLL(out)
     i, p = ctypes.c_int, ctypes.c_void_p
     L.moe_plan_slots.restype = i
-    L.moe_plan_slots.argtypes = [i] * 7 + [ctypes.POINTER(i)]
+    L.moe_plan_slots.argtypes = [i] * 8 + [ctypes.POINTER(i)]
     L.moe_plan_table.restype = None
-    L.moe_plan_table.argtypes = [p] + [i] * 9 + [p]
+    L.moe_plan_table.argtypes = [p] + [i] * 10 + [p]
     return L
 
 
-def plan(L, counts, Nr, Kr, shared_M, Ns, Ks):
+def plan(L, counts, Nr, Kr, shared_M, Ns, Ks, pairs=1):
     """(table [slots + reduce, 16], slots, split) of one launch."""
     E = len(counts)
     rows = int(sum(counts))
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     split = ctypes.c_int(0)
-    slots = L.moe_plan_slots(E, rows, shared_M, Nr, Kr, Ns, Ks, ctypes.byref(split))
+    slots = L.moe_plan_slots(E, rows, shared_M, Nr, Kr, Ns, Ks, pairs, ctypes.byref(split))
     n = slots + L.moe_plan_reduce_slots()
     table = np.full((n, L.moe_plan_entry_ints()), -7, dtype=np.int32)
     L.moe_plan_table(offsets.ctypes.data, E, rows, shared_M, Nr, Kr, Ns, Ks, split.value, slots,
-                     table.ctypes.data)
+                     pairs, table.ctypes.data)
     return table, slots, split.value
 
 
-def check(L, counts, Nr, Kr, shared_M, Ns, Ks):
+def check(L, counts, Nr, Kr, shared_M, Ns, Ks, pairs=1):
     E = len(counts)
     goff = list(np.concatenate([[0], np.cumsum(counts)])[:E]) + [0]
     gcnt = list(counts) + [shared_M]
-    table, slots, split = plan(L, counts, Nr, Kr, shared_M, Ns, Ks)
+    table, slots, split = plan(L, counts, Nr, Kr, shared_M, Ns, Ks, pairs)
     cover = {}  # (group, row, col) blocks -> list of (k slice, slices)
     red = set()
-    pairs = 0
+    npairs = 0
     for g in range(slots):
         e = table[g]
         kind = e[0]
         if kind < 0:
             continue
         if kind == 1:
-            pairs += 1
-            assert not split  # no pairs in split-K launches
+            npairs += 1
+            assert not split and pairs  # no pairs in split-K launches or when not allowed
             for (grp, ex, row0, M, n0) in [(e[1], e[2], e[3], e[4], e[5]),
                                            (e[9], e[10], e[11], e[12], e[13])]:
                 if M == 0:
@@ -112,7 +112,7 @@ def check(L, counts, Nr, Kr, shared_M, Ns, Ks):
     for key, v in cover.items():
         sp = v[0][1]
         assert sorted(x[0] for x in v) == list(range(sp)), (key, v)
-    return pairs, split and any(table[g][6] > 1 for g in range(slots) if table[g][0] == 0)
+    return npairs, split and any(table[g][6] > 1 for g in range(slots) if table[g][0] == 0)
 
 
 def test_schedule_covers_every_block_once(planner):
@@ -128,9 +128,11 @@ def test_schedule_covers_every_block_once(planner):
         Fs = int(rng.choice([0, F]))
         T = rows // max(1, int(rng.choice([1, 2, 8])))
         for (Nr, Kr, Ns, Ks) in [(F, H, Fs, H), (H, F, H, Fs)]:
-            pairs, split = check(planner, counts, Nr, Kr, T if Fs else 0, Ns, Ks)
-            stats["pairs"] += pairs > 0
-            stats["split"] += bool(split)
+            for allow in (1, 0):  # the 8-wave kernel's plan, then the 4-wave kernel's
+                pairs, split = check(planner, counts, Nr, Kr, T if Fs else 0, Ns, Ks, allow)
+                stats["pairs"] += pairs > 0
+                stats["split"] += bool(split)
+                assert allow or pairs == 0
     # both launch kinds were exercised
     assert stats["pairs"] > 20 and stats["split"] > 20, stats
 
@@ -146,6 +148,7 @@ def test_schedule_of_the_workload_shapes(planner):
     assert not check(planner, mix, 14336, 4096, 0, 14336, 4096)[1]
     fg = rng.multinomial(32768, rng.dirichlet(np.full(128, 0.05)))
     assert check(planner, fg, 1536, 4096, 4096, 1536, 4096)[0] > 0  # pairs
+    assert check(planner, fg, 1536, 4096, 4096, 1536, 4096, pairs=0)[0] == 0
     check(planner, fg, 4096, 1536, 4096, 4096, 1536)
     hs = rng.multinomial(131072, rng.dirichlet(np.full(256, 0.05)))
     check(planner, hs, 1024, 4096, 0, 1024, 4096)
