@@ -44,9 +44,12 @@ constexpr int tile_stride() { return kMaxE + kThreads / BT; }
 // or an equal score with a lower id. A NaN score reads as -inf and -0 as +0
 // (they compare equal). Key 0 is below every real entry and marks an empty
 // slot, so the k chosen ids are always real, distinct and < E.
+// Written with arithmetic only (max with -inf drops a NaN, adding +0 turns
+// -0 into +0, the sign mask flips the order of negatives): as selects the
+// compiler turned the mapping into three nested branches per key.
 __device__ __forceinline__ uint64_t topk_key(float s, int e) {
-  const uint32_t u = s == s ? (s == 0.0f ? 0u : __float_as_uint(s)) : __float_as_uint(-INFINITY);
-  const uint32_t o = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t u = __float_as_uint(fmaxf(s, -INFINITY) + 0.0f);
+  const uint32_t o = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
   return ((uint64_t)o << 32) | (uint32_t)(~(uint32_t)e);
 }
 __device__ __forceinline__ float key_score(uint64_t key) {
@@ -119,36 +122,48 @@ __device__ __forceinline__ float group_sum(float v) {
 
 // Top-k of the BT tokens whose scores (bias included) are in the LDS tile sc
 // (row stride tile_stride<BT>()). Token t of the tile uses lanes
-// [t*G, t*G + G); lane g scans the experts g, g + G, ... in blocks of KP,
-// sorts each block and merges it into its running list, then the G lists are
-// merged. KP >= k is a power of two.
+// [t*G, t*G + G); lane g reads the experts g, g + G, ... (at most EPX experts
+// in all, a compile-time bound, so the scan is unrolled and branch free: all
+// reads are issued first, from clamped columns, and columns >= E become
+// empty keys), sorts blocks of KP keys and merges each into its running list,
+// then the G lists are merged. KP >= k is a power of two.
 // When pp is not null, the full softmax p[t, e] = exp(s_e - m) / sum_e' exp(s_e' - m)
 // of every token overwrites its scores, and pp[e] receives the sum of p[t, e]
 // over the tile's tokens (t ascending).
-template <int BT, int KP>
+template <int BT, int KP, int EPX>
 __device__ __forceinline__ void topk_tokens(float* sc, int t0, int T, int E, int k,
                                             int32_t* __restrict__ topk_idx,
                                             float* __restrict__ topk_w, float* __restrict__ pp) {
   constexpr int G = kThreads / BT;
   constexpr int S = tile_stride<BT>();
   static_assert(G >= 1 && G <= 64 && BT * G == kThreads, "one group of lanes per token");
+  constexpr int NSUB = (EPX + G - 1) / G;  // experts per lane, at most
+  constexpr int NBLK = (NSUB + KP - 1) / KP;
   const int t = threadIdx.x / G, g = threadIdx.x % G;
   const int tok = t0 + t;
   float* row = sc + t * S;
-  const int nsub = (E + G - 1) / G;  // experts per lane
+  const int nsub = (E + G - 1) / G;
 
+  float v[NBLK * KP];
+#pragma unroll
+  for (int i = 0; i < NBLK * KP; ++i) v[i] = row[min(g + G * i, E - 1)];
   uint64_t list[KP];
 #pragma unroll
-  for (int i = 0; i < KP; ++i) list[i] = 0;
-  for (int i0 = 0; i0 < nsub; i0 += KP) {
+  for (int b = 0; b < NBLK; ++b) {
     uint64_t blk[KP];
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
-      const int e = g + G * (i0 + i);
-      blk[i] = (i0 + i < nsub && e < E) ? topk_key(row[e], e) : 0;
+      const int e = g + G * (b * KP + i);
+      // columns past E: an empty key (mask, not a select: see topk_key)
+      blk[i] = topk_key(v[b * KP + i], e) & (uint64_t)(-(int64_t)(e < E));
     }
     bitonic_sort<KP>(blk);
-    merge_top<KP>(list, blk);
+    if (b == 0) {
+#pragma unroll
+      for (int i = 0; i < KP; ++i) list[i] = blk[i];
+    } else {
+      merge_top<KP>(list, blk);
+    }
   }
   group_merge<0, G, KP>(list);
 
@@ -198,14 +213,14 @@ __device__ __forceinline__ void topk_tokens(float* sc, int t0, int T, int E, int
   }
 }
 
-template <int BT>
+template <int BT, int EPX>
 __device__ __forceinline__ void topk_phase(float* sc, int t0, int T, int E, int k,
                                            int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_w, float* __restrict__ pp) {
-  if (k <= 1) topk_tokens<BT, 1>(sc, t0, T, E, k, topk_idx, topk_w, pp);
-  else if (k <= 2) topk_tokens<BT, 2>(sc, t0, T, E, k, topk_idx, topk_w, pp);
-  else if (k <= 4) topk_tokens<BT, 4>(sc, t0, T, E, k, topk_idx, topk_w, pp);
-  else topk_tokens<BT, 8>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  if (k <= 1) topk_tokens<BT, 1, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else if (k <= 2) topk_tokens<BT, 2, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else if (k <= 4) topk_tokens<BT, 4, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else topk_tokens<BT, 8, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
 }
 
 // P[e] = (sum over workgroups b, ascending, of part[b][e]) / T, in double.
@@ -401,8 +416,8 @@ __global__ __launch_bounds__(kThreads) void route_bf16_kernel(
   f32x4_t acc[C::MC][C::NC];
   score_tile<BT, EP>(smem, x, wg, t0, T, 0, E, H, 0, H / 64, acc);
   scores_to_lds<BT, EP>(smem, E, bias, acc);
-  topk_phase<BT>(reinterpret_cast<float*>(smem), t0, T, E, k, topk_idx, topk_w,
-                 ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+  topk_phase<BT, EP>(reinterpret_cast<float*>(smem), t0, T, E, k, topk_idx, topk_w,
+                     ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 // fp32 scores with plain dot products (small fp32 layers).
@@ -429,8 +444,8 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
     sc[t * S + e] = bias != nullptr ? s + bias[e] : s;
   }
   __syncthreads();
-  topk_phase<BT>(sc, t0, T, E, k, topk_idx, topk_w,
-                 ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+  topk_phase<BT, kMaxE>(sc, t0, T, E, k, topk_idx, topk_w,
+                        ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 
@@ -475,7 +490,7 @@ __global__ __launch_bounds__(kThreads) void route_partial_kernel(const uint16_t*
 // BT tokens per workgroup: 256 / BT lanes per token in the top-k. Few lanes
 // per token sort whole blocks of experts and merge over fewer levels; many
 // lanes per token keep small batches spread over more workgroups.
-template <int NKS, int BT>
+template <int NKS, int BT, int EPX>
 __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __restrict__ ws,
                                                                 const float* __restrict__ bias,
                                                                 int T, int E, int k,
@@ -513,24 +528,33 @@ __global__ __launch_bounds__(kThreads) void route_select_kernel(const float* __r
     }
   }
   __syncthreads();
-  topk_phase<BT>(sc, t0, T, E, k, topk_idx, topk_w,
-                 ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+  topk_phase<BT, EPX>(sc, t0, T, E, k, topk_idx, topk_w,
+                      ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
-// The select for exactly nks K slices (a power of two up to kMaxSlices).
-template <int BT>
-hipError_t launch_select(int nks, const float* ws, const float* bias, int T, int E, int k,
-                         int32_t* idx, float* w, float* pp, hipStream_t s) {
+// The select for exactly nks K slices (a power of two up to kMaxSlices) and
+// at most EPX experts.
+template <int BT, int EPX>
+hipError_t launch_select_e(int nks, const float* ws, const float* bias, int T, int E, int k,
+                           int32_t* idx, float* w, float* pp, hipStream_t s) {
   const dim3 grid((T + BT - 1) / BT), block(kThreads);
   switch (nks) {
-    case 1: hipLaunchKernelGGL((route_select_kernel<1, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
-    case 2: hipLaunchKernelGGL((route_select_kernel<2, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
-    case 4: hipLaunchKernelGGL((route_select_kernel<4, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
-    case 8: hipLaunchKernelGGL((route_select_kernel<8, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
-    case 16: hipLaunchKernelGGL((route_select_kernel<16, BT>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 1: hipLaunchKernelGGL((route_select_kernel<1, BT, EPX>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 2: hipLaunchKernelGGL((route_select_kernel<2, BT, EPX>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 4: hipLaunchKernelGGL((route_select_kernel<4, BT, EPX>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 8: hipLaunchKernelGGL((route_select_kernel<8, BT, EPX>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
+    case 16: hipLaunchKernelGGL((route_select_kernel<16, BT, EPX>), grid, block, 0, s, ws, bias, T, E, k, idx, w, pp); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+template <int BT>
+hipError_t launch_select(int nks, const float* ws, const float* bias, int T, int E, int k,
+                         int32_t* idx, float* w, float* pp, hipStream_t s) {
+  if (E <= 64) return launch_select_e<BT, 64>(nks, ws, bias, T, E, k, idx, w, pp, s);
+  if (E <= 128) return launch_select_e<BT, 128>(nks, ws, bias, T, E, k, idx, w, pp, s);
+  return launch_select_e<BT, kMaxE>(nks, ws, bias, T, E, k, idx, w, pp, s);
 }
 
 // Path of a route call. Both two-launch paths write and re-read T x E partial

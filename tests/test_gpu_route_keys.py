@@ -1,0 +1,87 @@
+"""GPU: the route's ordering rule on exactly representable scores.
+
+The parity tests keep every routing decision away from ties (inputs are
+conditioned so that the scores of a token differ by at least 1e-3). This test
+does the opposite. Each token row of x is one signed one-hot vector and the
+gate rows hold small integers, so every score is an integer computed exactly
+in fp32, and ties between experts are the rule. The bias adds exactly
+representable steps, a NaN and a -inf; the route must
+
+  * order the k chosen experts by descending score, ties to the lower id
+    (the router listing of the "Kimi K3 fine-grained MoE" article returns
+    torch.topk's order; ties are resolved as the library documents),
+  * read a NaN score as -inf (never chosen while k other scores exist),
+  * weight them exp(s_j - max) / sum over the k chosen.
+
+The expected ids come from a host sort of the same fp32 values; every route
+path (two launches with small or big tiles, one launch with 16, 32 or 64
+tokens per workgroup, the expert counts of every tile width) is taken.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_mixture_experts_05_amd as moe
+
+pytestmark = pytest.mark.gpu
+
+
+def _bf16(a):
+    return torch.tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16)
+
+
+def _expected(scores, k):
+    """(ids, weights) by the documented rule: NaN as -inf, descending score,
+    ties to the lower id."""
+    s = np.where(np.isnan(scores), -np.inf, scores).astype(np.float64)
+    T, E = s.shape
+    # lexsort: the last key is the primary one (score, descending), then the id
+    order = np.lexsort((np.broadcast_to(np.arange(E), (T, E)), -s), axis=1)[:, :k]
+    sel = np.take_along_axis(s, order, axis=1)
+    ex = np.exp(sel - sel[:, :1])
+    return order.astype(np.int32), (ex / ex.sum(axis=1, keepdims=True)).astype(np.float32)
+
+
+CASES = [  # (T, H, E, k): route paths of the library
+    (64, 128, 16, 4),      # two launches, small tiles
+    (2048, 128, 16, 4),    # one launch, 16 tokens per workgroup, experts split over k steps
+    (4096, 128, 128, 8),   # two launches, 64 x 128 tiles
+    (4096, 192, 256, 8),   # two launches, 128 x 256 tiles
+    (8192, 128, 40, 3),    # one launch, 32 tokens per workgroup
+    (16384, 128, 256, 8),  # one launch, 64 tokens per workgroup
+    (3, 64, 256, 8),       # a few tokens, E = 256
+]
+
+
+@pytest.mark.parametrize("T,H,E,k", CASES, ids=[f"T{c[0]}_H{c[1]}_E{c[2]}_k{c[3]}" for c in CASES])
+def test_route_order_ties_and_nan(T, H, E, k):
+    print(f"\n[gpu] route keys T={T} H={H} E={E} k={k}", flush=True)
+    rng = np.random.default_rng(T * 1000 + E)
+    cols = rng.integers(0, H, size=T)
+    sign = np.where(rng.random(T) < 0.5, -1.0, 1.0)
+    x = np.zeros((T, H), dtype=np.float32)
+    x[np.arange(T), cols] = sign
+    wg = rng.integers(-3, 4, size=(E, H)).astype(np.float32)  # few values: many ties
+    wg[0] = 0.0  # a zero score for every token
+    bias = (rng.integers(-2, 3, size=E) * 0.5).astype(np.float32)
+    if E > 8:
+        bias[5] = np.nan
+        bias[6] = -np.inf
+    # exact in fp32: one nonzero product per score, integers and halves
+    scores = ((x @ wg.T) + bias[None, :]).astype(np.float32)
+    ids, w = _expected(scores, k)
+
+    xd = _bf16(x).cuda()
+    wgd = _bf16(wg).cuda()
+    bd = torch.tensor(bias).cuda()
+    got_i, got_w = moe.moe_route(xd, wgd, bd, k)
+    torch.cuda.synchronize()
+    got_i, got_w = got_i.cpu().numpy(), got_w.cpu().numpy()
+    bad = np.nonzero((got_i != ids).any(axis=1))[0]
+    assert bad.size == 0, (f"{bad.size} tokens differ; first {bad[0]}: got {got_i[bad[0]]}, "
+                           f"want {ids[bad[0]]}, scores {scores[bad[0]]}")
+    np.testing.assert_allclose(got_w, w, rtol=0, atol=1e-6)
+    # NaN and -inf experts are never chosen while k finite scores exist
+    if E > 8:
+        assert not np.isin(got_i, [5, 6]).any()
+    print(f"[gpu] route keys T={T} E={E}: ok", flush=True)
