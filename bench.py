@@ -7,10 +7,12 @@ A step is one pass of the whole layer over one batch: route, dispatch, grouped
 expert FFN, combine and load stats (left on the device), all on one stream
 with inputs already resident in HBM. W untimed warm-up steps, then exactly K
 timed steps between two device synchronisations; HIP events on the launch
-stream time every call of every step. Caches are cold: a 1 GiB fill kernel
-(more than the 256 MB last-level cache and all L2s) runs before every timed
-step, outside the events, and the step time is the event span of the five
-calls. The same K steps are then timed warm, as a labelled secondary.
+stream time every call of every step. Caches are cold: a kernel reading a
+1 GiB buffer (more than the 256 MB last-level cache and all L2s) runs before
+every timed step, outside the events, and the step time is the event span of
+the five calls (--flush-write: a 1 GiB fill kernel instead, which leaves the
+last-level cache full of dirty lines). The same K steps are then timed warm,
+as a labelled secondary.
 
 Headline workload: the Mixtral-8x7B-shaped layer (T=4096, H=4096, E=8, top-2,
 d_ff=14336, bf16 with fp32 accumulation), random weights and inputs from the
@@ -27,7 +29,8 @@ layers and the decode sweep (T = 1..128, graph replay). Prints one JSON line:
                (measured_copy_GB/s)
   warm         the headline layer with warm caches
   workloads    cold and warm summaries of the other 4096+-token layers
-  decode       per-T graph-replayed latency and the FFN's weight-read rate
+  decode       per-T graph-replayed latency (cold and warm) and the FFN's
+               weight-read rate
   cpu_baseline the float64 CPU oracle on a bounded sample of the headline layer
 """
 from __future__ import annotations
@@ -267,17 +270,43 @@ class Layer:
                                       drop=drop)
 
 
-def timed_steps(layer, torch, steps, flush_buf):
+class Flush:
+    """Evicts the layer's data from the L2s and the 256 MB last-level cache
+    before a step, outside the events: one kernel over a 1 GiB buffer.
+
+    "read" (the default) reads the buffer (a max over it), so the caches end
+    up holding clean lines of it. "write" fills it instead; the last-level
+    cache then holds 256 MB of dirty lines, and their write-backs compete with
+    the timed step's first reads (a heavier condition than a preceding layer
+    leaves: its writes are its activations, tens of MB)."""
+
+    def __init__(self, torch, mode="read"):
+        self.torch = torch
+        self.mode = mode
+        self.buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+
+    def __call__(self, s):
+        if self.mode == "write":
+            self.buf.fill_(s & 0xFF)   # a fill kernel, not a memset
+        else:
+            self.sink = self.torch.amax(self.buf.view(self.torch.int64))
+
+    def describe(self):
+        return ("a 1 GiB fill kernel before every step (dirty last-level cache)" if self.mode == "write"
+                else "a kernel reading 1 GiB before every step")
+
+
+def timed_steps(layer, torch, steps, flush):
     """K timed eager steps with HIP events around every call (on the launch
-    stream). With flush_buf, a fill kernel over it (larger than the last-level
-    cache and all L2s) runs before every step, outside the events. Returns the
-    per-call samples (ms), the per-step event spans (ms) and the wall time (s)."""
+    stream). With flush, its kernel runs before every step, outside the
+    events. Returns the per-call samples (ms), the per-step event spans (ms)
+    and the wall time (s)."""
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        if flush_buf is not None:
-            flush_buf.fill_(s & 0xFF)   # a fill kernel, not a memset
+        if flush is not None:
+            flush(s)
         layer.step(events[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
@@ -315,7 +344,7 @@ def kernel_table(cfg, samples, work, copy_gather=False):
     return k, achieved, peak
 
 
-def run_workload(name, args, moe, torch, flush_buf, headline=False):
+def run_workload(name, args, moe, torch, flush, headline=False):
     """Cold-cache (and warm) timing of one workload; returns a result dict."""
     from synth import get_config, make_layer
     cfg = get_config(name)
@@ -328,7 +357,7 @@ def run_workload(name, args, moe, torch, flush_buf, headline=False):
         layer.step()
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: timing {args.steps} steps, cold caches", file=sys.stderr, flush=True)
-    cold, cold_spans, cold_elapsed = timed_steps(layer, torch, args.steps, flush_buf)
+    cold, cold_spans, cold_elapsed = timed_steps(layer, torch, args.steps, flush)
     print(f"[bench] {cfg.name}: timing {args.steps} steps, warm caches", file=sys.stderr, flush=True)
     warm, warm_spans, warm_elapsed = timed_steps(layer, torch, args.steps, None)
     counts = layer.dsp["counts"].cpu().numpy()
@@ -355,10 +384,12 @@ def summary(res, which="cold"):
             "kernels_median_ms": {n: k[n]["median_ms"] for n in NAMES}}
 
 
-def decode_sweep(args, moe, torch, flush_buf):
+def decode_sweep(args, moe, torch, flush):
     """The decode-shaped sweep: per T, graph-replayed layer latency from cold
-    caches (a flush before every replay, events around the replay) and, from
-    cold eager steps, the FFN's weight-read rate against HBM."""
+    caches (a flush before every replay, events around the replay) and warm
+    (replays back to back, the weights of the chosen experts left in the
+    caches by the previous replay) and, from cold eager steps, the FFN's
+    weight-read rate against HBM."""
     from synth import DECODE_TOKENS, get_config, make_layer
     full = get_config("decode")
     print(f"[bench] decode sweep: generating inputs", file=sys.stderr, flush=True)
@@ -372,7 +403,7 @@ def decode_sweep(args, moe, torch, flush_buf):
         for _ in range(args.warmup):
             layer.step()
         steps = max(args.steps, 30)
-        cold, _, _ = timed_steps(layer, torch, steps, flush_buf)
+        cold, _, _ = timed_steps(layer, torch, steps, flush)
         counts = layer.dsp["counts"].cpu().numpy()
         work = algorithmic_work(cfg, counts)
         k, _, _ = kernel_table(cfg, cold, work)
@@ -383,20 +414,32 @@ def decode_sweep(args, moe, torch, flush_buf):
         ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
         torch.cuda.synchronize()
         for s in range(steps):
-            flush_buf.fill_(s & 0xFF)
+            flush(s)
             ev[s][0].record()
             g.graph.replay()
             ev[s][1].record()
         torch.cuda.synchronize()
         lat = np.array([a.elapsed_time(b) for a, b in ev])
         p10, p50, p90 = np.percentile(lat, [10, 50, 90])
+        # warm: the same replays without the flush; the host runs ahead, so
+        # each replay is queued before the previous one ends
+        ev_w = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        for s in range(steps):
+            ev_w[s][0].record()
+            g.graph.replay()
+            ev_w[s][1].record()
+        torch.cuda.synchronize()
+        warm_p50 = float(np.median([a.elapsed_time(b) for a, b in ev_w]))
         out[f"T{T}"] = {"graph_latency_ms_median": float(p50), "p10_ms": float(p10),
                         "p90_ms": float(p90), "tokens/s": T / (p50 * 1e-3),
+                        "graph_latency_warm_ms_median": warm_p50,
                         "eager_kernels_median_ms": {n: k[n]["median_ms"] for n in NAMES},
                         "ffn_weight_GB/s": work["ffn_weight_bytes"] / k["expert_ffn"]["median_ms"] / 1e6,
                         "ffn_weight_hbm_frac": work["ffn_weight_bytes"] / k["expert_ffn"]["median_ms"]
                         / 1e6 / HBM_PEAK_GBS}
-        print(f"[bench] decode T={T}: graph latency {p50 * 1e3:.1f} us", file=sys.stderr, flush=True)
+        print(f"[bench] decode T={T}: graph latency {p50 * 1e3:.1f} us cold, {warm_p50 * 1e3:.1f} us warm",
+              file=sys.stderr, flush=True)
         del g, layer
         torch.cuda.empty_cache()
     return out
@@ -419,8 +462,11 @@ def main():
                     help="enforce the expert capacity int(T*k/E*cf) on the headline workload: "
                          "dispatch drops the assignments past it (a variant, not the headline layer)")
     ap.add_argument("--warm", action="store_true",
-                    help="headline value from warm caches (default: cold, a 1 GiB fill kernel "
+                    help="headline value from warm caches (default: cold, a 1 GiB read kernel "
                          "before every step, outside the per-call events)")
+    ap.add_argument("--flush-write", action="store_true",
+                    help="cold caches by a 1 GiB fill kernel (leaves the last-level cache dirty) "
+                         "instead of a 1 GiB read")
     ap.add_argument("--copy-gather", action="store_true",
                     help="dispatch copies the rows into xs and the FFN reads xs (the default "
                          "FFN reads x through perm: moe_expert_ffn_gather)")
@@ -443,9 +489,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     moe.lib()  # fail loudly if the HIP library is missing
-    flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+    flush = Flush(torch, "write" if args.flush_write else "read")
 
-    head = run_workload(args.workload, args, moe, torch, flush_buf, headline=True)
+    head = run_workload(args.workload, args, moe, torch, flush, headline=True)
     cfg, work, layer = head["cfg"], head["work"], head["layer"]
     T = cfg.T
     kernels, achieved, peak = head["warm" if args.warm else "cold"]
@@ -464,7 +510,7 @@ def main():
         torch.cuda.synchronize()
         for s in range(args.steps):
             if not args.warm:
-                flush_buf.fill_(s & 0xFF)
+                flush(s)
             ev[s][0].record()
             g.graph.replay()
             ev[s][1].record()
@@ -494,7 +540,7 @@ def main():
                              "fused into the FFN (x read through perm)",
                    "launch": "hip graph replay" if args.graph else "eager",
                    "caches": "warm" if args.warm else
-                             "cold: a 1 GiB fill kernel before every step, outside the events"},
+                             f"cold: {flush.describe()}, outside the events"},
         "roofline": {"bound": "mfma" if bf16 else "alu", "kernel": gemm_kernel_name(cfg),
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
                      "frac": achieved / peak, "traffic": read_traffic()},
@@ -509,12 +555,12 @@ def main():
         for name in ["fine_grained_zipf", "heavy_skew"]:
             if name == args.workload:
                 continue
-            r = run_workload(name, args, moe, torch, flush_buf)
+            r = run_workload(name, args, moe, torch, flush)
             subs[name] = {"cold": summary(r, "cold"), "warm": summary(r, "warm")}
             del r
             torch.cuda.empty_cache()
         result["workloads"] = subs
-        result["decode"] = decode_sweep(args, moe, torch, flush_buf)
+        result["decode"] = decode_sweep(args, moe, torch, flush)
     # Context for the datasheet fractions of the HBM-bound steps: a plain
     # 512 MiB device copy (1 GiB of reads and writes, beyond the last-level
     # cache) timed with events on the same stream; copy_frac = a step's GB/s
