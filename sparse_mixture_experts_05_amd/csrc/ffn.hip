@@ -423,7 +423,7 @@ __device__ __forceinline__ void small_tile(const GemmArgs& args, const Tile& t, 
             continue;
           }
           float y = acc[i][j][v];
-          if (gelu) y = gelu_erf(y);
+          if (gelu) y = gelu_bf16(y);
           C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
         }
       }
@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kThreads) void gemm_small_reduce_kernel(GemmArgs ar
 #pragma unroll
     for (int s = 0; s < kMaxSmallSplit; ++s)
       if (s < nks) y += v[s];
-    if (gelu) y = gelu_erf(y);
+    if (gelu) y = gelu_bf16(y);
     C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
   }
 }
@@ -535,8 +535,8 @@ __device__ __forceinline__ void big_tile_epilogue(const GemmArgs& args, const Ti
       for (int v = 0; v < 16; v += 2) {
         float y0 = acc[i][j][v], y1 = acc[i][j][v + 1];
         if constexpr (GELU) {
-          y0 = gelu_erf_fast(y0);
-          y1 = gelu_erf_fast(y1);
+          y0 = gelu_bf16(y0);
+          y1 = gelu_bf16(y1);
         }
         const uint32_t own = cvt_bf16x2(y0, y1);  // (row R(v), row R(v) + 1) of this column
         const uint32_t partner = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xF, 0xF, false);
@@ -969,8 +969,8 @@ __global__ __launch_bounds__(kThreads) void gemm_tail_reduce_kernel(GemmArgs arg
         y1 += v[ks].y;
       }
     if (gelu) {
-      y0 = gelu_erf_fast(y0);
-      y1 = gelu_erf_fast(y1);
+      y0 = gelu_bf16(y0);
+      y1 = gelu_bf16(y1);
     }
     *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) = pack_bf16x2(y0, y1);
   }
