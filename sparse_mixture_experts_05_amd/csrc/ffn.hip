@@ -859,11 +859,13 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs args) {
     else if (r <= 4) fb_[r - 1] = ld16(sb + fb[r - 1] + off);
     else fa_[r - 4] = ld16(sa + fa[r - 4] + off);
   };
-  auto main_loop = [&](auto partial_tag) {
-    constexpr bool PARTIAL = decltype(partial_tag)::value;
-    auto mfma_m = [&](int m, const u32x4_t (&fa_)[SM], const u32x4_t (&fb_)[SN]) {
-      const int i = m >> 2, j = m & 3;
-      if (!PARTIAL || i < nsub)
+  // NS: the row sub-tiles of this wave that hold data (a compile-time count,
+  // so a partial tile's loop has no branch between its MFMAs)
+  auto main_loop = [&](auto ns_tag) {
+    constexpr int NS = decltype(ns_tag)::value;
+    auto mfma_m = [&](auto mc, const u32x4_t (&fa_)[SM], const u32x4_t (&fb_)[SN]) {
+      constexpr int m = decltype(mc)::value, i = m >> 2, j = m & 3;
+      if constexpr (i < NS)
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(fa_[i]), as_bf16x8(fb_[j]),
                                                             acc[i][j], 0, 0, 0);
     };
@@ -877,7 +879,7 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs args) {
       constexpr int q0 = decltype(q0c)::value, nq = decltype(q1c)::value - q0;
       static_for<16>([&](auto mc) {
         constexpr int m = decltype(mc)::value;
-        mfma_m(m, fa_, fb_);
+        mfma_m(mc, fa_, fb_);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (m < 8) {
           read_r(rsa, rsb, rks, m, ra_, rb_);
@@ -926,11 +928,28 @@ __global__ __launch_bounds__(256, 1) void gemm_bf16_w4_kernel(GemmArgs args) {
       bs = bs1;
     }
     wait_vmcnt<0>();
+    // every accumulator leaves each variant in its accumulation registers
+    // (the untouched ones too), so the variants meet the epilogue with one
+    // register assignment
+#pragma unroll
+    for (int i = 0; i < SM; ++i)
+#pragma unroll
+      for (int j = 0; j < SN; ++j) asm volatile("" : "+a"(acc[i][j]));
   };
-  if (M == BM)
-    main_loop(std::integral_constant<bool, false>{});
-  else
-    main_loop(std::integral_constant<bool, true>{});
+  // A segment's last, partial row tile skips the MFMAs of its empty 32-row
+  // sub-tiles. The count is wave-uniform and picks a loop built for it. One
+  // loop with a branch around each MFMA had made these tiles 15-20 % slower
+  // than full ones despite the skipped work; computing every sub-tile costs
+  // power the full tiles then lack (the Mixtral-shaped FFN gains 2.5 %, the
+  // fine-grained one loses 6 %), and choosing the count per stage inside one
+  // loop spills (per-tile s_memrealtime stamps, FFN timings).
+  switch (nsub) {
+    case 4: main_loop(std::integral_constant<int, 4>{}); break;
+    case 3: main_loop(std::integral_constant<int, 3>{}); break;
+    case 2: main_loop(std::integral_constant<int, 2>{}); break;
+    case 1: main_loop(std::integral_constant<int, 1>{}); break;
+    default: main_loop(std::integral_constant<int, 0>{}); break;
+  }
   big_tile_epilogue<BM, BN, NW, GELU>(args, t, C, N, M, nvalid, acc, smem);
 }
 
