@@ -543,9 +543,13 @@ __device__ __forceinline__ void big_tile_epilogue(const GemmArgs& args, const Ti
         const uint32_t pair = __builtin_amdgcn_perm(partner, own, sel);
         const int roff = (i * 32 + (v >> 2) * 8 + (v & 3)) * CROWB;
         *reinterpret_cast<uint32_t*>(smem + cbase[j] + roff) = pair;
-        // one accumulator pair at a time: keeps the scheduler from reading
-        // every accumulator out to VGPRs ahead of its conversion
-        if constexpr (NW == 4) __builtin_amdgcn_sched_barrier(0);
+        // two accumulator pairs at a time: keeps the scheduler from reading
+        // every accumulator out to VGPRs ahead of its conversion, while four
+        // independent GeLU chains fill the VALU pipeline (one pair at a time:
+        // the FFN 0.8-3 % slower, four: no better than two)
+        if constexpr (NW == 4) {
+          if ((v & 3) == 2) __builtin_amdgcn_sched_barrier(0);
+        }
       }
   lds_barrier();
   const int cl = lane & 31;
