@@ -47,15 +47,19 @@ __device__ __forceinline__ float gelu_erf(float a) {
 
 // GeLU (erf form) for bf16 outputs: 0.5 * a * (1 + erf(a / sqrt(2))) is
 // a * Phi(a), Phi the standard normal distribution function. With u = |a| and
-// q = Phi(-u), Phi(a) = 1 - q for a >= 0 and q for a < 0. q = 2^p(u), p a
-// degree-6 polynomial fitted to log2 Phi(-u) on [0, 6] (near-minimax,
+// q = Phi(-u), Phi(a) = 1 - q for a >= 0 and q for a < 0, so
+// GeLU(a) = max(a, 0) - u * q on both sides. q = 2^p(u), p a degree-6
+// polynomial fitted to log2 Phi(-u) on [0, 6] (near-minimax,
 // |p - log2 Phi(-u)| <= 6.5e-5, so q is within 4.5e-5 of Phi(-u) relative;
 // csrc/gelu_fit.py derives the coefficients). u is clamped at 6, where
-// Phi(-6) = 1e-9, so past |a| = 6 the error is below |a| * 1e-9. One exp2 and
-// no division: the relative error of the result stays within about 5e-5, far
-// below the bf16 step (2^-8) it is rounded to. NaN stays NaN, +inf stays +inf.
+// Phi(-6) = 1e-9: past |a| = 6 the result is max(a, 0) - 6 * Phi(-6), within
+// 6e-9 of the exact value. One exp2 and no division: the relative error of the
+// result stays within about 5e-5, far below the bf16 step (2^-8) it is rounded
+// to. Per element the VALU runs one med3 (the clamp, |a| a source modifier),
+// six FMAs, the exp2, a compare and select (max(a, 0) that keeps a NaN) and
+// one FMA. NaN stays NaN, +inf stays +inf.
 __device__ __forceinline__ float gelu_bf16(float a) {
-  const float u = fminf(fabsf(a), 6.0f);
+  const float u = __builtin_amdgcn_fmed3f(fabsf(a), 0.0f, 6.0f);
   float p = fmaf(2.29900634e-05f, u, -0.000611100055f);
   p = fmaf(p, u, 0.00719556585f);
   p = fmaf(p, u, -0.051185336f);
@@ -63,7 +67,8 @@ __device__ __forceinline__ float gelu_bf16(float a) {
   p = fmaf(p, u, -1.15017426f);
   p = fmaf(p, u, -1.00006473f);
   const float q = __builtin_amdgcn_exp2f(p);  // p in [-30, -1]: no range reduction needed
-  return a * (a < 0.0f ? q : 1.0f - q);
+  const float r = !(a <= 0.0f) ? a : 0.0f;    // a NaN passes through
+  return fmaf(-u, q, r);
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }

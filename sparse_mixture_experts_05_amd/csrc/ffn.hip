@@ -539,7 +539,7 @@ __device__ __forceinline__ void big_tile_epilogue(const GemmArgs& args, const Ti
           y1 = gelu_bf16(y1);
         }
         const uint32_t own = cvt_bf16x2(y0, y1);  // (row R(v), row R(v) + 1) of this column
-        const uint32_t partner = __builtin_amdgcn_update_dpp(0u, own, 0xB1, 0xF, 0xF, false);
+        const uint32_t partner = __builtin_amdgcn_mov_dpp(own, 0xB1, 0xF, 0xF, true);
         const uint32_t pair = __builtin_amdgcn_perm(partner, own, sel);
         const int roff = (i * 32 + (v >> 2) * 8 + (v & 3)) * CROWB;
         *reinterpret_cast<uint32_t*>(smem + cbase[j] + roff) = pair;

@@ -1,9 +1,9 @@
 """The bf16 layers' GeLU (gelu_bf16 in csrc/common.hpp) meets its stated bound.
 
 GeLU(a) = a * Phi(a) with Phi the standard normal distribution function
-(the erf form, 0.5 * (1 + erf(a / sqrt(2)))). The kernel takes q = Phi(-|a|)
-as 2^p(min(|a|, 6)), p a degree-6 polynomial, and returns a * q for a < 0,
-a * (1 - q) otherwise. The coefficients are read from the kernel source and
+(the erf form, 0.5 * (1 + erf(a / sqrt(2)))). The kernel takes u = min(|a|, 6)
+and q = Phi(-u) as 2^p(u), p a degree-6 polynomial, and returns
+max(a, 0) - u * q in one fma (a * (1 - q) for 0 <= a <= 6, a * q below 0). The coefficients are read from the kernel source and
 the device arithmetic is replayed in float32 (each fma rounded once; exp2
 rounded to float32; the bound leaves room for the hardware exp2, within 1 ulp):
 
@@ -27,9 +27,9 @@ def _coefficients():
     body = body[body.index("float gelu_bf16(float a)"):]
     body = body[: body.index("\n}\n")]
     lits = [float(v) for v in re.findall(r"(-?\d+\.\d+(?:e-?\d+)?)f", body)]
-    # lits: the clamp 6.0, then c6, c5, c4, ..., c0 in Horner order, then 0.0, 1.0
-    assert lits[0] == 6.0
-    return np.array(lits[1:8][::-1], dtype=np.float32)  # c0..c6
+    # lits: the clamp's bounds 0.0 and 6.0, then c6, c5, c4, ..., c0 in Horner order
+    assert lits[:2] == [0.0, 6.0]
+    return np.array(lits[2:9][::-1], dtype=np.float32)  # c0..c6
 
 
 def _gelu_device(a):
@@ -37,12 +37,15 @@ def _gelu_device(a):
     a = np.asarray(a, dtype=np.float32)
     with np.errstate(invalid="ignore", over="ignore"):
         u = np.minimum(np.abs(a), np.float32(6.0))
-        u = np.where(np.isnan(a), np.float32(6.0), u)  # v_min_f32 drops a NaN operand
+        u = np.where(np.isnan(a), np.float32(6.0), u)  # whatever med3 makes of a NaN: r decides
         p = np.float32(c[6])
         for k in range(5, -1, -1):
             p = np.float32(p.astype(np.float64) * u.astype(np.float64) + np.float64(c[k]))
         q = np.float32(np.exp2(p.astype(np.float64)))
-        return np.where(a < 0, a * q, a * (np.float32(1.0) - q)), q
+        r = np.where(~(a <= 0), a, np.float32(0.0))  # NaN passes through
+        # one fma: the product u * q is exact in float64, one rounding to float32
+        g = (-u.astype(np.float64) * q.astype(np.float64) + r.astype(np.float64)).astype(np.float32)
+        return g, q
 
 
 def test_coefficients_fit_log2_phi():
