@@ -18,20 +18,26 @@
 // sized for the worst case (sum over experts of ceil(count/BM) <= rows/BM +
 // min(E, rows)); surplus workgroups exit at once.
 //
-// Two bf16 kernels, both v_mfma_f32_32x32x16_bf16 with fp32 accumulation and
-// operands copied global -> LDS by global_load_lds (8 rows of 128 contiguous
-// bytes per instruction), 16-byte chunks XOR-swizzled by row so fragment
-// reads are bank-conflict free; rows past the segment end are clamped on load
-// and masked on store:
-//   gemm_bf16_big_kernel   256x256 tiles, 8 waves, two LDS stages, blocked
-//                          XCD-aware tile order, split K in the last round of
-//                          long-K launches (gemm_tail_reduce_kernel sums it);
-//                          segments of at most 32 rows as pairs of 32x128
-//                          tiles, one per half of the waves;
-//   gemm_bf16_kernel       32x64 tiles for launches with few rows per expert
-//                          (decode): weight streaming through a 3-stage ring,
-//                          split over K when there are fewer tiles than CUs
-//                          (gemm_small_reduce_kernel sums the slices).
+// bf16 kernels (fp32 accumulation). The tile kernels copy operands global ->
+// LDS with global_load_lds (8 rows of 128 contiguous bytes per instruction),
+// 16-byte chunks XOR-swizzled by row so fragment reads are bank-conflict free,
+// and multiply with v_mfma_f32_32x32x16_bf16; rows past the segment end are
+// clamped on load and masked on store:
+//   gemm_bf16_w4_kernel    256x256 tiles, 4 waves (one per SIMD), 2 A and 3 B
+//                          LDS stages, blocked XCD-aware tile order, split K
+//                          in the last round of long-K launches
+//                          (gemm_tail_reduce_kernel sums it);
+//   gemm_bf16_big_kernel   the same tiles on 8 waves with 64-bit row offsets
+//                          (an operand buffer of 4 GiB or more); segments of
+//                          at most 32 rows as pairs of 32x128 tiles;
+//   gemm_bf16_kernel       32x64 tiles for launches with few rows per expert:
+//                          weight streaming through a 3-stage ring, split over
+//                          K when there are fewer tiles than CUs
+//                          (gemm_small_reduce_kernel sums the slices);
+//   gemm_bf16_rows_kernel  decode launches (up to about two rows per expert):
+//                          16-row blocks, weights loaded straight to registers
+//                          and multiplied with v_mfma_f32_16x16x32_bf16, K
+//                          split over the waves of a workgroup.
 // fp32 path (small fp32 layers): 64x64 tiles of plain FMA.
 #include <algorithm>
 #include <type_traits>
@@ -469,6 +475,162 @@ __global__ __launch_bounds__(kThreads) void gemm_small_reduce_kernel(GemmArgs ar
       if (s < nks) y += v[s];
     if (gelu) y = gelu_bf16(y);
     C[(size_t)row * N + col] = (uint16_t)f32_to_bf16(y);
+  }
+}
+
+// ----------------------------------------------------------------- bf16 MFMA, few rows
+
+// Row block mt of the routed group: experts in order, each expert's segment
+// cut into blocks of BMR rows from its start. One wave finds it (every wave of
+// the workgroup runs the same search, so no barrier): each lane sums the blocks
+// of 4 consecutive experts (E <= 256), a wave scan orders the lanes, and the
+// lane whose range holds mt names the expert. Returns the expert (row0, M:
+// the block's first buffer row and row count), or -1 past the last block.
+template <int BMR>
+__device__ __forceinline__ int find_row_block(const GemmArgs& a, int mt, int& row0, int& M) {
+  constexpr int EPL = 4;
+  const int lane = threadIdx.x & 63;
+  int off[EPL], cnt[EPL], nb[EPL], sum = 0;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    const int e = lane * EPL + j;
+    off[j] = 0;
+    cnt[j] = 0;
+    if (e < a.E) {
+      // clamped like find_tile: a segment never leaves the buffer
+      off[j] = min(max(a.offsets[e], 0), a.rows);
+      cnt[j] = min(max(a.offsets[e + 1], off[j]), a.rows) - off[j];
+    }
+    nb[j] = (cnt[j] + BMR - 1) / BMR;
+    sum += nb[j];
+  }
+  int incl = sum;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int v = __shfl_up(incl, d);
+    if (lane >= d) incl += v;
+  }
+  const int excl = incl - sum;
+  const bool mine = mt >= excl && mt < incl;
+  const uint64_t owner = __ballot(mine);
+  if (owner == 0) return -1;
+  const int src = __ffsll((unsigned long long)owner) - 1;
+  int e = 0, r0 = 0, m = 0, base = excl;
+#pragma unroll
+  for (int j = 0; j < EPL; ++j) {
+    if (mine && mt >= base && mt < base + nb[j]) {
+      e = lane * EPL + j;
+      r0 = off[j] + (mt - base) * BMR;
+      m = min(BMR, cnt[j] - (mt - base) * BMR);
+    }
+    base += nb[j];
+  }
+  row0 = __shfl(r0, src);
+  M = __shfl(m, src);
+  return __shfl(e, src);
+}
+
+// Few-row kernel (decode: a few tokens per expert, so a launch is a stream of
+// the weights). A workgroup takes a block of up to 16 * R rows of one group
+// and 16 * (4 / KQ) columns; each of its 4 waves takes 16 of those columns
+// and one of KQ slices of K. Weights go from memory straight to registers (no
+// LDS staging: no other wave reads them), one 16-byte load per lane per 16
+// columns x 32 k, in chunks of U loads with the next chunk in flight while
+// the current one is multiplied. v_mfma_f32_16x16x32_bf16 takes the weights as
+// its A operand (16 columns) and the token rows as B (16 rows): lane l loads
+// column l % 16 and row l % 16 at k = 8 * (l / 16) of each 32-deep step, the
+// same k for both operands. Rows past the block's end read its last row and
+// their results are not stored (each output row depends on its own input row
+// alone). The KQ partial sums of a column block are added in slice order
+// through LDS, then erf-GeLU (up projection) and bf16 rounding; lane l stores
+// 4 adjacent columns of row l % 16.
+template <int R, int KQ, int U>
+__global__ __launch_bounds__(kThreads) void gemm_bf16_rows_kernel(GemmArgs args) {
+  constexpr int BMR = 16 * R, NC = 16 * (4 / KQ);
+  static_assert(KQ == 1 || KQ == 2 || KQ == 4, "K slices per workgroup");
+  __shared__ f32x4_t red[4][R][64];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int g = blockIdx.x;
+  int group, e, row0, M, n0;
+  if (g >= args.routed_tiles) {
+    const int gs = g - args.routed_tiles;
+    const int ntn = args.shared.N / NC;
+    group = 1;
+    e = 0;
+    row0 = (gs / ntn) * BMR;
+    M = min(BMR, args.shared_M - row0);
+    n0 = (gs % ntn) * NC;
+    if (M <= 0) return;
+  } else {
+    const int ntn = args.routed.N / NC;
+    group = 0;
+    e = find_row_block<BMR>(args, g / ntn, row0, M);
+    if (e < 0) return;
+    n0 = (g % ntn) * NC;
+  }
+  const Group G = pick_group(args, group);
+  const int N = G.N, K = G.K;
+  const int cb = wave / KQ, q = wave % KQ;
+  const int Ks = K / KQ;
+  const int kc = q * Ks + (lane >> 4) * 8;
+  const uint16_t* wp =
+      static_cast<const uint16_t*>(G.B) + ((size_t)e * N + n0 + cb * 16 + (lane & 15)) * K + kc;
+  const uint16_t* xp[R];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb)
+    xp[rb] = static_cast<const uint16_t*>(G.A) +
+             a_row(args, group, row0 + min(rb * 16 + (lane & 15), M - 1)) * K + kc;
+
+  f32x4_t acc[R];
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) acc[rb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  u32x4_t wa[U], xa[U][R], wb[U], xb[U][R];
+  const int nch = Ks / (32 * U);
+#define MOE_ROWS_LOAD(W, X, c)                                   \
+  _Pragma("unroll") for (int u = 0; u < U; ++u) {                \
+    const int k = ((c) * U + u) * 32;                            \
+    W[u] = ld16(wp + k);                                         \
+    _Pragma("unroll") for (int rb = 0; rb < R; ++rb) X[u][rb] = ld16(xp[rb] + k); \
+  }
+#define MOE_ROWS_MMA(W, X)                                                                  \
+  _Pragma("unroll") for (int u = 0; u < U; ++u)                                             \
+  _Pragma("unroll") for (int rb = 0; rb < R; ++rb) acc[rb] =                                \
+      __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(W[u]), as_bf16x8(X[u][rb]), acc[rb], 0, 0, 0);
+  MOE_ROWS_LOAD(wa, xa, 0)
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) { MOE_ROWS_LOAD(wb, xb, c + 1) }
+    MOE_ROWS_MMA(wa, xa)
+    if (c + 2 < nch) { MOE_ROWS_LOAD(wa, xa, c + 2) }
+    if (c + 1 < nch) { MOE_ROWS_MMA(wb, xb) }
+  }
+#undef MOE_ROWS_LOAD
+#undef MOE_ROWS_MMA
+
+  if constexpr (KQ > 1) {
+    if (q != 0) {
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) red[wave][rb][lane] = acc[rb];
+    }
+    __syncthreads();
+    if (q != 0) return;
+#pragma unroll
+    for (int sl = 1; sl < KQ; ++sl)
+#pragma unroll
+      for (int rb = 0; rb < R; ++rb) acc[rb] += red[wave + sl][rb][lane];
+  }
+  const bool gelu = args.gelu != 0;
+  uint16_t* C = static_cast<uint16_t*>(G.C);
+#pragma unroll
+  for (int rb = 0; rb < R; ++rb) {
+    const int r = rb * 16 + (lane & 15);
+    if (r >= M) continue;
+    float y[4] = {acc[rb][0], acc[rb][1], acc[rb][2], acc[rb][3]};
+    if (gelu) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) y[v] = gelu_bf16(y[v]);
+    }
+    const uint2 out = make_uint2(cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]));
+    *reinterpret_cast<uint2*>(C + (size_t)(row0 + r) * N + n0 + cb * 16 + 4 * (lane >> 4)) = out;
   }
 }
 
@@ -1105,6 +1267,76 @@ hipError_t run_bf16(GemmArgs a, int rows, int E, int nks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Few-row kernel. Workgroups of a launch with 16 * R-row blocks and KQ K
+// slices per workgroup (16 * 4 / KQ columns each). kRowsU: loads per chunk of
+// a wave's weight stream (two chunks in flight). Measured on the
+// graph-replayed decode layer (H = 4096, E = 128, k = 8, F = 1536 + shared),
+// FFN at T = 16: 8 loads 401 us, 4 loads 401 us, 2 loads 388 us, 1 load 396 us
+// (fewer registers per wave, more waves per SIMD).
+constexpr int kRowsU = 2;
+
+template <int R>
+int rows_grid(const GemmArgs& a, int rows, int E, int kq) {
+  constexpr int BMR = 16 * R;
+  const int nc = 16 * (4 / kq);
+  // sum_e ceil(c_e / BMR) <= rows / BMR + #{e : c_e > 0}
+  const int mt_max = rows / BMR + std::min(E, rows);
+  const int shared = a.shared_M > 0 ? ((a.shared_M + BMR - 1) / BMR) * (a.shared.N / nc) : 0;
+  return mt_max * (a.routed.N / nc) + shared;
+}
+
+// K slices per workgroup: the most of 4, 2, 1 that leave each wave's slice
+// whole chunks of kRowsU loads in both groups (0: none fits). More slices
+// mean more, shorter weight streams in flight: measured on the graph-replayed
+// decode layer (H = 4096, E = 128, k = 8, F = 1536 + shared) at T = 16, FFN
+// 396 us with 4 slices against 427 us with the fewest slices that still give
+// 1024 workgroups (1 slice, 64-column blocks: each token row read by 4x fewer
+// workgroups), both with 8-load chunks.
+template <int R>
+int rows_kq(const GemmArgs& a, int rows, int E) {
+  (void)rows;
+  (void)E;
+  for (int kq : {4, 2, 1}) {
+    const int step = 32 * kRowsU * kq;
+    if (a.routed.K % step == 0 && (a.shared_M == 0 || a.shared.K % step == 0)) return kq;
+  }
+  return 0;
+}
+
+// 16-row blocks per workgroup of the few-row kernel for a launch, or 0 for
+// the 32 x 64 tile kernel. The few-row kernel reads each token row once per
+// 16 columns (the tile kernel: once per 64, through LDS) and every row block
+// re-reads its expert's weights, so it pays at up to about two rows per
+// expert on average. Measured (decode layer above, graph replay from cold
+// caches, few-row kernel against tile kernel): T = 1 77 against 83 us,
+// T = 16 415 against 440, T = 32 561 against 573, T = 64 639 against 616,
+// T = 128 742 against 629.
+int rows_blocks(const GemmArgs& a, int rows, int E) {
+  if (rows_kq<1>(a, rows, E) == 0 || a.routed.N % 64 != 0 ||
+      (a.shared_M > 0 && a.shared.N % 64 != 0))
+    return 0;
+  return rows <= 2 * E ? 1 : 0;
+}
+
+template <int R, int KQ>
+hipError_t run_rows(GemmArgs a, int rows, int E, hipStream_t s) {
+  constexpr int BMR = 16 * R, NC = 16 * (4 / KQ);
+  a.routed_tiles = (rows / BMR + std::min(E, rows)) * (a.routed.N / NC);
+  const int grid = rows_grid<R>(a, rows, E, KQ);
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_bf16_rows_kernel<R, KQ, kRowsU>), dim3(grid), dim3(kThreads), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int R>
+hipError_t run_rows_r(const GemmArgs& a, int rows, int E, hipStream_t s) {
+  switch (rows_kq<R>(a, rows, E)) {
+    case 4: return run_rows<R, 4>(a, rows, E, s);
+    case 2: return run_rows<R, 2>(a, rows, E, s);
+    default: return run_rows<R, 1>(a, rows, E, s);
+  }
+}
+
 hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_segments,
                     hipStream_t s) {
   if (!bf16) {
@@ -1115,6 +1347,7 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
     return hipGetLastError();
   }
   if (small_segments) {
+    if (rows_blocks(a, rows, E) == 1) return run_rows_r<1>(a, rows, E, s);
     // 32x64 tiles: 36 KiB rings, so more workgroups per CU keep weight copies
     // in flight than with 32x128 tiles (measured, graph-replayed decode layer,
     // H = 4096, E = 128, k = 8: FFN at T = 128 640 -> 603 us, T = 16 426 ->

@@ -5,10 +5,11 @@ The tile schedule of the 256x256 kernel is built on the device from the
 offsets alone, so these layouts aim at its corners: empty experts, segments of
 1, 255, 256 and 257 rows, rows in several n-blocks of column tiles, every row
 in one expert, the largest expert count, the split-K last round (K >= 8192),
-and the small-segment kernel, whole-K and split over K. ys is filled with NaN first, so a tile that is
-never computed (or computed twice into the wrong rows) cannot pass. Every
-segment must meet the bf16 bar on its own (relative L2 <= 2e-2 against the
-float64 oracle), and so must the shared expert.
+the small-segment kernel, whole-K and split over K, and the decode kernel
+(16-row blocks, K split over the waves). ys is filled with NaN first, so a
+tile that is never computed (or computed twice into the wrong rows) cannot
+pass. Every segment must meet the bf16 bar on its own (relative L2 <= 2e-2
+against the float64 oracle), and so must every row and the shared expert.
 """
 import numpy as np
 import pytest
@@ -30,8 +31,15 @@ CASES = [
     ("e256_skewed_big_tiles", 128, 192, 64, ("zipf", 256, 60000, 7)),
     ("split_k_tail", 256, 8192, 8192, [300, 0, 129, 40]),
     ("small_segments", 512, 448, 128, [1, 0, 2, 0, 0, 3, 0, 1, 0, 0, 0, 5, 0, 0, 2, 0]),
-    # a few rows and long K: the small-tile up projection splits K over 8 slices
+    # a few rows and long K (the decode kernel: K in 4 slices per workgroup)
     ("small_split_k", 4096, 512, 256, [1, 0, 2, 0, 0, 0, 1, 0]),
+    # the decode kernel (at most 2 rows per expert on average) with segments of
+    # 16, 17, 33 and 40 rows (several 16-row blocks re-reading one expert's
+    # weights), a 107-row shared group (7 blocks); up K = 256 in 4 slices, down
+    # K = 320 (shared 192) whole per wave
+    ("decode_kernel_blocks", 256, 320, 192, [17, 0, 33, 16, 1, 0, 40] + [0] * 57),
+    # the decode kernel with K in 2 slices per workgroup (K = 384, 640)
+    ("decode_kernel_two_slices", 384, 640, 0, [3, 0, 1, 16, 0, 2, 0, 0, 0, 0, 1, 0, 0, 0, 0, 5]),
 ]
 
 
@@ -68,7 +76,8 @@ def test_ffn_segments(case):
     offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
     big = rows >= 64 * E
     print(f"\n[gpu] ffn segments {name}: E={E} rows={rows} H={H} F={F} Fs={Fs} "
-          f"{'256x256 tiles' if big else 'small tiles'} max={counts.max()}", flush=True)
+          f"{'256x256 tiles' if big else ('decode kernel' if rows <= 2 * E else 'small tiles')} "
+          f"max={counts.max()}", flush=True)
 
     d_xs = to_dev(xs)
     ys = torch.full((rows, H), float("nan"), dtype=torch.bfloat16, device="cuda")
@@ -85,13 +94,16 @@ def test_ffn_segments(case):
             continue
         ref = oracle.expert_ffn(xs[lo:hi], w1[e], w2[e])
         err = np.linalg.norm(got[lo:hi] - ref) / np.linalg.norm(ref)
-        assert err <= TOL_BF16_REL_L2, (e, lo, hi, err)
+        rows_err = np.linalg.norm(got[lo:hi] - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        assert err <= TOL_BF16_REL_L2 and rows_err.max() <= TOL_BF16_REL_L2, (e, lo, hi, err,
+                                                                             rows_err.max())
     if Fs:
         gsh = bf16_bits_to_f32(to_host(ysh)).astype(np.float64)
         ref = oracle.shared_outputs(xs, ws1, ws2)
         assert np.isfinite(gsh).all()
         err = np.linalg.norm(gsh - ref) / np.linalg.norm(ref)
-        assert err <= TOL_BF16_REL_L2, err
+        rows_err = np.linalg.norm(gsh - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        assert err <= TOL_BF16_REL_L2 and rows_err.max() <= TOL_BF16_REL_L2, (err, rows_err.max())
 
 
 def test_ffn_with_an_operand_buffer_past_4_gib():
