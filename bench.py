@@ -195,6 +195,19 @@ def cpu_baseline(cfg, L, n_tokens, min_seconds=0.0):
             "seconds": dt}
 
 
+def single_thread_baseline(cfg, L, min_seconds=2.0):
+    """The oracle on one BLAS thread over a whole small layer (decode T = 1,
+    the tiny fp32 layer), passes repeated until min_seconds have gone by."""
+    from threadpoolctl import threadpool_limits
+
+    import oracle  # noqa: F401  (its thread pools load first, so the limit reaches them)
+
+    with threadpool_limits(limits=1):
+        cb = cpu_baseline(cfg, L, cfg.T, min_seconds=min_seconds)
+    cb.pop("seconds")
+    return cb
+
+
 NAMES = ["route", "dispatch", "expert_ffn", "combine", "load_stats"]
 
 
@@ -395,6 +408,7 @@ def decode_sweep(args, moe, torch, flush):
     print(f"[bench] decode sweep: generating inputs", file=sys.stderr, flush=True)
     L = make_layer(full)
     out = {}
+    single = getattr(args, "single_thread", {})
     for T in DECODE_TOKENS:
         cfg = get_config(f"decode@T{T}")
         Lt = dict(L)
@@ -442,6 +456,8 @@ def decode_sweep(args, moe, torch, flush):
               file=sys.stderr, flush=True)
         del g, layer
         torch.cuda.empty_cache()
+        if T == 1 and not getattr(args, "no_cpu_baseline", True):
+            single["decode@T1"] = single_thread_baseline(cfg, Lt)
     return out
 
 
@@ -560,6 +576,7 @@ def main():
             del r
             torch.cuda.empty_cache()
         result["workloads"] = subs
+        args.single_thread = {}
         result["decode"] = decode_sweep(args, moe, torch, flush)
     # Context for the datasheet fractions of the HBM-bound steps: a plain
     # 512 MiB device copy (1 GiB of reads and writes, beyond the last-level
@@ -604,6 +621,12 @@ def main():
             # a whole layer that takes under 10 s is run again until 10 s have gone by
             cb = cpu_baseline(cfg, L, n2, min_seconds=10.0 if n2 == T else 0.0)
         cb.pop("seconds")
+        # context: the oracle on one thread over two whole small layers
+        from synth import get_config as _gc, make_layer as _ml
+        single = dict(getattr(args, "single_thread", {}))
+        tiny = _gc("tiny_fp32")
+        single["tiny_fp32"] = single_thread_baseline(tiny, _ml(tiny))
+        cb["single_thread"] = single
         result["cpu_baseline"] = cb
     print(json.dumps(result), flush=True)
 
