@@ -22,7 +22,10 @@ layers and the decode sweep (T = 1..128, graph replay). Prints one JSON line:
   value        tokens/s of the headline layer (T / cold step time)
   roofline     the dominant kernel, the bf16 MFMA grouped GEMM (launched twice
                per step: up and down projections, 2*rows*H*F flops each),
-               against the dense bf16 MFMA peak of 2500 TFLOP/s
+               against the dense bf16 MFMA peak of 2500 TFLOP/s; its launches
+               are timed with HIP events that the library records right
+               before and after each of them on their stream
+               (moe_expert_ffn_gather_timed)
   kernels      per-call average ms (p10 / median / p90 too) and the achieved
                fraction of its roofline; route, dispatch and combine also as a
                fraction of a plain device copy timed in the same run
@@ -221,6 +224,7 @@ class Layer:
             else torch.from_numpy(a).cuda())
         self.cfg, self.moe, self.torch = cfg, moe, torch
         self.copy_gather = copy_gather
+        self.times_gemm = not copy_gather  # moe_expert_ffn_gather_timed
         self.x, self.wg, self.bias = dev(L["x"]), dev(L["wg"]), dev(L["bias"])
         self.w1, self.w2, self.ws1, self.ws2 = dev(L["w1"]), dev(L["w2"]), dev(L["ws1"]), dev(L["ws2"])
         T, H, E, k, F, Fs = cfg.T, cfg.H, cfg.E, cfg.k, cfg.F, cfg.Fs
@@ -252,7 +256,7 @@ class Layer:
         self.cap = moe.moe_capacity(T, k, E, cfg.cf) if drop else None
         self.stream = torch.cuda.current_stream()
 
-    def step(self, ev=None):
+    def step(self, ev=None, gemm_ev=None):
         moe, s, cfg = self.moe, self.stream, self.cfg
         rec = (lambda i: ev[i].record(s)) if ev is not None else (lambda i: None)
         rec(0)
@@ -269,7 +273,7 @@ class Layer:
         else:
             moe.moe_expert_ffn_gather(self.x, self.dsp["perm"], cfg.k, self.dsp["offsets"],
                                       self.w1, self.w2, ws1=self.ws1, ws2=self.ws2, ys=self.ys,
-                                      ysh=self.ysh, ws=self.ws_f, stream=s)
+                                      ysh=self.ysh, ws=self.ws_f, stream=s, gemm_events=gemm_ev)
         rec(3)
         moe.moe_combine(self.ys, self.dsp["inv"], self.wts, self.ysh, out=self.out, stream=s)
         rec(4)
@@ -315,16 +319,22 @@ def timed_steps(layer, torch, steps, flush):
     events. Returns the per-call samples (ms), the per-step event spans (ms)
     and the wall time (s)."""
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
+    # the library records these right before and after each GEMM launch
+    gev = ([[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
+           if layer.times_gemm else None)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         if flush is not None:
             flush(s)
-        layer.step(events[s])
+        layer.step(events[s], gev[s] if gev else None)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     samples = {n: np.array([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])
                for i, n in enumerate(NAMES)}
+    if gev:
+        samples["gemm_up"] = np.array([g[0].elapsed_time(g[1]) for g in gev])
+        samples["gemm_down"] = np.array([g[2].elapsed_time(g[3]) for g in gev])
     spans = np.array([events[s][0].elapsed_time(events[s][5]) for s in range(steps)])
     return samples, spans, elapsed
 
@@ -336,11 +346,18 @@ def kernel_table(cfg, samples, work, copy_gather=False):
     peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
     ffn_ms = per["expert_ffn"]
     # two launches of the same GEMM kernel per step, equal algorithmic flops each
-    achieved = (work["ffn_flops"] / 2) / ((ffn_ms / 2) * 1e-3) / 1e12
+    call_rate = (work["ffn_flops"] / 2) / ((ffn_ms / 2) * 1e-3) / 1e12
+    achieved = call_rate
+    launch = None
+    if "gemm_up" in samples:
+        # the kernel's own launches, timed by events the library records
+        # around them on their stream (planning and reduce launches outside)
+        launch = float(np.concatenate([samples["gemm_up"], samples["gemm_down"]]).mean())
+        achieved = (work["ffn_flops"] / 2) / (launch * 1e-3) / 1e12
     k = {
         "route": {"ms": per["route"], "GB/s": work["route_bytes"] / per["route"] / 1e6},
         "dispatch": {"ms": per["dispatch"], "GB/s": work["dispatch_bytes"] / per["dispatch"] / 1e6},
-        "expert_ffn": {"ms": ffn_ms, "TFLOP/s": achieved, "mfma_frac": achieved / peak,
+        "expert_ffn": {"ms": ffn_ms, "TFLOP/s": call_rate, "mfma_frac": call_rate / peak,
                        "weight_stream_GB/s": work["ffn_weight_bytes"] / ffn_ms / 1e6},
         "combine": {"ms": per["combine"], "GB/s": work["combine_bytes"] / per["combine"] / 1e6},
         "load_stats": {"ms": per["load_stats"]},
@@ -351,6 +368,12 @@ def kernel_table(cfg, samples, work, copy_gather=False):
     if not copy_gather:
         k["dispatch"]["moves"] = ("ids and indices only (the FFN gathers the token rows "
                                   "through perm), so launch latency bounds it")
+    if launch is not None:
+        k["expert_ffn"]["gemm_launch_ms"] = {"up": float(samples["gemm_up"].mean()),
+                                             "down": float(samples["gemm_down"].mean()),
+                                             "mean": launch}
+        k["expert_ffn"]["gemm_TFLOP/s"] = achieved
+        k["expert_ffn"]["gemm_mfma_frac"] = achieved / peak
     for n in NAMES:
         p10, p50, p90 = np.percentile(samples[n], [10, 50, 90])
         k[n].update(p10_ms=float(p10), median_ms=float(p50), p90_ms=float(p90))
@@ -392,7 +415,8 @@ def summary(res, which="cold"):
     k, achieved, peak = res[which]
     ms = res["cold_ms"] if which == "cold" else res["warm_ms"]
     return {"tokens/s": cfg.T / (ms * 1e-3), "ms_per_step": ms,
-            "ffn_TFLOP/s": achieved, "ffn_mfma_frac": achieved / peak,
+            "gemm_TFLOP/s": achieved, "gemm_mfma_frac": achieved / peak,
+            "ffn_call_TFLOP/s": k["expert_ffn"]["TFLOP/s"],
             "route_hbm_frac": k["route"]["hbm_frac"], "combine_hbm_frac": k["combine"]["hbm_frac"],
             "kernels_median_ms": {n: k[n]["median_ms"] for n in NAMES}}
 
@@ -559,7 +583,11 @@ def main():
                              f"cold: {flush.describe()}, outside the events"},
         "roofline": {"bound": "mfma" if bf16 else "alu", "kernel": gemm_kernel_name(cfg),
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s",
-                     "frac": achieved / peak, "traffic": read_traffic()},
+                     "frac": achieved / peak, "traffic": read_traffic(),
+                     "timing": ("the FFN call's event span, halved (--copy-gather)" if layer.copy_gather
+                                else "HIP events recorded by the library right before and after each "
+                                     "GEMM launch on its stream (moe_expert_ffn_gather_timed); mean "
+                                     "over the up and down launches of the timed steps")},
         "kernels": kernels,
         "mfma_util_pct_ffn": 100.0 * achieved / peak,
         "warm": summary(head, "warm"),

@@ -245,6 +245,23 @@ int moe_expert_ffn_gather(const void* x, const int32_t* perm, int k, const int32
                           void* ysh, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * moe_expert_ffn_gather_timed - moe_expert_ffn_gather that also records
+ * caller-created HIP events on `stream`, for timing the grouped GEMM kernel
+ * itself (the FFN's dominant kernel) with events on the stream it runs on:
+ * events[0] / events[1] right before / after the up projection's GEMM launch,
+ * events[2] / events[3] the same for the down projection. The planning launch
+ * and any split-K reduce launch fall outside the pairs. events: host array of
+ * 4 hipEvent_t (as void*), owned by the caller; NULL, or a NULL entry, records
+ * nothing there. Results, arguments and errors as moe_expert_ffn_gather; a
+ * failed event record returns MOE_ERR_HIP.
+ */
+int moe_expert_ffn_gather_timed(const void* x, const int32_t* perm, int k, const int32_t* offsets,
+                                int rows, int E, int H, int F, const void* w1, const void* w2,
+                                const void* ws1, const void* ws2, int T, int Fs, int dtype,
+                                void* ys, void* ysh, void* ws, size_t ws_bytes, void* stream,
+                                void* const* events);
+
+/*
  * moe_combine - weighted combine back to token order ([K3] combine phase;
  * [BLOG] section 3.1 "scatter back to the original positions").
  *   out[t,:] = sum_{j=0..k-1} topk_w[t,j] * ys[inv[t*k+j],:]  (+ ysh[t,:])

@@ -32,6 +32,8 @@ SIGNATURES = {
                             _vp, _vp, _sz, _vp]),
     "moe_expert_ffn_gather": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp, _i,
                                    _i, _i, _vp, _vp, _vp, _sz, _vp]),
+    "moe_expert_ffn_gather_timed": (_i, [_vp, _vp, _i, _vp, _i, _i, _i, _i, _vp, _vp, _vp, _vp,
+                                         _i, _i, _i, _vp, _vp, _vp, _sz, _vp, _vp]),
     "moe_combine": (_i, [_vp, _vp, _vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "moe_load_stats": (_i, [_vp, _i, _i, _i, _d, _vp, _vp, _vp, _vp]),
     "moe_bias_update": (_i, [_vp, _i, ctypes.c_float, _vp, _vp, _vp]),
@@ -317,9 +319,12 @@ def moe_expert_ffn(xs, offsets, w1, w2, x=None, ws1=None, ws2=None, T=None, ys=N
 
 
 def moe_expert_ffn_gather(x, perm, k: int, offsets, w1, w2, ws1=None, ws2=None, rows=None,
-                          ys=None, ysh=None, ws=None, stream=None):
+                          ys=None, ysh=None, ws=None, stream=None, gemm_events=None):
     """moe_expert_ffn reading routed row p from x[perm[p] // k] (no xs copy).
-    Returns (ys [rows,H], ysh [T,H] or None); rows defaults to T*k."""
+    Returns (ys [rows,H], ysh [T,H] or None); rows defaults to T*k.
+    gemm_events: four torch.cuda.Event (timing enabled) that the library
+    records right before and after the up and the down GEMM launches
+    (moe_expert_ffn_gather_timed), or None."""
     T, H = _dims(x, "x", 2)
     E, F, _ = _dims(w1, "w1", 3)
     Fs = 0 if ws1 is None else _dims(ws1, "ws1", 2)[0]
@@ -346,12 +351,22 @@ def moe_expert_ffn_gather(x, perm, k: int, offsets, w1, w2, ws1=None, ws2=None, 
         ysh = torch.empty((T, H), dtype=x.dtype, device=dev)
     nbytes = moe_expert_ffn_workspace_bytes(rows, T, H, E, F, Fs, dt)
     ws = _workspace(nbytes, dev, ws)
-    _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(
-        _dev(x, "x"), _dev(perm, "perm", torch.int32), k, _dev(offsets, "offsets", torch.int32),
-        rows, E, H, F, _dev(w1, "w1", x.dtype), _dev(w2, "w2", x.dtype),
-        _dev(ws1, "ws1", x.dtype), _dev(ws2, "ws2", x.dtype), T, Fs, dt, _dev(ys, "ys", x.dtype),
-        _dev(ysh, "ysh", x.dtype) if Fs > 0 else None, _dev(ws, "ws"), ws.numel(),
-        _stream(stream)))
+    args = (_dev(x, "x"), _dev(perm, "perm", torch.int32), k, _dev(offsets, "offsets", torch.int32),
+            rows, E, H, F, _dev(w1, "w1", x.dtype), _dev(w2, "w2", x.dtype),
+            _dev(ws1, "ws1", x.dtype), _dev(ws2, "ws2", x.dtype), T, Fs, dt, _dev(ys, "ys", x.dtype),
+            _dev(ysh, "ysh", x.dtype) if Fs > 0 else None, _dev(ws, "ws"), ws.numel(),
+            _stream(stream))
+    if gemm_events is None:
+        _check("moe_expert_ffn_gather", lib().moe_expert_ffn_gather(*args))
+    else:
+        if len(gemm_events) != 4:
+            raise ValueError("gemm_events takes four events (up before / after, down before / after)")
+        s = stream if stream is not None else torch.cuda.current_stream(dev)
+        handles = (ctypes.c_void_p * 4)()
+        for i, ev in enumerate(gemm_events):
+            ev.record(s)  # torch creates the HIP event on its first record
+            handles[i] = ev.cuda_event
+        _check("moe_expert_ffn_gather_timed", lib().moe_expert_ffn_gather_timed(*args, handles))
     return ys, (ysh if Fs > 0 else None)
 
 

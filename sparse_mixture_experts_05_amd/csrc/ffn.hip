@@ -1254,14 +1254,18 @@ int small_splits(const GemmArgs& a, int rows, int E) {
   return std::max(1, std::min(std::min(by_tiles, by_k), kMaxSmallSplit));
 }
 
+// Records ev on s when given (the caller's timing of one GEMM launch).
+hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
+
 template <int BM, int BN, int WM, int WN>
-hipError_t run_bf16(GemmArgs a, int rows, int E, int nks, hipStream_t s) {
+hipError_t run_bf16(GemmArgs a, int rows, int E, int nks, hipStream_t s, hipEvent_t after) {
   dim3 grid;
   grid_of<BM, BN>(a, rows, E, grid);
   const unsigned nt = grid.x;
   grid.y = nks;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN>), grid, dim3(kThreads), 0, s, a);
   hipError_t err = hipGetLastError();
+  if (err == hipSuccess) err = mark(after, s);
   if (err != hipSuccess || nks <= 1) return err;
   hipLaunchKernelGGL((gemm_small_reduce_kernel<BM, BN>), dim3(nt), dim3(kThreads), 0, s, a, nks);
   return hipGetLastError();
@@ -1319,41 +1323,47 @@ int rows_blocks(const GemmArgs& a, int rows, int E) {
 }
 
 template <int R, int KQ>
-hipError_t run_rows(GemmArgs a, int rows, int E, hipStream_t s) {
+hipError_t run_rows(GemmArgs a, int rows, int E, hipStream_t s, hipEvent_t after) {
   constexpr int BMR = 16 * R, NC = 16 * (4 / KQ);
   a.routed_tiles = (rows / BMR + std::min(E, rows)) * (a.routed.N / NC);
   const int grid = rows_grid<R>(a, rows, E, KQ);
-  if (grid == 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_bf16_rows_kernel<R, KQ, kRowsU>), dim3(grid), dim3(kThreads), 0, s, a);
-  return hipGetLastError();
+  if (grid > 0)
+    hipLaunchKernelGGL((gemm_bf16_rows_kernel<R, KQ, kRowsU>), dim3(grid), dim3(kThreads), 0, s, a);
+  const hipError_t err = hipGetLastError();
+  return err == hipSuccess ? mark(after, s) : err;
 }
 
 template <int R>
-hipError_t run_rows_r(const GemmArgs& a, int rows, int E, hipStream_t s) {
+hipError_t run_rows_r(const GemmArgs& a, int rows, int E, hipStream_t s, hipEvent_t after) {
   switch (rows_kq<R>(a, rows, E)) {
-    case 4: return run_rows<R, 4>(a, rows, E, s);
-    case 2: return run_rows<R, 2>(a, rows, E, s);
-    default: return run_rows<R, 1>(a, rows, E, s);
+    case 4: return run_rows<R, 4>(a, rows, E, s, after);
+    case 2: return run_rows<R, 2>(a, rows, E, s, after);
+    default: return run_rows<R, 1>(a, rows, E, s, after);
   }
 }
 
+// One GEMM launch (and its split-K reduce, if any). before / after: events
+// recorded right before and right after the GEMM kernel itself, or null.
 hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_segments,
-                    hipStream_t s) {
+                    hipStream_t s, hipEvent_t before = nullptr, hipEvent_t after = nullptr) {
+  hipError_t err = mark(before, s);
+  if (err != hipSuccess) return err;
   if (!bf16) {
     GemmArgs b = a;
     dim3 grid;
     grid_of<64, 64>(b, rows, E, grid);
     hipLaunchKernelGGL(gemm_f32_kernel, grid, dim3(kThreads), 0, s, b);
-    return hipGetLastError();
+    err = hipGetLastError();
+    return err == hipSuccess ? mark(after, s) : err;
   }
   if (small_segments) {
-    if (rows_blocks(a, rows, E) == 1) return run_rows_r<1>(a, rows, E, s);
+    if (rows_blocks(a, rows, E) == 1) return run_rows_r<1>(a, rows, E, s, after);
     // 32x64 tiles: 36 KiB rings, so more workgroups per CU keep weight copies
     // in flight than with 32x128 tiles (measured, graph-replayed decode layer,
     // H = 4096, E = 128, k = 8: FFN at T = 128 640 -> 603 us, T = 16 426 ->
     // 412 us, T = 1 unchanged; a four- or five-stage ring gains nothing more)
     const int nks = a.part != nullptr ? small_splits(a, rows, E) : 1;
-    return run_bf16<kSmallBM, kSmallBN, 1, 2>(a, rows, E, nks, s);
+    return run_bf16<kSmallBM, kSmallBN, 1, 2>(a, rows, E, nks, s, after);
   }
   // big tiles: the table was written by big_plan_kernel. The 4-wave kernel
   // addresses its operand rows with 32-bit offsets; a launch with an operand
@@ -1370,7 +1380,8 @@ hipError_t run_gemm(const GemmArgs& a, int rows, int E, bool bf16, bool small_se
   } else {
     hipLaunchKernelGGL((gemm_bf16_w4_kernel<false>), dim3(a.slots), dim3(256), 0, s, a);
   }
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
+  if (err == hipSuccess) err = mark(after, s);
   if (err != hipSuccess || a.part == nullptr) return err;
   hipLaunchKernelGGL((gemm_tail_reduce_kernel<256, 256>), dim3(kReduceSlots * kReduceParts),
                      dim3(kThreads), 0, s, a);
@@ -1482,7 +1493,10 @@ hipError_t launch_expert_ffn(const void* xs, const int32_t* gather, int gk,
                              const int32_t* offsets, int rows, int E, int H, int F, const void* w1,
                              const void* w2, const void* x, const void* ws1, const void* ws2,
                              int T, int Fs, bool bf16, void* ys, void* ysh, void* ws,
-                             hipStream_t s) {
+                             hipStream_t s, void* const* events) {
+  hipEvent_t ev[4] = {nullptr, nullptr, nullptr, nullptr};
+  if (events)
+    for (int i = 0; i < 4; ++i) ev[i] = static_cast<hipEvent_t>(events[i]);
   const FfnLayout Lo = ffn_layout(xs, gather, gk, offsets, rows, E, H, F, w1, w2, x, ws1, ws2, T,
                                   Fs, bf16, ys, ysh, ws);
   hipError_t err;
@@ -1493,9 +1507,9 @@ hipError_t launch_expert_ffn(const void* xs, const int32_t* gather, int gk,
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
-  err = run_gemm(Lo.up, rows, E, bf16, Lo.small_segments, s);
+  err = run_gemm(Lo.up, rows, E, bf16, Lo.small_segments, s, ev[0], ev[1]);
   if (err != hipSuccess) return err;
-  return run_gemm(Lo.down, rows, E, bf16, Lo.small_segments, s);
+  return run_gemm(Lo.down, rows, E, bf16, Lo.small_segments, s, ev[2], ev[3]);
 }
 
 }  // namespace moe

@@ -28,7 +28,7 @@ hipError_t launch_expert_ffn(const void* xs, const int32_t* gather, int gk,
                              const int32_t* offsets, int rows, int E, int H, int F, const void* w1,
                              const void* w2, const void* x, const void* ws1, const void* ws2,
                              int T, int Fs, bool bf16, void* ys, void* ysh, void* ws,
-                             hipStream_t s);
+                             hipStream_t s, void* const* events = nullptr);
 
 hipError_t launch_combine(const void* ys, const int32_t* inv, const float* topk_w,
                           const void* ysh, int T, int H, int k, bool bf16, void* out,

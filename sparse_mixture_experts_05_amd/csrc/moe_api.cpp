@@ -156,6 +156,15 @@ int moe_expert_ffn_gather(const void* x, const int32_t* perm, int k, const int32
                           int rows, int E, int H, int F, const void* w1, const void* w2,
                           const void* ws1, const void* ws2, int T, int Fs, int dtype, void* ys,
                           void* ysh, void* ws, size_t ws_bytes, void* stream) {
+  return moe_expert_ffn_gather_timed(x, perm, k, offsets, rows, E, H, F, w1, w2, ws1, ws2, T, Fs,
+                                     dtype, ys, ysh, ws, ws_bytes, stream, nullptr);
+}
+
+int moe_expert_ffn_gather_timed(const void* x, const int32_t* perm, int k, const int32_t* offsets,
+                                int rows, int E, int H, int F, const void* w1, const void* w2,
+                                const void* ws1, const void* ws2, int T, int Fs, int dtype,
+                                void* ys, void* ysh, void* ws, size_t ws_bytes, void* stream,
+                                void* const* events) {
   if (!x || !perm || !offsets || !w1 || !w2 || !ys) return MOE_ERR_INVALID_ARG;
   if (!aligned16(x) || !aligned16(w1) || !aligned16(w2) || !aligned16(ys)) return MOE_ERR_INVALID_ARG;
   if (k < 1) return MOE_ERR_INVALID_ARG;
@@ -170,7 +179,7 @@ int moe_expert_ffn_gather(const void* x, const int32_t* perm, int k, const int32
     return MOE_ERR_WORKSPACE;
   return from_hip(moe::launch_expert_ffn(x, perm, k, offsets, rows, E, H, F, w1, w2, x, ws1, ws2,
                                          T, Fs, dtype == MOE_BF16, ys, Fs > 0 ? ysh : nullptr, ws,
-                                         as_stream(stream)));
+                                         as_stream(stream), events));
 }
 
 int moe_combine(const void* ys, const int32_t* inv, const float* topk_w, const void* ysh, int T,

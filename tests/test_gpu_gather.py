@@ -50,3 +50,36 @@ def test_gather_ffn_matches_dispatch_copy(case):
     if cfg.Fs:
         assert np.array_equal(to_host(fused["ysh"]), to_host(copy["ysh"]))
     assert np.array_equal(to_host(fused["out"]), to_host(copy["out"]))
+
+
+TIMED = [MoEConfig("t_big", T=700, H=512, E=8, k=2, F=640),            # 256x256 tiles
+         MoEConfig("t_split_k", T=600, H=256, E=4, k=1, F=8192, Fs=8192),  # + split-K reduce
+         "decode@T1"]                                                       # decode kernel
+
+
+@pytest.mark.parametrize("cfg", TIMED, ids=lambda c: c if isinstance(c, str) else c.name)
+def test_timed_gather_ffn(cfg):
+    """moe_expert_ffn_gather_timed gives the bits of moe_expert_ffn_gather and
+    records its four events around the two GEMM launches, in order, inside the
+    call."""
+    cfg = get_config(cfg) if isinstance(cfg, str) else cfg
+    L = make_layer(cfg)
+    d = {k: to_dev(v) for k, v in L.items()}
+    print(f"\n[gpu] timed gather FFN {cfg.name}", flush=True)
+    r = moe.moe_layer_forward(d["x"], d["wg"], d["bias"], d["w1"], d["w2"], cfg.k,
+                              ws1=d["ws1"], ws2=d["ws2"])
+    args = (d["x"], r["perm"], cfg.k, r["offsets"], d["w1"], d["w2"])
+    kw = dict(ws1=d["ws1"], ws2=d["ws2"])
+    ys0, ysh0 = moe.moe_expert_ffn_gather(*args, **kw)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+    ev[0].record()
+    ys1, ysh1 = moe.moe_expert_ffn_gather(*args, **kw, gemm_events=ev[1:5])
+    ev[5].record()
+    torch.cuda.synchronize()
+    assert np.array_equal(to_host(ys0), to_host(ys1))
+    if cfg.Fs:
+        assert np.array_equal(to_host(ysh0), to_host(ysh1))
+    gaps = [ev[i].elapsed_time(ev[i + 1]) for i in range(5)]
+    assert all(g >= 0 for g in gaps), gaps          # recorded in this order on the stream
+    assert gaps[1] > 0 and gaps[3] > 0, gaps        # the up and down GEMM launches
+    assert sum(gaps) <= ev[0].elapsed_time(ev[5]) * (1 + 1e-6) + 1e-3
