@@ -25,7 +25,8 @@ layers and the decode sweep (T = 1..128, graph replay). Prints one JSON line:
                against the dense bf16 MFMA peak of 2500 TFLOP/s; its launches
                are timed with HIP events that the library records right
                before and after each of them on their stream
-               (moe_expert_ffn_gather_timed)
+               (moe_expert_ffn_gather_timed), in steps interleaved with the
+               timed ones (event records add work to the stream)
   kernels      per-call average ms (p10 / median / p90 too) and the achieved
                fraction of its roofline; route, dispatch and combine also as a
                fraction of a plain device copy timed in the same run
@@ -313,21 +314,32 @@ class Flush:
                 else "a kernel reading 1 GiB before every step")
 
 
-def timed_steps(layer, torch, steps, flush):
+def timed_steps(layer, torch, steps, flush, gemm=False):
     """K timed eager steps with HIP events around every call (on the launch
     stream). With flush, its kernel runs before every step, outside the
-    events. Returns the per-call samples (ms), the per-step event spans (ms)
-    and the wall time (s)."""
+    events. With gemm, every timed step is followed by one more step in which
+    the library records events right before and after each GEMM launch
+    (samples gemm_up, gemm_down): the records add about 4 us each to the
+    stream, so they stay out of the timed steps, and the interleaving gives
+    both the same conditions. Returns the per-call samples (ms) of the timed
+    steps, their event spans (ms) and the wall time (s) of the whole loop."""
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
-    # the library records these right before and after each GEMM launch
     gev = ([[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
-           if layer.times_gemm else None)
+           if gemm and layer.times_gemm else None)
+    if gev:
+        for g in gev:  # create the HIP events before the timed steps
+            for e in g:
+                e.record(layer.stream)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
         if flush is not None:
             flush(s)
-        layer.step(events[s], gev[s] if gev else None)
+        layer.step(events[s])
+        if gev:
+            if flush is not None:
+                flush(s)
+            layer.step(None, gev[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     samples = {n: np.array([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])
@@ -339,9 +351,12 @@ def timed_steps(layer, torch, steps, flush):
     return samples, spans, elapsed
 
 
-def kernel_table(cfg, samples, work, copy_gather=False):
-    """Per-call mean / p10 / median / p90 and the fraction of each call's roofline."""
-    per = {n: float(v.mean()) for n, v in samples.items()}
+def kernel_table(cfg, samples, work, copy_gather=False, gemm=None):
+    """Per-call mean / p10 / median / p90 and the fraction of each call's
+    roofline; gemm: samples of a pass with the GEMM launches timed."""
+    if gemm is not None and "gemm_up" in gemm:  # from a pass of its own
+        samples = dict(samples, gemm_up=gemm["gemm_up"], gemm_down=gemm["gemm_down"])
+    per = {n: float(samples[n].mean()) for n in NAMES}
     bf16 = cfg.dtype == "bf16"
     peak = BF16_PEAK_TFLOPS if bf16 else FP32_PEAK_TFLOPS
     ffn_ms = per["expert_ffn"]
@@ -393,15 +408,19 @@ def run_workload(name, args, moe, torch, flush, headline=False):
         layer.step()
     torch.cuda.synchronize()
     print(f"[bench] {cfg.name}: timing {args.steps} steps, cold caches", file=sys.stderr, flush=True)
-    cold, cold_spans, cold_elapsed = timed_steps(layer, torch, args.steps, flush)
+    # each cold step is followed by one with the GEMM launches timed (same caches)
+    cold, cold_spans, cold_elapsed = timed_steps(layer, torch, args.steps, flush, gemm=True)
     print(f"[bench] {cfg.name}: timing {args.steps} steps, warm caches", file=sys.stderr, flush=True)
+    # warm steps back to back (their wall time is the rate), then a pass with
+    # the GEMM launches timed
     warm, warm_spans, warm_elapsed = timed_steps(layer, torch, args.steps, None)
+    gemm_warm, _, _ = timed_steps(layer, torch, args.steps, None, gemm=True)
     counts = layer.dsp["counts"].cpu().numpy()
     kept = np.diff(layer.dsp["offsets"].cpu().numpy()) if layer.cap is not None else None
     work = algorithmic_work(cfg, counts, kept, fused=not layer.copy_gather)
     res = {"cfg": cfg, "L": L, "layer": layer, "work": work}
     res["cold"] = kernel_table(cfg, cold, work, layer.copy_gather)
-    res["warm"] = kernel_table(cfg, warm, work, layer.copy_gather)
+    res["warm"] = kernel_table(cfg, warm, work, layer.copy_gather, gemm_warm)
     res["cold_ms"] = float(cold_spans.mean())
     res["warm_ms"] = warm_elapsed * 1e3 / args.steps
     res["cold_spans"] = cold_spans
@@ -586,8 +605,9 @@ def main():
                      "frac": achieved / peak, "traffic": read_traffic(),
                      "timing": ("the FFN call's event span, halved (--copy-gather)" if layer.copy_gather
                                 else "HIP events recorded by the library right before and after each "
-                                     "GEMM launch on its stream (moe_expert_ffn_gather_timed); mean "
-                                     "over the up and down launches of the timed steps")},
+                                     "GEMM launch on its stream (moe_expert_ffn_gather_timed), in "
+                                     "steps interleaved with the timed ones (one after each, flushed "
+                                     "the same way); mean over their up and down launches")},
         "kernels": kernels,
         "mfma_util_pct_ffn": 100.0 * achieved / peak,
         "warm": summary(head, "warm"),

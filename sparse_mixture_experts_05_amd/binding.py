@@ -364,7 +364,8 @@ def moe_expert_ffn_gather(x, perm, k: int, offsets, w1, w2, ws1=None, ws2=None, 
         s = stream if stream is not None else torch.cuda.current_stream(dev)
         handles = (ctypes.c_void_p * 4)()
         for i, ev in enumerate(gemm_events):
-            ev.record(s)  # torch creates the HIP event on its first record
+            if not ev.cuda_event:
+                ev.record(s)  # torch creates the HIP event on its first record
             handles[i] = ev.cuda_event
         _check("moe_expert_ffn_gather_timed", lib().moe_expert_ffn_gather_timed(*args, handles))
     return ys, (ysh if Fs > 0 else None)
