@@ -321,11 +321,15 @@ def timed_steps(layer, torch, steps, flush, gemm=False):
     the library records events right before and after each GEMM launch
     (samples gemm_up, gemm_down): the records add about 4 us each to the
     stream, so they stay out of the timed steps, and the interleaving gives
-    both the same conditions. Returns the per-call samples (ms) of the timed
-    steps, their event spans (ms) and the wall time (s) of the whole loop."""
+    both the same conditions; with gemm="only", the GEMM-timed steps alone.
+    Returns the per-call samples (ms) of the timed steps, their event spans
+    (ms) and the wall time (s) of the whole loop."""
+    only = gemm == "only"  # the GEMM-timed steps alone
     events = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(steps)]
     gev = ([[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(steps)]
            if gemm and layer.times_gemm else None)
+    if only and gev is None:
+        return {}, None, 0.0
     if gev:
         for g in gev:  # create the HIP events before the timed steps
             for e in g:
@@ -333,21 +337,23 @@ def timed_steps(layer, torch, steps, flush, gemm=False):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(steps):
-        if flush is not None:
-            flush(s)
-        layer.step(events[s])
+        if not only:
+            if flush is not None:
+                flush(s)
+            layer.step(events[s])
         if gev:
             if flush is not None:
                 flush(s)
             layer.step(None, gev[s])
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    samples = {n: np.array([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])
-               for i, n in enumerate(NAMES)}
+    samples = {} if only else {
+        n: np.array([events[s][i].elapsed_time(events[s][i + 1]) for s in range(steps)])
+        for i, n in enumerate(NAMES)}
     if gev:
         samples["gemm_up"] = np.array([g[0].elapsed_time(g[1]) for g in gev])
         samples["gemm_down"] = np.array([g[2].elapsed_time(g[3]) for g in gev])
-    spans = np.array([events[s][0].elapsed_time(events[s][5]) for s in range(steps)])
+    spans = None if only else np.array([events[s][0].elapsed_time(events[s][5]) for s in range(steps)])
     return samples, spans, elapsed
 
 
@@ -414,7 +420,7 @@ def run_workload(name, args, moe, torch, flush, headline=False):
     # warm steps back to back (their wall time is the rate), then a pass with
     # the GEMM launches timed
     warm, warm_spans, warm_elapsed = timed_steps(layer, torch, args.steps, None)
-    gemm_warm, _, _ = timed_steps(layer, torch, args.steps, None, gemm=True)
+    gemm_warm, _, _ = timed_steps(layer, torch, args.steps, None, gemm="only")
     counts = layer.dsp["counts"].cpu().numpy()
     kept = np.diff(layer.dsp["offsets"].cpu().numpy()) if layer.cap is not None else None
     work = algorithmic_work(cfg, counts, kept, fused=not layer.copy_gather)
