@@ -1235,13 +1235,14 @@ void grid_of(GemmArgs& a, int rows, int E, dim3& grid) {
   grid = dim3(a.routed_tiles + shared_tiles);
 }
 
-// K slices of a small-tile launch. With fewer tiles than CUs (a single token:
-// every workgroup would walk all of K alone on a CU of its own) K is split so
-// that about 1024 workgroups stream the weights, each slice at least 8 stages
-// of the routed K; gemm_small_reduce_kernel sums the slices. Measured on the
-// graph-replayed decode layer (H = 4096, E = 128, k = 8, F = 1536 + shared):
-// T = 1 FFN 55.1 -> 48.7 us (216 up-projection tiles, 4 slices); at T = 2
-// (408 tiles) a 2-way split cost 3 us more than it saved, hence the limit.
+// K slices of a small-tile launch. With fewer tiles than CUs (every
+// workgroup would walk all of K alone on a CU of its own) K is split so that
+// about 1024 workgroups stream the weights, each slice at least 8 stages of
+// the routed K; gemm_small_reduce_kernel sums the slices. Measured on the
+// graph-replayed decode layer (H = 4096, E = 128, k = 8, F = 1536 + shared),
+// which the few-row kernel now runs: T = 1 FFN 55.1 -> 48.7 us (216
+// up-projection tiles, 4 slices); at T = 2 (408 tiles) a 2-way split cost
+// 3 us more than it saved, hence the limit.
 constexpr int kSmallBM = 32, kSmallBN = 64;
 
 int small_splits(const GemmArgs& a, int rows, int E) {
