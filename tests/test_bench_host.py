@@ -81,3 +81,23 @@ def test_cpu_baseline_repeats_short_samples():
     assert set(st) == {"route", "dispatch", "expert_ffn", "combine", "load_stats"}
     assert all(v >= 0 for v in st.values())
     assert sum(st.values()) * passes <= cb["seconds"] * 1.001
+
+
+def test_roofline_takes_the_gemm_launch_events():
+    """kernel_table: with GEMM launch samples, the roofline rate is the flops
+    of one launch (half the FFN's) over the mean of the up and down launch
+    times; the whole-call rate stays beside it; without them it falls back to
+    the call time halved."""
+    cfg = get_config("mixtral_8x7b")
+    w = bench.algorithmic_work(cfg)
+    calls = {n: np.full(4, 0.01) for n in bench.NAMES}
+    calls["expert_ffn"] = np.array([1.8, 1.8, 1.8, 1.8])  # ms per FFN call
+    gemm = {"gemm_up": np.array([0.9, 0.94]), "gemm_down": np.array([0.8, 0.76])}
+    k, achieved, peak = bench.kernel_table(cfg, calls, w, gemm=gemm)
+    launch_ms = np.mean([0.9, 0.94, 0.8, 0.76])
+    assert np.isclose(achieved, w["ffn_flops"] / 2 / (launch_ms * 1e-3) / 1e12)
+    assert np.isclose(k["expert_ffn"]["gemm_launch_ms"]["mean"], launch_ms)
+    assert np.isclose(k["expert_ffn"]["TFLOP/s"], w["ffn_flops"] / 1.8e-3 / 1e12)
+    assert peak == bench.BF16_PEAK_TFLOPS
+    _, fallback, _ = bench.kernel_table(cfg, calls, w)
+    assert np.isclose(fallback, w["ffn_flops"] / 1.8e-3 / 1e12)
