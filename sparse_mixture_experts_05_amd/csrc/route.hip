@@ -30,12 +30,12 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kMaxE = 256;
 
-// Row stride (floats) of a score tile of BT tokens. The top-k gives each
-// token G = 256/BT consecutive lanes; lane g of a token reads the columns
-// g, g + G, ..., so a stride of G (mod 64) puts the 64 lanes of a wave on 64
-// distinct banks.
-template <int BT>
-constexpr int tile_stride() { return kMaxE + kThreads / BT; }
+// Row stride (floats) of a score tile of BT tokens in a workgroup of NW
+// waves. The top-k gives each token G = 64*NW/BT consecutive lanes; lane g of
+// a token reads the columns g, g + G, ..., so a stride of G (mod 64) puts the
+// 64 lanes of a wave on 64 distinct banks.
+template <int BT, int NW = 4>
+constexpr int tile_stride() { return kMaxE + NW * 64 / BT; }
 
 // ---------------------------------------------------------------- top-k
 // Every (score, expert) pair is one 64-bit key: the score's bits mapped to an
@@ -130,13 +130,14 @@ __device__ __forceinline__ float group_sum(float v) {
 // When pp is not null, the full softmax p[t, e] = exp(s_e - m) / sum_e' exp(s_e' - m)
 // of every token overwrites its scores, and pp[e] receives the sum of p[t, e]
 // over the tile's tokens (t ascending).
-template <int BT, int KP, int EPX>
+template <int BT, int KP, int EPX, int NW = 4>
 __device__ __forceinline__ void topk_tokens(float* sc, int t0, int T, int E, int k,
                                             int32_t* __restrict__ topk_idx,
                                             float* __restrict__ topk_w, float* __restrict__ pp) {
-  constexpr int G = kThreads / BT;
-  constexpr int S = tile_stride<BT>();
-  static_assert(G >= 1 && G <= 64 && BT * G == kThreads, "one group of lanes per token");
+  constexpr int NT = NW * 64;
+  constexpr int G = NT / BT;
+  constexpr int S = tile_stride<BT, NW>();
+  static_assert(G >= 1 && G <= 64 && BT * G == NT, "one group of lanes per token");
   constexpr int NSUB = (EPX + G - 1) / G;  // experts per lane, at most
   constexpr int NBLK = (NSUB + KP - 1) / KP;
   const int t = threadIdx.x / G, g = threadIdx.x % G;
@@ -205,7 +206,7 @@ __device__ __forceinline__ void topk_tokens(float* sc, int t0, int T, int E, int
     }
     __syncthreads();
     const int nt = min(BT, T - t0);
-    for (int e = threadIdx.x; e < E; e += kThreads) {
+    for (int e = threadIdx.x; e < E; e += NT) {
       float a = 0.0f;
       for (int q = 0; q < nt; ++q) a += sc[q * S + e];
       pp[e] = a;
@@ -213,14 +214,14 @@ __device__ __forceinline__ void topk_tokens(float* sc, int t0, int T, int E, int
   }
 }
 
-template <int BT, int EPX>
+template <int BT, int EPX, int NW = 4>
 __device__ __forceinline__ void topk_phase(float* sc, int t0, int T, int E, int k,
                                            int32_t* __restrict__ topk_idx,
                                            float* __restrict__ topk_w, float* __restrict__ pp) {
-  if (k <= 1) topk_tokens<BT, 1, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
-  else if (k <= 2) topk_tokens<BT, 2, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
-  else if (k <= 4) topk_tokens<BT, 4, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
-  else topk_tokens<BT, 8, EPX>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  if (k <= 1) topk_tokens<BT, 1, EPX, NW>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else if (k <= 2) topk_tokens<BT, 2, EPX, NW>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else if (k <= 4) topk_tokens<BT, 4, EPX, NW>(sc, t0, T, E, k, topk_idx, topk_w, pp);
+  else topk_tokens<BT, 8, EPX, NW>(sc, t0, T, E, k, topk_idx, topk_w, pp);
 }
 
 // P[e] = (sum over workgroups b, ascending, of part[b][e]) / T, in double.
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(kThreads) void prob_mean_kernel(const float* __rest
 // Work split: EP >= 64, wave w computes experts [w*EP/4, (w+1)*EP/4) over all
 // panels; EP < 64, wave w takes the panels p = w (mod 4) of every stage for
 // the whole tile and the 4 partial tiles are summed in a fixed order.
-template <int BT, int EP>
+template <int BT, int EP, int NW = 4>
 struct RouteTile {
   static constexpr int R = (BT + EP + 31) / 32 * 32;  // rows per panel
   static constexpr int PB = R * 128;                  // panel bytes
@@ -266,25 +267,27 @@ struct RouteTile {
   static constexpr int PPS = KSPLIT ? (PPS_RAW >= 8 ? 8 : 4) : (PPS_RAW > 2 ? 2 : PPS_RAW);
   static constexpr int SB = PPS * PB;                 // stage bytes
   static constexpr int NS = 3;                        // stages
-  static constexpr int NI = PPS * R / 32;             // DMA instructions per wave per stage
+  static constexpr int NI = PPS * R / 8 / NW;         // DMA instructions per wave per stage
   static constexpr int MC = BT / 16;                  // 16-row tiles per wave
-  static constexpr int NC = KSPLIT ? EP / 16 : EP / 64;  // 16-column tiles per wave
-  static constexpr int SC_BYTES = BT * tile_stride<BT>() * 4;
+  static constexpr int NC = KSPLIT ? EP / 16 : EP / 16 / NW;  // 16-column tiles per wave
+  static constexpr int SC_BYTES = BT * tile_stride<BT, NW>() * 4;
   static constexpr int PART_BYTES = KSPLIT ? 4 * BT * EP * 4 : 0;
   static constexpr int LDS = NS * SB > SC_BYTES + PART_BYTES ? NS * SB : SC_BYTES + PART_BYTES;
-  static_assert(PPS * R % 32 == 0, "whole DMA instructions per wave");
+  static_assert(PPS * R % (8 * NW) == 0, "whole DMA instructions per wave");
+  static_assert(!KSPLIT || NW == 4, "the waves split the panels four ways");
+  static_assert(KSPLIT || NC >= 1, "whole 16-column tiles per wave");
   static_assert(NI < 32, "vmcnt range");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
 // The K loop of one tile; returns with every wave's accumulators complete and
 // the LDS free for reuse (after a barrier).
-template <int BT, int EP>
+template <int BT, int EP, int NW = 4>
 __device__ __forceinline__ void score_tile(uint8_t* smem, const uint16_t* __restrict__ x,
                                            const uint16_t* __restrict__ wg, int t0, int T, int e0,
                                            int E, int H, int kp0, int kp1,
-                                           f32x4_t (&acc)[RouteTile<BT, EP>::MC][RouteTile<BT, EP>::NC]) {
-  using C = RouteTile<BT, EP>;
+                                           f32x4_t (&acc)[RouteTile<BT, EP, NW>::MC][RouteTile<BT, EP, NW>::NC]) {
+  using C = RouteTile<BT, EP, NW>;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int NST = (kp1 - kp0 + C::PPS - 1) / C::PPS;  // stages
 
@@ -318,7 +321,7 @@ __device__ __forceinline__ void score_tile(uint8_t* smem, const uint16_t* __rest
   // fragment of a 16-row tile: row lane%16, chunk ks*4 + lane/16 (a 32-deep k step)
   const int fr = (lane & 15) * 128;
   const int sw = (lane >> 1) & 7;
-  const int c0 = C::KSPLIT ? 0 : wave * (EP / 4);
+  const int c0 = C::KSPLIT ? 0 : wave * (EP / NW);
 
 #pragma unroll
   for (int st = 0; st < C::NS - 1; ++st)
@@ -359,15 +362,15 @@ __device__ __forceinline__ void score_tile(uint8_t* smem, const uint16_t* __rest
 // Scores of the tile plus the bias into LDS (row-major, tile_stride<BT>()),
 // columns < ncol. D layout of 16x16: lane holds column lane%16, rows
 // (lane/16)*4 + v.
-template <int BT, int EP>
+template <int BT, int EP, int NW = 4>
 __device__ __forceinline__ void scores_to_lds(uint8_t* smem, int ncol, const float* __restrict__ bias,
-                                              const f32x4_t (&acc)[RouteTile<BT, EP>::MC][RouteTile<BT, EP>::NC]) {
-  using C = RouteTile<BT, EP>;
-  constexpr int S = tile_stride<BT>();
+                                              const f32x4_t (&acc)[RouteTile<BT, EP, NW>::MC][RouteTile<BT, EP, NW>::NC]) {
+  using C = RouteTile<BT, EP, NW>;
+  constexpr int S = tile_stride<BT, NW>();
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   float* sc = reinterpret_cast<float*>(smem);
   if (!C::KSPLIT) {
-    const int c0 = wave * (EP / 4);
+    const int c0 = wave * (EP / NW);
 #pragma unroll
     for (int m = 0; m < C::MC; ++m)
 #pragma unroll
@@ -404,20 +407,21 @@ __device__ __forceinline__ void scores_to_lds(uint8_t* smem, int ncol, const flo
   __syncthreads();
 }
 
-// One launch: BT tokens x all E experts (EP >= E) over all of H, then top-k.
-template <int BT, int EP>
-__global__ __launch_bounds__(kThreads) void route_bf16_kernel(
+// One launch: BT tokens x all E experts (EP >= E) over all of H, then top-k,
+// by NW waves.
+template <int BT, int EP, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void route_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wg,
     const float* __restrict__ bias, int T, int H, int E, int k, int32_t* __restrict__ topk_idx,
     float* __restrict__ topk_w, float* __restrict__ ppart) {
-  using C = RouteTile<BT, EP>;
+  using C = RouteTile<BT, EP, NW>;
   __shared__ __align__(16) uint8_t smem[C::LDS];
   const int t0 = blockIdx.x * BT;
   f32x4_t acc[C::MC][C::NC];
-  score_tile<BT, EP>(smem, x, wg, t0, T, 0, E, H, 0, H / 64, acc);
-  scores_to_lds<BT, EP>(smem, E, bias, acc);
-  topk_phase<BT, EP>(reinterpret_cast<float*>(smem), t0, T, E, k, topk_idx, topk_w,
-                     ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
+  score_tile<BT, EP, NW>(smem, x, wg, t0, T, 0, E, H, 0, H / 64, acc);
+  scores_to_lds<BT, EP, NW>(smem, E, bias, acc);
+  topk_phase<BT, EP, NW>(reinterpret_cast<float*>(smem), t0, T, E, k, topk_idx, topk_w,
+                         ppart != nullptr ? ppart + (size_t)blockIdx.x * E : nullptr);
 }
 
 // fp32 scores with plain dot products (small fp32 layers).
@@ -461,24 +465,24 @@ __global__ __launch_bounds__(kThreads) void route_f32_kernel(
 //   L2 -> LDS traffic that bounds the one-launch kernel at large E.
 constexpr int kPartBT = 16, kPartEP = 64, kMaxSlices = 16;
 
-template <int BT, int EP>
-__global__ __launch_bounds__(kThreads) void route_partial_kernel(const uint16_t* __restrict__ x,
-                                                                 const uint16_t* __restrict__ wg,
-                                                                 int T, int H, int E, int kps,
-                                                                 float* __restrict__ ws) {
-  using C = RouteTile<BT, EP>;
-  static_assert(!C::KSPLIT, "each wave owns EP / 4 experts");
+template <int BT, int EP, int NW = 4>
+__global__ __launch_bounds__(NW * 64) void route_partial_kernel(const uint16_t* __restrict__ x,
+                                                                const uint16_t* __restrict__ wg,
+                                                                int T, int H, int E, int kps,
+                                                                float* __restrict__ ws) {
+  using C = RouteTile<BT, EP, NW>;
+  static_assert(!C::KSPLIT, "each wave owns EP / NW experts");
   __shared__ __align__(16) uint8_t smem[C::NS * C::SB];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int t0 = blockIdx.x * BT, e0 = blockIdx.y * EP, ks = blockIdx.z;
   f32x4_t acc[C::MC][C::NC];
-  score_tile<BT, EP>(smem, x, wg, t0, T, e0, E, H, ks * kps, (ks + 1) * kps, acc);
+  score_tile<BT, EP, NW>(smem, x, wg, t0, T, e0, E, H, ks * kps, (ks + 1) * kps, acc);
   // D layout of 16x16: lane holds column lane%16, rows (lane/16)*4 + v
 #pragma unroll
   for (int m = 0; m < C::MC; ++m)
 #pragma unroll
     for (int n = 0; n < C::NC; ++n) {
-      const int e = e0 + wave * (EP / 4) + n * 16 + (lane & 15);
+      const int e = e0 + wave * (EP / NW) + n * 16 + (lane & 15);
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int t = t0 + m * 16 + (lane >> 4) * 4 + v;
@@ -564,6 +568,18 @@ hipError_t launch_select(int nks, const float* ws, const float* bias, int T, int
 // big tiles against one launch between T = 4096 and 8192 (E = 128: 27.2
 // against 29.3 us at 4096, 42.4 against 33.8 at 8192; E = 256: 35.6 against
 // 39.4, 52.0 against 45.6).
+// Waves of a workgroup of the bf16 score kernels: 8 for tiles of 128 or more
+// experts whose panels split into whole copy instructions over 8 waves, else
+// 4. With 8, a CU keeps twice the waves issuing the L2 -> LDS copies of Wg
+// (the same bytes in flight stream faster: a microbenchmark read 75 against
+// 49 GB/s per CU with 32 KiB in flight) and the top-k has twice the lanes per
+// token.
+template <int BT, int EP>
+constexpr int route_waves() {
+  using C = RouteTile<BT, EP>;  // its panel rows and panels per stage do not depend on the waves
+  return EP >= 128 && (C::PPS * C::R) % 64 == 0 ? 8 : 4;
+}
+
 enum RouteMode { kOneLaunch, kTwoSmall, kTwoBig };
 RouteMode route_mode(int T, int E, bool bf16) {
   if (!bf16) return kOneLaunch;
@@ -587,11 +603,11 @@ int route_kslices(int T, int H, int E) {
   return ks;
 }
 
-template <int BT, int EP>
+template <int BT, int EP, int NW = 4>
 hipError_t launch_bf16(const void* x, const void* wg, const float* bias, int T, int H, int E,
                        int k, int32_t* idx, float* w, float* pp, hipStream_t s) {
   const int grid = (T + BT - 1) / BT;
-  hipLaunchKernelGGL((route_bf16_kernel<BT, EP>), dim3(grid), dim3(kThreads), 0, s,
+  hipLaunchKernelGGL((route_bf16_kernel<BT, EP, NW>), dim3(grid), dim3(NW * 64), 0, s,
                      static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(wg), bias, T,
                      H, E, k, idx, w, pp);
   return hipGetLastError();
@@ -603,8 +619,8 @@ hipError_t launch_bf16_bt(const void* x, const void* wg, const float* bias, int 
   if (E <= 16) return launch_bf16<BT, 16>(x, wg, bias, T, H, E, k, idx, w, pp, s);
   if (E <= 32) return launch_bf16<BT, 32>(x, wg, bias, T, H, E, k, idx, w, pp, s);
   if (E <= 64) return launch_bf16<BT, 64>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-  if (E <= 128) return launch_bf16<BT, 128>(x, wg, bias, T, H, E, k, idx, w, pp, s);
-  return launch_bf16<BT, 256>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+  if (E <= 128) return launch_bf16<BT, 128, route_waves<BT, 128>()>(x, wg, bias, T, H, E, k, idx, w, pp, s);
+  return launch_bf16<BT, 256, route_waves<BT, 256>()>(x, wg, bias, T, H, E, k, idx, w, pp, s);
 }
 
 // Tokens per workgroup of the one-launch bf16 path: as many as keep >= 256
@@ -664,11 +680,13 @@ hipError_t launch_route(const void* x, const void* wg, const float* bias, int T,
                          wp, T, H, E, kps, sp);
     } else if (E > 128) {
       const dim3 grid((T + 127) / 128, (E + 255) / 256, nks);
-      hipLaunchKernelGGL((route_partial_kernel<128, 256>), grid, dim3(kThreads), 0, s, xp, wp, T,
+      hipLaunchKernelGGL((route_partial_kernel<128, 256, route_waves<128, 256>()>), grid,
+                         dim3(route_waves<128, 256>() * 64), 0, s, xp, wp, T,
                          H, E, kps, sp);
     } else {
       const dim3 grid((T + 63) / 64, (E + 127) / 128, nks);
-      hipLaunchKernelGGL((route_partial_kernel<64, 128>), grid, dim3(kThreads), 0, s, xp, wp, T, H,
+      hipLaunchKernelGGL((route_partial_kernel<64, 128, route_waves<64, 128>()>), grid,
+                         dim3(route_waves<64, 128>() * 64), 0, s, xp, wp, T, H,
                          E, kps, sp);
     }
     err = hipGetLastError();
