@@ -563,11 +563,16 @@ hipError_t launch_select(int nks, const float* ws, const float* bias, int T, int
 
 // Path of a route call. Both two-launch paths write and re-read T x E partial
 // scores per K slice, so their time grows faster with T than the one-launch
-// path's. Measured crossovers (graph replay, H = 4096, k = 8): small tiles
-// against one launch near T = 2048 up to E = 128 and near 3072 for E = 256;
-// big tiles against one launch between T = 4096 and 8192 (E = 128: 27.2
-// against 29.3 us at 4096, 42.4 against 33.8 at 8192; E = 256: 35.6 against
-// 39.4, 52.0 against 45.6).
+// path's; the one-launch path re-reads Wg once per 16, 32 or 64 tokens.
+// Measured crossovers (H = 4096, k = 8): small tiles against one launch near
+// T = 2048 up to E = 128 and near 3072 for E = 256 (graph replay). Big tiles
+// against one launch (route alone, read-flushed caches, 8-wave tiles on both
+// paths for E >= 128): E = 128 30.0 against 54.7 us at T = 6144, 32.4
+// against 33.3 at 8192, 47.5 against 58.9 at 12288, 45.9 against 46.1 at
+// 16384; E = 256 39.3 against 85.8 at 6144, 59.6 against 99.3 at 12288,
+// 62.9 against 63.1 at 16384. So big tiles up to T = 16384, where the
+// one-launch path has 64-token tiles.
+
 // Waves of a workgroup of the bf16 score kernels: 8 for tiles of 128 or more
 // experts whose panels split into whole copy instructions over 8 waves, else
 // 4. With 8, a CU keeps twice the waves issuing the L2 -> LDS copies of Wg
@@ -587,7 +592,7 @@ enum RouteMode { kOneLaunch, kTwoSmall, kTwoBig };
 RouteMode route_mode(int T, int E, bool bf16) {
   if (!bf16) return kOneLaunch;
   if (T < (E > 128 ? 3072 : 2048)) return kTwoSmall;
-  return E > 64 && T < 6144 ? kTwoBig : kOneLaunch;
+  return E > 64 && T < 16384 ? kTwoBig : kOneLaunch;
 }
 bool route_two_phase(int T, int E, bool bf16) { return route_mode(T, E, bf16) != kOneLaunch; }
 

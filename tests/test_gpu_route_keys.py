@@ -48,6 +48,7 @@ CASES = [  # (T, H, E, k): route paths of the library
     (4096, 128, 128, 8),   # two launches, 64 x 128 tiles
     (4096, 192, 256, 8),   # two launches, 128 x 256 tiles
     (8192, 128, 40, 3),    # one launch, 32 tokens per workgroup
+    (8192, 128, 200, 8),   # two launches, 128 x 256 tiles, 64 token tiles
     (16384, 128, 256, 8),  # one launch, 64 tokens per workgroup
     (3, 64, 256, 8),       # a few tokens, E = 256
 ]
