@@ -565,7 +565,10 @@ hipError_t launch_select(int nks, const float* ws, const float* bias, int T, int
 // scores per K slice, so their time grows faster with T than the one-launch
 // path's; the one-launch path re-reads Wg once per 16, 32 or 64 tokens.
 // Measured crossovers (H = 4096, k = 8): small tiles against one launch near
-// T = 2048 up to E = 128 and near 3072 for E = 256 (graph replay). Big tiles
+// T = 2048 up to E = 128 and near 3072 for E = 256 (graph replay, 4-wave
+// tiles); small against big tiles near T = 2048 (E = 128: 18.0 against 18.5
+// us at 1024, equal at 2048; E = 256: 26.7 against 27.8 at 1024, 35.0
+// against 31.0 at 2048; route alone, read-flushed caches). Big tiles
 // against one launch (route alone, read-flushed caches, 8-wave tiles on both
 // paths for E >= 128): E = 128 30.0 against 54.7 us at T = 6144, 32.4
 // against 33.3 at 8192, 47.5 against 58.9 at 12288, 45.9 against 46.1 at
@@ -591,7 +594,7 @@ constexpr int route_waves() {
 enum RouteMode { kOneLaunch, kTwoSmall, kTwoBig };
 RouteMode route_mode(int T, int E, bool bf16) {
   if (!bf16) return kOneLaunch;
-  if (T < (E > 128 ? 3072 : 2048)) return kTwoSmall;
+  if (T < 2048) return kTwoSmall;
   return E > 64 && T < 16384 ? kTwoBig : kOneLaunch;
 }
 bool route_two_phase(int T, int E, bool bf16) { return route_mode(T, E, bf16) != kOneLaunch; }
