@@ -1138,26 +1138,28 @@ __global__ __launch_bounds__(kThreads) void gemm_tail_reduce_kernel(GemmArgs arg
   const float* P = args.part + (size_t)t.unit0 * BM * BN;
   constexpr int RR = BM / kReduceParts;  // rows of this workgroup
   const int r0 = (blockIdx.x % kReduceParts) * RR;
-  for (int q = threadIdx.x; q < RR * BN / 2; q += kThreads) {
-    const int row = r0 + q / (BN / 2), col = (q % (BN / 2)) * 2;
+  // 4 columns per thread (N % 64 == 0: a group of 4 is all in or all out);
+  // every slice load is issued, from a slice index clamped into [0, spl), before
+  // the sum in slice order (guarded loads would each wait in a branch)
+  const int spl = t.spl;
+  for (int q = threadIdx.x; q < RR * BN / 4; q += kThreads) {
+    const int row = r0 + q / (BN / 4), col = (q % (BN / 4)) * 4;
     if (row >= t.M || col >= nvalid) continue;
-    float2 v[kMaxSplit];
-#pragma unroll
-    for (int ks = 0; ks < kMaxSplit; ++ks)  // all loads first, then the sum in slice order
-      if (ks < t.spl)
-        v[ks] = *reinterpret_cast<const float2*>(P + (size_t)ks * BM * BN + (size_t)row * BN + col);
-    float y0 = 0.0f, y1 = 0.0f;
+    f32x4_t v[kMaxSplit];
 #pragma unroll
     for (int ks = 0; ks < kMaxSplit; ++ks)
-      if (ks < t.spl) {
-        y0 += v[ks].x;
-        y1 += v[ks].y;
-      }
+      v[ks] = *reinterpret_cast<const f32x4_t*>(P + (size_t)min(ks, spl - 1) * BM * BN +
+                                                (size_t)row * BN + col);
+    f32x4_t y = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int ks = 0; ks < kMaxSplit; ++ks)
+      if (ks < spl) y += v[ks];
     if (gelu) {
-      y0 = gelu_bf16(y0);
-      y1 = gelu_bf16(y1);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) y[c] = gelu_bf16(y[c]);
     }
-    *reinterpret_cast<uint32_t*>(C + (size_t)row * N + col) = pack_bf16x2(y0, y1);
+    *reinterpret_cast<uint2*>(C + (size_t)row * N + col) =
+        make_uint2(cvt_bf16x2(y[0], y[1]), cvt_bf16x2(y[2], y[3]));
   }
 }
 
