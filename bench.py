@@ -31,6 +31,8 @@ layers and the decode sweep (T = 1..128, graph replay). Prints one JSON line:
                fraction of its roofline; route, dispatch and combine also as a
                fraction of a plain device copy timed in the same run
                (measured_copy_GB/s)
+  measured_dense_gemm  the vendor library's bf16 GEMM on the dense problem of
+               the same size (context for the MFMA fraction)
   warm         the headline layer with warm caches
   workloads    cold and warm summaries of the other 4096+-token layers
   decode       per-T graph-replayed latency (cold and warm) and the FFN's
@@ -446,6 +448,39 @@ def summary(res, which="cold"):
             "kernels_median_ms": {n: k[n]["median_ms"] for n in NAMES}}
 
 
+def dense_gemm_reference(cfg, torch, reps=10):
+    """Context for the MFMA fraction: the vendor library (hipBLASLt through
+    torch.nn.functional.linear) on the dense problem of the same size, all
+    T*k routed rows as one matrix, with the weights laid out as the layer's
+    (rows along K): [rows, H] x [F, H]^T and [rows, F] x [H, F]^T in bf16
+    with fp32 accumulation, timed with events after two untimed calls each."""
+    import torch.nn.functional as Fn
+    rows, H, F = cfg.T * cfg.k, cfg.H, cfg.F
+    g = torch.Generator(device="cuda").manual_seed(0)
+    a = torch.randn(rows, H, device="cuda", generator=g).to(torch.bfloat16)
+    w1 = (torch.randn(F, H, device="cuda", generator=g) / 64).to(torch.bfloat16)
+    w2 = (torch.randn(H, F, device="cuda", generator=g) / 64).to(torch.bfloat16)
+    h = Fn.linear(a, w1)
+    out = {}
+    for name, x, w in [("up", a, w1), ("down", h, w2)]:
+        Fn.linear(x, w)
+        Fn.linear(x, w)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(reps):
+            Fn.linear(x, w)
+        ev1.record()
+        torch.cuda.synchronize()
+        out[name] = ev0.elapsed_time(ev1) / reps
+    del a, w1, w2, h
+    torch.cuda.empty_cache()
+    flops = 2.0 * rows * H * F
+    return {"TFLOP/s": 2 * flops / ((out["up"] + out["down"]) * 1e-3) / 1e12,
+            "up_ms": out["up"], "down_ms": out["down"],
+            "shape": f"[{rows},{H}]x[{F},{H}]^T and [{rows},{F}]x[{H},{F}]^T, bf16, fp32 accumulation",
+            "library": "hipBLASLt (torch.nn.functional.linear), warm caches"}
+
+
 def decode_sweep(args, moe, torch, flush):
     """The decode-shaped sweep: per T, graph-replayed layer latency from cold
     caches (a flush before every replay, events around the replay) and warm
@@ -650,6 +685,10 @@ def main():
     result["measured_copy_GB/s"] = copy_gbs
     for n in ["route", "dispatch", "combine"]:
         kernels[n]["copy_frac"] = kernels[n]["GB/s"] / copy_gbs
+    if bf16:
+        ref = dense_gemm_reference(cfg, torch)
+        result["measured_dense_gemm"] = ref
+        result["roofline"]["frac_of_measured_dense_gemm"] = achieved / ref["TFLOP/s"]
     if args.copy_calibration:
         # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
         # readings convert those counters to bytes for the kernels above
