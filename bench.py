@@ -33,6 +33,8 @@ layers and the decode sweep (T = 1..128, graph replay). Prints one JSON line:
                (measured_copy_GB/s)
   measured_dense_gemm  the vendor library's bf16 GEMM on the dense problem of
                the same size (context for the MFMA fraction)
+  measured_mfma_loop   the bf16 matrix-core rate of a register-only MFMA loop
+               (libmoe_probe.so; context for the MFMA fraction)
   warm         the headline layer with warm caches
   workloads    cold and warm summaries of the other 4096+-token layers
   decode       per-T graph-replayed latency (cold and warm) and the FFN's
@@ -481,6 +483,42 @@ def dense_gemm_reference(cfg, torch, reps=10):
             "library": "hipBLASLt (torch.nn.functional.linear), warm caches"}
 
 
+def mfma_loop_reference(torch, blocks=512, iters=20000):
+    """Context for the MFMA fraction: the bf16 matrix-core rate with no memory
+    traffic (libmoe_probe.so, moe_probe_mfma_bf16: 8 independent 32x32x16
+    MFMA chains per wave, two 4-wave workgroups per CU), timed with events
+    over three calls after one untimed call."""
+    import ctypes
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "sparse_mixture_experts_05_amd",
+                        "libmoe_probe.so")
+    lib = ctypes.CDLL(path)
+    lib.moe_probe_mfma_bf16.restype = ctypes.c_int
+    lib.moe_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    lib.moe_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.moe_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def run(n):
+        rc = lib.moe_probe_mfma_bf16(blocks, n, ctypes.c_void_p(sink.data_ptr()), stream)
+        if rc != 0:
+            raise RuntimeError(f"moe_probe_mfma_bf16 returned {rc}")
+
+    run(iters // 10)
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(3):
+        run(iters)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / 3
+    if not bool(torch.isfinite(sink).all()):
+        raise RuntimeError("moe_probe_mfma_bf16 produced a non-finite sum")
+    del sink
+    return {"TFLOP/s": lib.moe_probe_mfma_bf16_flops(blocks, iters) / (ms * 1e-3) / 1e12, "ms": ms,
+            "kernel": "register-only v_mfma_f32_32x32x16_bf16 loop, no memory traffic"}
+
+
 def decode_sweep(args, moe, torch, flush):
     """The decode-shaped sweep: per T, graph-replayed layer latency from cold
     caches (a flush before every replay, events around the replay) and warm
@@ -689,6 +727,9 @@ def main():
         ref = dense_gemm_reference(cfg, torch)
         result["measured_dense_gemm"] = ref
         result["roofline"]["frac_of_measured_dense_gemm"] = achieved / ref["TFLOP/s"]
+        loop = mfma_loop_reference(torch)
+        result["measured_mfma_loop"] = loop
+        result["roofline"]["frac_of_measured_mfma_loop"] = achieved / loop["TFLOP/s"]
     if args.copy_calibration:
         # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE
         # readings convert those counters to bytes for the kernels above

@@ -3,7 +3,8 @@
     python -m sparse_mixture_experts_05_amd.build
 
 Every HIP source is compiled to an object under _build/ (in parallel), then
-linked into sparse_mixture_experts_05_amd/libmoe.so. Always recompiles.
+linked into sparse_mixture_experts_05_amd/libmoe.so; the measurement probes
+(csrc/probe.hip) go into libmoe_probe.so beside it. Always recompiles.
 """
 from __future__ import annotations
 
@@ -19,8 +20,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
+PROBE_LIB = os.path.join(PKG, "libmoe_probe.so")
 
 SOURCES = ["route.hip", "dispatch.hip", "ffn.hip", "combine.hip", "stats.hip", "bias.hip", "moe_api.cpp"]
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -43,18 +46,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(min(8, len(SOURCES))) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, lib: str) -> None:
+    tmp = lib + ".tmp"
     cmd = [HIPCC, "-shared", "-fPIC", "--offload-arch=gfx950", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    shutil.move(tmp, LIB)
+    shutil.move(tmp, lib)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(min(8, len(srcs))) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

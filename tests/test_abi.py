@@ -369,3 +369,23 @@ def test_dispatch_noalloc_validation():
         assert L.moe_dispatch_workspace_bytes(T_max + 256, E, 1) > 1 << 20
         assert f(FAKE, None, T_max + 256, 64, E, 1, 1, FAKE, FAKE, FAKE, FAKE, None, None) == -5
     assert "scratch" in moe.moe_status_string(-5)
+
+
+def test_probe_library_exports_and_validates():
+    """libmoe_probe.so (bench context only) exports what include/moe_probe.h
+    declares, rejects bad arguments before any HIP call and counts its flops."""
+    path = os.path.join(os.path.dirname(moe.lib()._name), "libmoe_probe.so")
+    lib = ctypes.CDLL(path)
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(ROOT, "include", "moe_probe.h")).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(moe_[a-z_0-9]+)\s*\(", text)))
+    assert names == ["moe_probe_mfma_bf16", "moe_probe_mfma_bf16_flops"]
+    for n in names:
+        assert hasattr(lib, n), f"libmoe_probe.so does not export {n}"
+    lib.moe_probe_mfma_bf16.restype = ctypes.c_int
+    lib.moe_probe_mfma_bf16.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    for blocks, iters, sink in [(0, 1, FAKE), (65537, 1, FAKE), (1, 0, FAKE), (1, 1, None)]:
+        assert lib.moe_probe_mfma_bf16(blocks, iters, sink, None) == -1
+    lib.moe_probe_mfma_bf16_flops.restype = ctypes.c_double
+    lib.moe_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    # 4 waves x 8 chains x 32*32*16*2 flops per round
+    assert lib.moe_probe_mfma_bf16_flops(3, 5) == 3 * 4 * 5 * 8 * 32768
